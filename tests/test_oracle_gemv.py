@@ -1,0 +1,137 @@
+"""Pins for the oracle's GEMV: two independent forms, exact rationals, and the
+unit-scale special case that reduces to an integer matmul."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats, gemv
+from oracle.quant import quantize_q8
+
+FMTS = formats.FORMATS
+
+
+def _cb():
+    return synth.codebook(9)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 3])
+def test_intdot_form_equals_dequant_form(fmt, m):
+    n, k = 37, 1024
+    raw = synth.weights(fmt, n, k, seed=4)
+    x = synth.activations(5, m, k)
+    cb = _cb()
+    xq, dx, sx = quantize_q8(x)
+    y2 = gemv.gemv_dequant(fmt, raw, n, k, xq, dx, cb)
+    y1 = gemv.gemv_intdot(fmt, raw, n, k, xq, dx, sx, cb)
+    assert np.linalg.norm(y1 - y2) <= 1e-13 * np.linalg.norm(y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unit_scales_reduce_to_integer_matmul(fmt):
+    # d = 1, sc = 1, m = 0, dmin = 0 and activations with block absmax 127
+    # (so dx = 1, xq = x): y must equal the int64 matmul of the code matrices.
+    n, k = 9, 512
+    rng = np.random.default_rng(21)
+    nb = k // formats.BLOCK_ELEMS[fmt]
+    f = {"d": np.ones((n, nb))}
+    cb = _cb().astype(np.int64)
+    if fmt in ("q4_0", "iq4_nl"):
+        f["q"] = rng.integers(0, 16, (n, nb, 32))
+        ints = (f["q"] - 8) if fmt == "q4_0" else cb[f["q"]]
+    elif fmt == "q8_0":
+        f["q"] = rng.integers(-127, 128, (n, nb, 32))
+        ints = f["q"]
+    elif fmt == "q4_k":
+        f.update(dmin=np.zeros((n, nb)), sc=np.ones((n, nb, 8), np.int64),
+                 m=np.zeros((n, nb, 8), np.int64), q=rng.integers(0, 16, (n, nb, 256)))
+        ints = f["q"]
+    else:
+        f.update(sc=np.ones((n, nb, 16), np.int64), q=rng.integers(0, 64, (n, nb, 256)))
+        ints = f["q"] - 32
+    W = ints.reshape(n, k)
+    raw = formats.encode(fmt, f)
+    xi = rng.integers(-127, 128, (2, k))
+    xi[:, ::32] = 127
+    xq, dx, sx = quantize_q8(xi.astype(np.float32))
+    assert np.all(dx == 1) and np.array_equal(xq.astype(np.int64), xi)
+    expect = xi @ W.T
+    y = gemv.gemv_dequant(fmt, raw, n, k, xq, dx, cb)
+    assert np.array_equal(y, expect.astype(np.float64))
+    yi = gemv.gemv_intdot(fmt, raw, n, k, xq, dx, sx, cb)
+    assert np.array_equal(yi, expect.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_block_dots_equal_naive_python_sums(fmt):
+    n, k = 3, 512
+    raw = synth.weights(fmt, n, k, seed=6)
+    x = synth.activations(8, 2, k)
+    xq, _, _ = quantize_q8(x)
+    cb = _cb()
+    D = gemv.block_dots(fmt, raw, n, k, xq, cb)
+    f = formats.decode(fmt, raw, n, k)
+    q = f["q"].reshape(n, k)
+    g = 16 if fmt == "q6_k" else 32
+    for t in range(2):
+        for r in range(n):
+            for b in range(k // g):
+                acc = 0
+                for i in range(b * g, b * g + g):
+                    c = int(q[r, i])
+                    if fmt == "q4_0":
+                        c -= 8
+                    elif fmt == "iq4_nl":
+                        c = int(cb[c])
+                    elif fmt == "q6_k":
+                        c -= 32
+                    acc += int(xq[t, i]) * c
+                assert D[t, r, b] == acc
+    assert np.abs(D).max() <= 32 * 127 * 127
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("k", [32, 64, 256])
+def test_exact_rationals_tiny(fmt, k):
+    if k % formats.BLOCK_ELEMS[fmt]:
+        pytest.skip("K below the super-block size")
+    n = 4
+    raw = synth.weights(fmt, n, k, seed=k)
+    x = synth.activations(k + 1, 1, k)
+    xq, dx, sx = quantize_q8(x)
+    cb = _cb()
+    y = gemv.gemv_dequant(fmt, raw, n, k, xq, dx, cb)[0]
+    w = formats.values(fmt, raw, n, k, cb)
+    for r in range(n):
+        exact = sum(Fraction(float(w[r, i])) * Fraction(float(dx[0, i // 32])) * int(xq[0, i])
+                    for i in range(k))
+        scale = sum(abs(Fraction(float(w[r, i])) * Fraction(float(dx[0, i // 32])) * int(xq[0, i]))
+                    for i in range(k))
+        assert abs(Fraction(float(y[r])) - exact) <= Fraction(1, 2 ** 50) * (scale + 1)
+
+
+def test_scale_linearity_q4_0():
+    n, k = 8, 256
+    rng = np.random.default_rng(2)
+    q = rng.integers(0, 16, (n, k // 32, 32))
+    d = rng.uniform(1e-3, 1e-2, (n, k // 32)).astype(np.float16).astype(np.float64)
+    r1 = formats.encode("q4_0", {"d": d, "q": q})
+    r2 = formats.encode("q4_0", {"d": 2 * d, "q": q})
+    x = synth.activations(3, 1, k)
+    xq, dx, _ = quantize_q8(x)
+    y1 = gemv.gemv_dequant("q4_0", r1, n, k, xq, dx)
+    y2 = gemv.gemv_dequant("q4_0", r2, n, k, xq, dx)
+    assert np.array_equal(2 * y1, y2)
+
+
+def test_rows_subset_matches_full():
+    n, k = 300, 512
+    raw = synth.weights("q6_k", n, k, seed=1)
+    x = synth.activations(2, 1, k)
+    xq, dx, _ = quantize_q8(x)
+    full = gemv.gemv_dequant("q6_k", raw, n, k, xq, dx)
+    rows = np.array([0, 7, 150, 299])
+    sub = gemv.gemv_rows("q6_k", raw, n, k, rows, xq, dx)
+    assert np.array_equal(sub, full[:, rows])
