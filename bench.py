@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized decode GEMV library on one MI355X.
+
+Headline: effective weight GB/s of the M=1 decode GEMVs at dense-layer shapes
+-- Q8_0 and Q4_K weights, K = 4096, N = 4096, 12288 and 24576 (six GEMVs per
+step; each is the activation quantizer plus the format's GEMV kernel) --
+and its fraction of the 8 TB/s HBM3E peak. One step = those six calls once,
+each on its own fp32 N(0, 1) activation vector. Weights rotate through
+enough copies (> 2 GiB) that every step reads them from HBM, not from the
+256 MB Infinity Cache or the L2s.
+
+Also reported (same run, after the timed region): microseconds per fused
+FFN sublayer (hidden 4096, intermediate 12288, Q4_K gate|up + Q6_K down),
+the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV and the MoE
+layer (256 experts, top-8 + shared, hidden 2048, intermediate 512) at M=1
+and M=16.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12           # B/s, MI355X HBM3E
+ROTATE_BYTES = 2 * 2 ** 30  # weights touched per rotation cycle
+METRIC = "effective weight GB/s (% of HBM peak) for M=1 quant GEMV; µs per fused FFN"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copies_for(nbytes, cap=4096):
+    return int(min(cap, max(2, -(-ROTATE_BYTES // max(1, nbytes)))))
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rotated(w_np, r):
+    import torch
+    base = dev(w_np)
+    return [base] + [base.clone() for _ in range(r - 1)]
+
+
+def time_calls(fn, calls, warm=5):
+    """Mean microseconds per call of fn(i), back to back, with HIP events."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        fn(warm + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def cpu_baseline(mats, k, budget_s=12.0):
+    """The oracle (dequantize to fp64, fp64 matvec) timed on this host's cores
+    over a bounded sample: the first rows of each headline matrix."""
+    import synth
+    from oracle import gemv as og
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    rows = 1024
+    done_bytes, t_used, reps = 0, 0.0, 0
+    samples = []
+    for fmt, n in mats:
+        w = synth.weights(fmt, rows, k, seed=7)
+        x = synth.activations(8, 1, k)
+        samples.append((fmt, w, x))
+    og.gemv_ref(samples[0][0], samples[0][1], rows, k, samples[0][2])  # warm-up
+    while t_used < budget_s:
+        for fmt, w, x in samples:
+            t0 = time.perf_counter()
+            og.gemv_ref(fmt, w, rows, k, x)
+            t_used += time.perf_counter() - t0
+            done_bytes += rows * synth.row_bytes(fmt, k)
+        reps += 1
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {
+        "value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": int(max(1, blas)),
+        "kind": "oracle",
+        "sample": (f"first {rows} rows of each of the six headline matrices ({reps} passes, "
+                   f"{t_used:.1f} s), fp64 dequantize + fp64 matvec; numpy BLAS threads={blas}, "
+                   f"host cores available={cores}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_quant_gemv_amd as qg
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    K = 4096
+    mats = [(f, n) for f in ("q8_0", "q4_k") for n in (4096, 12288, 24576)]
+    step_bytes = sum(n * synth.row_bytes(f, K) for f, n in mats)
+    R = copies_for(step_bytes)
+    log(f"setup: 6 matrices, {step_bytes / 1e6:.1f} MB per step, {R} rotating copies")
+    plans, ws, ws_m, xs, ys, W = [], [], [], [], [], []
+    for j, (f, n) in enumerate(mats):
+        g = qg.GEMV(f, n, K)
+        plans.append(g)
+        ws.append(g.workspace(1))
+        xs.append(dev(synth.activations(200 + j, 1, K)))
+        ys.append(torch.empty((1, n), dtype=torch.float32, device="cuda"))
+        W.append(rotated(synth.weights(f, n, K, seed=100 + j), R))
+    dom = mats.index(("q8_0", 24576))
+    dom_bytes = mats[dom][1] * synth.row_bytes("q8_0", K)
+    dom_alg = dom_bytes + K + (K // 32) * 4 + mats[dom][1] * 4   # weights + xq + dx + y
+    stream = torch.cuda.current_stream()
+
+    ev_pairs = []
+
+    def step(i, record):
+        r = i % R
+        for j, g in enumerate(plans):
+            g.quantize(xs[j], ws[j], stream=stream)
+            if record and j == dom:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.run_quantized(W[j][r], ws[j], 1, ys[j], stream=stream)
+                b.record(stream)
+                ev_pairs.append((a, b))
+            else:
+                g.run_quantized(W[j][r], ws[j], 1, ys[j], stream=stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dom_us = sum(a.elapsed_time(b) for a, b in ev_pairs) * 1e3 / len(ev_pairs)
+    achieved = dom_alg / (dom_us * 1e-6) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e3:.3f} ms wall), {value:.0f} GB/s; "
+        f"Q8_0 24576x4096 GEMV kernel {dom_us:.2f} us -> {achieved:.0f} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "M=1 decode GEMVs, K=4096, Q8_0 and Q4_K weights, N=4096/12288/24576 "
+                               "(activation quantizer + GEMV per call)",
+                   "m": 1, "k": K, "n": [4096, 12288, 24576], "formats": ["q8_0", "q4_k"],
+                   "weight_bytes_per_step": step_bytes, "rotating_copies": R},
+        "pct_hbm_peak": round(100 * value * 1e9 / HBM_PEAK, 2),
+        "roofline": {"bound": "hbm", "kernel": "gemv Q8_0 N=24576 K=4096 M=1",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                     "bytes_per_launch": dom_alg, "avg_kernel_us": round(dom_us, 3)},
+    }
+
+    if not args.no_extras:
+        out["extras"] = extras(qg, synth, torch)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(mats, K)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def extras(qg, synth, torch):
+    res = {}
+    # fused FFN (hidden 4096, inter 12288)
+    H, I = 4096, 12288
+    f = qg.FFN(H, I, "q4_k", "q6_k")
+    b_gu = 2 * I * synth.row_bytes("q4_k", H)
+    b_dn = H * synth.row_bytes("q6_k", I)
+    R = copies_for(b_gu + b_dn)
+    gus = rotated(synth.weights("q4_k", 2 * I, H, seed=300), R)
+    dns = rotated(synth.weights("q6_k", H, I, seed=301), R)
+    x = dev(synth.activations(302, 1, H))
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = f.workspace(1)
+    us = time_calls(lambda i: f.run(gus[i % R], dns[i % R], x, y=y, ws=ws), 100)
+    res["ffn_us"] = round(us, 3)
+    res["ffn_weight_gbps"] = round((b_gu + b_dn) / (us * 1e-6) / 1e9, 1)
+    log(f"ffn: {us:.2f} us per fused FFN, {res['ffn_weight_gbps']} GB/s")
+    del gus, dns
+    # IQ4_NL lm_head
+    N = 248320
+    cb = synth.codebook(1)
+    g = qg.GEMV("iq4_nl", N, 4096, codebook=cb)
+    b = N * synth.row_bytes("iq4_nl", 4096)
+    R = copies_for(b)
+    Ws = rotated(synth.weights("iq4_nl", N, 4096, seed=310), R)
+    x = dev(synth.activations(311, 1, 4096))
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    us = time_calls(lambda i: g.run(Ws[i % R], x, y=y), 20, warm=2)
+    res["lm_head_us"] = round(us, 2)
+    res["lm_head_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+    log(f"lm_head: {us:.1f} us, {res['lm_head_gbps']} GB/s")
+    del Ws
+    # Q4_0 2048 x 2048
+    g = qg.GEMV("q4_0", 2048, 2048)
+    b = 2048 * synth.row_bytes("q4_0", 2048)
+    R = copies_for(b, cap=1024)
+    base = dev(synth.weights("q4_0", 2048, 2048, seed=320))
+    Ws = [base] + [base.clone() for _ in range(R - 1)]
+    x = dev(synth.activations(321, 1, 2048))
+    y = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
+    us = time_calls(lambda i: g.run(Ws[i % R], x, y=y), 200)
+    res["q4_0_2048_us"] = round(us, 3)
+    res["q4_0_2048_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+    log(f"q4_0 2048x2048: {us:.2f} us, {res['q4_0_2048_gbps']} GB/s")
+    del Ws
+    # MoE
+    E, Hm, Im, Kt = 256, 2048, 512, 8
+    gu_all, dn_all = synth.moe_experts(330, E, Hm, Im)
+    gu_sh, dn_sh = synth.moe_experts(331, 1, Hm, Im)
+    wr = dev(synth.router_weights(332, E, Hm))
+    R = 4
+    GU = rotated(gu_all, R)
+    DN = rotated(dn_all, R)
+    gsh, dsh = dev(gu_sh), dev(dn_sh)
+    for m in (1, 16):
+        mo = qg.MoE(Hm, Im, E, Kt, "q4_0", max_m=m)
+        x = dev(synth.activations(333 + m, m, Hm))
+        y = torch.empty((m, Hm), dtype=torch.float32, device="cuda")
+        ws = mo.workspace(m)
+        us = time_calls(lambda i: mo.run(wr, GU[i % R], DN[i % R], gsh, dsh, x, y=y, ws=ws), 100)
+        res[f"moe_m{m}_us"] = round(us, 3)
+        log(f"moe m={m}: {us:.2f} us")
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,301 @@
+"""Python binding of libqgemv.so, the block-quantized decode GEMV library
+for AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/qgemv.h. Tensors are torch
+tensors on the GPU; streams are torch's current stream. There is no CPU
+fallback: importing this package raises if the library is missing, and every
+call raises RuntimeError on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first; the library then binds to it
+
+__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "debug_quantize", "lib_path", "LAYOUT_VERSION"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libqgemv.so")
+LAYOUT_VERSION = 1
+
+FORMATS = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "iq4_nl": 5}
+_KIND = {"gemv": 0, "ffn": 1, "moe": 2}
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+if not os.path.exists(_LIB):
+    raise ImportError(
+        f"{_LIB} is not built; run `python block_quant_gemv_amd/build.py` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(_LIB)
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("layout_version", ctypes.c_int32),
+        ("fmt", ctypes.c_int32), ("max_m", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("fmt_gateup", ctypes.c_int32), ("fmt_down", ctypes.c_int32),
+        ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64),
+        ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int32),
+        ("fmt_expert", ctypes.c_int32),
+        ("codebook16", ctypes.POINTER(ctypes.c_int8)),
+    ]
+
+
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64
+_lib.qgemv_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_Desc)]
+_lib.qgemv_destroy.argtypes = [_vp]
+_lib.qgemv_workspace_size.argtypes = [_vp, _i32, ctypes.POINTER(_sz)]
+_lib.qgemv_workspace_offset.argtypes = [_vp, _i32, ctypes.c_char_p, ctypes.POINTER(_sz)]
+_lib.qgemv_weight_bytes.argtypes = [_vp, _i32, ctypes.POINTER(_sz)]
+_lib.qgemv_run.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qffn_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qmoe_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qgemv_quantize.argtypes = [_vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qgemv_run_quantized.argtypes = [_vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qgemv_status_string.argtypes = [_i32]
+_lib.qgemv_status_string.restype = ctypes.c_char_p
+_lib.qgemv_last_error.restype = ctypes.c_char_p
+_lib.qgemv_debug_quantize.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
+_lib.qgemv_debug_block_dots.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp]
+for _f in ("qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
+           "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
+           "qgemv_debug_block_dots"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.qgemv_status_string(status).decode()
+        detail = _lib.qgemv_last_error().decode()
+        super().__init__(f"{where}: {msg} ({status}): {detail}")
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise QgemvError(rc, where)
+
+
+def _fmt_id(f):
+    if isinstance(f, str):
+        return FORMATS[f.lower()]
+    return int(f)
+
+
+def _dev(t: torch.Tensor, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class _Plan:
+    def __init__(self, desc: _Desc):
+        h = _vp()
+        _check(_lib.qgemv_create(ctypes.byref(h), ctypes.byref(desc)), "qgemv_create")
+        self._h = h
+        self.max_m = desc.max_m
+        self._ws = {}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.qgemv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, m: int) -> int:
+        b = _sz()
+        _check(_lib.qgemv_workspace_size(self._h, m, ctypes.byref(b)), "qgemv_workspace_size")
+        return b.value
+
+    def workspace_offset(self, m: int, name: str) -> int:
+        b = _sz()
+        _check(_lib.qgemv_workspace_offset(self._h, m, name.encode(), ctypes.byref(b)),
+               "qgemv_workspace_offset")
+        return b.value
+
+    def weight_bytes(self, which: int = 0) -> int:
+        b = _sz()
+        _check(_lib.qgemv_weight_bytes(self._h, which, ctypes.byref(b)), "qgemv_weight_bytes")
+        return b.value
+
+    def workspace(self, m: int, device=None) -> torch.Tensor:
+        """A cached workspace tensor for m tokens (reused across calls)."""
+        device = torch.device(device or torch.cuda.current_device())
+        key = (device.index, m)
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = torch.empty(self.workspace_size(m), dtype=torch.uint8, device=device)
+            self._ws[key] = ws
+        return ws
+
+    def ws_view(self, ws: torch.Tensor, m: int, name: str, dtype, count: int) -> torch.Tensor:
+        """View of a named workspace region as a 1-D tensor of `count` items."""
+        off = self.workspace_offset(m, name)
+        isz = torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + count * isz].view(dtype)
+
+    def _check_w(self, w, which, name):
+        _dev(w, torch.uint8, name)
+        need = self.weight_bytes(which)
+        if w.numel() < need:
+            raise ValueError(f"{name} has {w.numel()} bytes, needs {need}")
+        return w.data_ptr()
+
+
+class GEMV(_Plan):
+    """y[m, n] = W[n, k] . x[m, k] with W packed in `fmt` blocks."""
+
+    def __init__(self, fmt, n: int, k: int, max_m: int = 1, codebook=None):
+        d = _Desc()
+        d.kind, d.layout_version, d.fmt, d.max_m, d.n, d.k = 0, LAYOUT_VERSION, _fmt_id(fmt), max_m, n, k
+        self._cb = None
+        if codebook is not None:
+            cb = [int(v) for v in codebook]
+            self._cb = (ctypes.c_int8 * 16)(*cb)
+            d.codebook16 = ctypes.cast(self._cb, ctypes.POINTER(ctypes.c_int8))
+        super().__init__(d)
+        self.fmt, self.n, self.k = _fmt_id(fmt), n, k
+
+    def run(self, w, x, y=None, ws=None, stream=None):
+        m = x.shape[0] if x.dim() == 2 else 1
+        if x.dim() not in (1, 2) or x.shape[-1] != self.k:
+            raise ValueError(f"x must be [m, {self.k}]")
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        if y.numel() != m * self.n:
+            raise ValueError("y has the wrong size")
+        if ws is None:
+            ws = self.workspace(m, x.device)
+        wp = self._check_w(w, 0, "w")
+        _check(_lib.qgemv_run(self._h, wp, _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
+                              _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qgemv_run")
+        return y
+
+    def quantize(self, x, ws=None, stream=None):
+        """Quantize x[m, k] into the workspace (first half of run)."""
+        m = x.shape[0]
+        if ws is None:
+            ws = self.workspace(m, x.device)
+        _check(_lib.qgemv_quantize(self._h, _dev(x, torch.float32, "x"), m, _dev(ws, torch.uint8, "ws"),
+                                   ws.numel(), _stream(stream)), "qgemv_quantize")
+        return ws
+
+    def run_quantized(self, w, ws, m, y=None, stream=None):
+        """GEMV on activations already quantized into ws (second half of run)."""
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=ws.device)
+        _check(_lib.qgemv_run_quantized(self._h, self._check_w(w, 0, "w"), _dev(y, torch.float32, "y"), m,
+                                        _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+               "qgemv_run_quantized")
+        return y
+
+    def block_dots(self, w, xq, stream=None):
+        """Exact per-block int32 dot products (checking export)."""
+        m = xq.shape[0]
+        g = 16 if self.fmt == FORMATS["q6_k"] else 32
+        dots = torch.empty((m, self.n, self.k // g), dtype=torch.int32, device=xq.device)
+        wp = self._check_w(w, 0, "w")
+        _check(_lib.qgemv_debug_block_dots(self._h, wp, _dev(xq, torch.int8, "xq"),
+                                           _dev(dots, torch.int32, "dots"), m, _stream(stream)),
+               "qgemv_debug_block_dots")
+        return dots
+
+
+class FFN(_Plan):
+    """Fused FFN sublayer: down(silu(gate(x)) * up(x)), one stream, one workspace."""
+
+    def __init__(self, hidden: int, inter: int, fmt_gateup="q4_k", fmt_down="q6_k", max_m: int = 1,
+                 codebook=None):
+        d = _Desc()
+        d.kind, d.layout_version, d.max_m = 1, LAYOUT_VERSION, max_m
+        d.fmt_gateup, d.fmt_down, d.hidden, d.inter = _fmt_id(fmt_gateup), _fmt_id(fmt_down), hidden, inter
+        self._cb = None
+        if codebook is not None:
+            self._cb = (ctypes.c_int8 * 16)(*[int(v) for v in codebook])
+            d.codebook16 = ctypes.cast(self._cb, ctypes.POINTER(ctypes.c_int8))
+        super().__init__(d)
+        self.hidden, self.inter = hidden, inter
+
+    def run(self, w_gateup, w_down, x, y=None, ws=None, stream=None):
+        m = x.shape[0]
+        if x.shape[-1] != self.hidden:
+            raise ValueError(f"x must be [m, {self.hidden}]")
+        if y is None:
+            y = torch.empty((m, self.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = self.workspace(m, x.device)
+        _check(_lib.qffn_run(self._h, self._check_w(w_gateup, 0, "w_gateup"), self._check_w(w_down, 1, "w_down"),
+                             _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
+                             _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qffn_run")
+        return y
+
+
+class MoE(_Plan):
+    """MoE layer: fp32 router, top-k softmax, routed experts + shared expert."""
+
+    def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int, fmt_expert="q4_0",
+                 max_m: int = 1, codebook=None):
+        d = _Desc()
+        d.kind, d.layout_version, d.max_m = 2, LAYOUT_VERSION, max_m
+        d.hidden, d.inter, d.n_experts, d.top_k, d.fmt_expert = hidden, inter, n_experts, top_k, _fmt_id(fmt_expert)
+        self._cb = None
+        if codebook is not None:
+            self._cb = (ctypes.c_int8 * 16)(*[int(v) for v in codebook])
+            d.codebook16 = ctypes.cast(self._cb, ctypes.POINTER(ctypes.c_int8))
+        super().__init__(d)
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+
+    def run(self, w_router, w_gateup, w_down, w_shared_gateup, w_shared_down, x, y=None, ws=None,
+            stream=None):
+        m = x.shape[0]
+        if x.shape[-1] != self.hidden:
+            raise ValueError(f"x must be [m, {self.hidden}]")
+        if tuple(w_router.shape) != (self.n_experts, self.hidden):
+            raise ValueError("router must be [n_experts, hidden] fp32")
+        if y is None:
+            y = torch.empty((m, self.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = self.workspace(m, x.device)
+        _check(_lib.qmoe_run(self._h, _dev(w_router, torch.float32, "w_router"),
+                             self._check_w(w_gateup, 0, "w_gateup"), self._check_w(w_down, 1, "w_down"),
+                             self._check_w(w_shared_gateup, 2, "w_shared_gateup"),
+                             self._check_w(w_shared_down, 3, "w_shared_down"),
+                             _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
+                             _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qmoe_run")
+        return y
+
+
+def debug_quantize(x: torch.Tensor, stream=None):
+    """Device activation quantizer alone: returns (xq int8, dx fp32, sx int32)."""
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    dx = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    sx = torch.empty((m, k // 32), dtype=torch.int32, device=x.device)
+    _check(_lib.qgemv_debug_quantize(_dev(x, torch.float32, "x"), xq.data_ptr(), dx.data_ptr(), sx.data_ptr(),
+                                     m, k, _stream(stream)), "qgemv_debug_quantize")
+    return xq, dx, sx

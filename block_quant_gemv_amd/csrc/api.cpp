@@ -1,0 +1,487 @@
+// C-ABI layer: plan validation, workspace layout and kernel launches.
+//
+// Every entry point validates its arguments on the host before it enqueues
+// anything, returns a status code and never aborts, throws or prints -- the
+// convention of the pure-C device module in "01 · Phase overview: from 2B to
+// 8B to MoE" (icman.com.cn, section 一 and ledger item ①), without its CPU
+// fallback: an error is reported, never silently degraded (the same page's
+// ledger item ⑤ on explicit warnings instead of silent slowdowns).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/qgemv.h"
+#include "internal.h"
+#include "moe.h"
+#include "mfma.h"
+#include "swiglu.h"
+
+using namespace qg;
+
+struct qgemv_plan {
+  qgemv_desc d;
+  int8_t cb[16];
+  uint32_t cbw[4];
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_block_fmt(int f) { return f >= QFMT_Q4_0 && f <= QFMT_IQ4_NL; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Named regions of a workspace, in order, each 256-byte aligned.
+struct Region { const char* name; size_t bytes; };
+
+struct Layout {
+  Region r[24];
+  int n = 0;
+  void add(const char* name, size_t bytes) { r[n++] = Region{name, bytes}; }
+  size_t offset(const char* name, bool* found) const {
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) {
+      if (strcmp(r[i].name, name) == 0) { *found = true; return off; }
+      off += round_up(r[i].bytes, 256);
+    }
+    *found = false;
+    return 0;
+  }
+  size_t total() const {
+    size_t off = 0;
+    for (int i = 0; i < n; ++i) off += round_up(r[i].bytes, 256);
+    return off;
+  }
+};
+
+Layout layout_of(const qgemv_plan* h, int m) {
+  Layout L;
+  const qgemv_desc& d = h->d;
+  if (d.kind == QKIND_GEMV) {
+    L.add("xq", (size_t)m * d.k);
+    L.add("dx", (size_t)m * (d.k / 32) * 4);
+    L.add("sx", (size_t)m * (d.k / 32) * 4);
+  } else if (d.kind == QKIND_FFN) {
+    L.add("xq", (size_t)m * d.hidden);
+    L.add("dx", (size_t)m * (d.hidden / 32) * 4);
+    L.add("sx", (size_t)m * (d.hidden / 32) * 4);
+    L.add("gu", (size_t)m * 2 * d.inter * 4);
+    L.add("h", (size_t)m * d.inter * 4);
+    L.add("hq", (size_t)m * d.inter);
+    L.add("hd", (size_t)m * (d.inter / 32) * 4);
+    L.add("hs", (size_t)m * (d.inter / 32) * 4);
+  } else {
+    const size_t slots = (size_t)m * (d.top_k + 1);
+    L.add("logits", (size_t)m * d.n_experts * 4);
+    L.add("ids", (size_t)m * d.top_k * 4);
+    L.add("wts", (size_t)m * d.top_k * 4);
+    L.add("xq", (size_t)m * d.hidden);
+    L.add("dx", (size_t)m * (d.hidden / 32) * 4);
+    L.add("sx", (size_t)m * (d.hidden / 32) * 4);
+    L.add("gu", slots * 2 * d.inter * 4);
+    L.add("h", slots * d.inter * 4);
+    L.add("hq", slots * d.inter);
+    L.add("hd", slots * (d.inter / 32) * 4);
+    L.add("hs", slots * (d.inter / 32) * 4);
+    L.add("out", slots * d.hidden * 4);
+    L.add("tbl", (size_t)moe_table_ints(m, d.top_k) * 4);
+  }
+  return L;
+}
+
+template <typename T>
+T* region(void* ws, const Layout& L, const char* name) {
+  bool found = false;
+  const size_t off = L.offset(name, &found);
+  return found ? reinterpret_cast<T*>(static_cast<char*>(ws) + off) : nullptr;
+}
+
+bool fault_injected() {
+  const char* e = getenv("QGEMV_FAULT");
+  return e && strcmp(e, "launch") == 0;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QGEMV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return QGEMV_OK;
+}
+
+int check_gemv_shape(int fmt, int64_t n, int64_t k, const char* what) {
+  if (!is_block_fmt(fmt)) return fail(QGEMV_EFORMAT, "%s: format %d is not a block format", what, fmt);
+  const int be = fmt_block_elems(fmt);
+  if (n < 1 || n > (int64_t)1 << 31) return fail(QGEMV_ESHAPE, "%s: N=%lld out of range", what, (long long)n);
+  if (k < be || k % be || k > 65536)
+    return fail(QGEMV_ESHAPE, "%s: K=%lld must be a multiple of %d in [%d, 65536]", what, (long long)k, be, be);
+  return QGEMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qgemv_status_string(int s) {
+  switch (s) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_EINVAL: return "invalid argument";
+    case QGEMV_EFORMAT: return "unsupported format";
+    case QGEMV_ESHAPE: return "shape out of range";
+    case QGEMV_EALIGN: return "misaligned pointer";
+    case QGEMV_EWORKSPACE: return "workspace too small";
+    case QGEMV_EVERSION: return "layout version mismatch";
+    case QGEMV_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* qgemv_last_error(void) { return g_err; }
+
+int qgemv_create(qgemv_t* out, const qgemv_desc* d) {
+  if (!out || !d) return fail(QGEMV_EINVAL, "qgemv_create: null argument");
+  *out = nullptr;
+  if (d->layout_version != QGEMV_LAYOUT_VERSION)
+    return fail(QGEMV_EVERSION, "qgemv_create: layout version %d, library has %d", d->layout_version,
+                QGEMV_LAYOUT_VERSION);
+  int rc;
+  bool need_cb = false;
+  switch (d->kind) {
+    case QKIND_GEMV:
+      if ((rc = check_gemv_shape(d->fmt, d->n, d->k, "gemv")) != QGEMV_OK) return rc;
+      if (d->max_m < 1 || d->max_m > 32) return fail(QGEMV_ESHAPE, "gemv: max_m=%d not in 1..32", d->max_m);
+      need_cb = d->fmt == QFMT_IQ4_NL;
+      break;
+    case QKIND_FFN:
+      if ((rc = check_gemv_shape(d->fmt_gateup, 2 * d->inter, d->hidden, "ffn gate|up")) != QGEMV_OK) return rc;
+      if ((rc = check_gemv_shape(d->fmt_down, d->hidden, d->inter, "ffn down")) != QGEMV_OK) return rc;
+      if (d->max_m < 1 || d->max_m > kGemvMaxTokens)
+        return fail(QGEMV_ESHAPE, "ffn: max_m=%d not in 1..%d", d->max_m, kGemvMaxTokens);
+      need_cb = d->fmt_gateup == QFMT_IQ4_NL || d->fmt_down == QFMT_IQ4_NL;
+      break;
+    case QKIND_MOE:
+      if (d->n_experts < 1 || d->n_experts > 4096)
+        return fail(QGEMV_ESHAPE, "moe: n_experts=%lld not in 1..4096", (long long)d->n_experts);
+      if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts)
+        return fail(QGEMV_ESHAPE, "moe: top_k=%d not in 1..min(16, n_experts)", d->top_k);
+      if (d->hidden % 32)
+        return fail(QGEMV_ESHAPE, "moe: hidden=%lld must be a multiple of 32", (long long)d->hidden);
+      if ((rc = check_gemv_shape(d->fmt_expert, 2 * d->inter, d->hidden, "moe gate|up")) != QGEMV_OK) return rc;
+      if ((rc = check_gemv_shape(d->fmt_expert, d->hidden, d->inter, "moe down")) != QGEMV_OK) return rc;
+      if (d->max_m < 1 || d->max_m > kGemvMaxTokens)
+        return fail(QGEMV_ESHAPE, "moe: max_m=%d not in 1..%d", d->max_m, kGemvMaxTokens);
+      need_cb = d->fmt_expert == QFMT_IQ4_NL;
+      break;
+    default:
+      return fail(QGEMV_EINVAL, "qgemv_create: unknown kind %d", d->kind);
+  }
+  if (d->kind != QKIND_GEMV && d->inter % 32)
+    return fail(QGEMV_ESHAPE, "inter=%lld must be a multiple of 32", (long long)d->inter);
+  qgemv_plan* p = new (std::nothrow) qgemv_plan;
+  if (!p) return fail(QGEMV_EINVAL, "qgemv_create: out of host memory");
+  p->d = *d;
+  p->d.codebook16 = nullptr;
+  memset(p->cb, 0, sizeof p->cb);
+  memset(p->cbw, 0, sizeof p->cbw);
+  if (need_cb) {
+    if (!d->codebook16) {
+      delete p;
+      return fail(QGEMV_EINVAL, "IQ4_NL needs a 16-entry codebook");
+    }
+    for (int i = 0; i < 16; ++i) p->cb[i] = d->codebook16[i];
+    for (int i = 1; i < 16; ++i)
+      if (p->cb[i] <= p->cb[i - 1]) {
+        delete p;
+        return fail(QGEMV_EINVAL, "IQ4_NL codebook must be strictly ascending");
+      }
+    memcpy(p->cbw, p->cb, 16);
+  }
+  *out = p;
+  return QGEMV_OK;
+}
+
+int qgemv_destroy(qgemv_t h) {
+  delete h;
+  return QGEMV_OK;
+}
+
+int qgemv_workspace_size(qgemv_t h, int m, size_t* bytes) {
+  if (!h || !bytes) return fail(QGEMV_EINVAL, "qgemv_workspace_size: null argument");
+  if (m < 1 || m > h->d.max_m) return fail(QGEMV_ESHAPE, "m=%d not in 1..%d", m, h->d.max_m);
+  *bytes = layout_of(h, m).total();
+  return QGEMV_OK;
+}
+
+int qgemv_workspace_offset(qgemv_t h, int m, const char* name, size_t* offset) {
+  if (!h || !name || !offset) return fail(QGEMV_EINVAL, "qgemv_workspace_offset: null argument");
+  if (m < 1 || m > h->d.max_m) return fail(QGEMV_ESHAPE, "m=%d not in 1..%d", m, h->d.max_m);
+  bool found = false;
+  *offset = layout_of(h, m).offset(name, &found);
+  if (!found) return fail(QGEMV_EINVAL, "workspace has no region '%s'", name);
+  return QGEMV_OK;
+}
+
+int qgemv_weight_bytes(qgemv_t h, int which, size_t* bytes) {
+  if (!h || !bytes) return fail(QGEMV_EINVAL, "qgemv_weight_bytes: null argument");
+  const qgemv_desc& d = h->d;
+  size_t b = 0;
+  if (d.kind == QKIND_GEMV && which == 0) b = (size_t)d.n * fmt_row_bytes(d.fmt, d.k);
+  else if (d.kind == QKIND_FFN && which == 0) b = (size_t)2 * d.inter * fmt_row_bytes(d.fmt_gateup, d.hidden);
+  else if (d.kind == QKIND_FFN && which == 1) b = (size_t)d.hidden * fmt_row_bytes(d.fmt_down, d.inter);
+  else if (d.kind == QKIND_MOE && (which == 0 || which == 2))
+    b = (size_t)(which == 0 ? d.n_experts : 1) * 2 * d.inter * fmt_row_bytes(d.fmt_expert, d.hidden);
+  else if (d.kind == QKIND_MOE && (which == 1 || which == 3))
+    b = (size_t)(which == 1 ? d.n_experts : 1) * d.hidden * fmt_row_bytes(d.fmt_expert, d.inter);
+  else if (d.kind == QKIND_MOE && which == 4) b = (size_t)d.n_experts * d.hidden * 4;
+  else return fail(QGEMV_EINVAL, "weight buffer %d does not exist for this plan", which);
+  *bytes = round_up(b, 16);
+  return QGEMV_OK;
+}
+
+namespace {
+
+int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const char* fn) {
+  if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);
+  if (!ws) return fail(QGEMV_EINVAL, "%s: null workspace", fn);
+  if (!aligned(ws, 256)) return fail(QGEMV_EALIGN, "%s: ws needs 256-byte alignment", fn);
+  if (m < 1 || m > h->d.max_m) return fail(QGEMV_ESHAPE, "%s: m=%d not in 1..%d", fn, m, h->d.max_m);
+  const size_t need = layout_of(h, m).total();
+  if (ws_bytes < need) return fail(QGEMV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return QGEMV_OK;
+}
+
+int gemv_quantize(qgemv_t h, const float* x, int m, void* ws, hipStream_t s) {
+  const Layout L = layout_of(h, m);
+  return check_launch(launch_quant_q8(x, region<int8_t>(ws, L, "xq"), region<float>(ws, L, "dx"),
+                                      region<int32_t>(ws, L, "sx"), (int64_t)m * (h->d.k / 32), s),
+                      "quantize");
+}
+
+int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* ws, hipStream_t s) {
+  const qgemv_desc& d = h->d;
+  const Layout L = layout_of(h, m);
+  void* wsm = const_cast<void*>(ws);
+  const int8_t* xq = region<int8_t>(wsm, L, "xq");
+  const float* dx = region<float>(wsm, L, "dx");
+  const int32_t* sx = region<int32_t>(wsm, L, "sx");
+  if (m > kGemvMaxTokens && mfma_supported(d.fmt))
+    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y, d.n, d.k, m, s),
+                        "gemm32");
+  GemvProblem p;
+  p.w = static_cast<const uint8_t*>(w);
+  p.xq = xq;
+  p.dx = dx;
+  p.xs = d.k;
+  p.y = y;
+  p.ldy = d.n;
+  p.n = d.n;
+  p.k = d.k;
+  memcpy(p.cb, h->cbw, sizeof p.cb);
+  for (int t0 = 0; t0 < m; t0 += kGemvMaxTokens) {
+    GemvProblem c = p;
+    c.m = (m - t0) < kGemvMaxTokens ? (m - t0) : kGemvMaxTokens;
+    c.xq = xq + (int64_t)t0 * d.k;
+    c.dx = dx + (int64_t)t0 * (d.k / 32);
+    c.y = y + (int64_t)t0 * d.n;
+    int rc = check_launch(launch_gemv(d.fmt, c, false, s), "gemv");
+    if (rc) return rc;
+  }
+  return QGEMV_OK;
+}
+
+}  // namespace
+
+int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* ws, size_t ws_bytes,
+              void* stream) {
+  int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_run");
+  if (rc) return rc;
+  if (!w || !x || !y) return fail(QGEMV_EINVAL, "qgemv_run: null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return fail(QGEMV_EALIGN, "qgemv_run: w and x need 16-byte, y 4-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run: launch failure injected (QGEMV_FAULT)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
+  return gemv_from_quantized(h, w, y, m, ws, s);
+}
+
+int qgemv_quantize(qgemv_t h, const float* x, int m, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_quantize");
+  if (rc) return rc;
+  if (!x) return fail(QGEMV_EINVAL, "qgemv_quantize: null pointer");
+  if (!aligned(x, 16)) return fail(QGEMV_EALIGN, "qgemv_quantize: x needs 16-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_quantize: launch failure injected (QGEMV_FAULT)");
+  return gemv_quantize(h, x, m, ws, static_cast<hipStream_t>(stream));
+}
+
+int qgemv_run_quantized(qgemv_t h, const void* w, float* y, int m, const void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_run_quantized");
+  if (rc) return rc;
+  if (!w || !y) return fail(QGEMV_EINVAL, "qgemv_run_quantized: null pointer");
+  if (!aligned(w, 16) || !aligned(y, 4))
+    return fail(QGEMV_EALIGN, "qgemv_run_quantized: w needs 16-byte, y 4-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run_quantized: launch failure injected (QGEMV_FAULT)");
+  return gemv_from_quantized(h, w, y, m, ws, static_cast<hipStream_t>(stream));
+}
+
+int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x, float* y, int m,
+             void* ws, size_t ws_bytes, void* stream) {
+  if (!h || h->d.kind != QKIND_FFN) return fail(QGEMV_EINVAL, "qffn_run: not an FFN plan");
+  if (!w_gateup || !w_down || !x || !y || !ws) return fail(QGEMV_EINVAL, "qffn_run: null pointer");
+  if (!aligned(w_gateup, 16) || !aligned(w_down, 16) || !aligned(x, 16) || !aligned(y, 4) ||
+      !aligned(ws, 256))
+    return fail(QGEMV_EALIGN, "qffn_run: weights and x need 16-byte, y 4-byte, ws 256-byte alignment");
+  const qgemv_desc& d = h->d;
+  if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qffn_run: m=%d not in 1..%d", m, d.max_m);
+  const Layout L = layout_of(h, m);
+  if (ws_bytes < L.total())
+    return fail(QGEMV_EWORKSPACE, "qffn_run: workspace %zu < %zu bytes", ws_bytes, L.total());
+  if (fault_injected()) return fail(QGEMV_EHIP, "qffn_run: launch failure injected (QGEMV_FAULT)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int8_t* xq = region<int8_t>(ws, L, "xq");
+  float* dx = region<float>(ws, L, "dx");
+  int32_t* sx = region<int32_t>(ws, L, "sx");
+  float* gu = region<float>(ws, L, "gu");
+  float* hh = region<float>(ws, L, "h");
+  int8_t* hq = region<int8_t>(ws, L, "hq");
+  float* hd = region<float>(ws, L, "hd");
+  int32_t* hs = region<int32_t>(ws, L, "hs");
+  int rc = check_launch(launch_quant_q8(x, xq, dx, sx, (int64_t)m * (d.hidden / 32), s), "quantize");
+  if (rc) return rc;
+  GemvProblem p;
+  p.w = static_cast<const uint8_t*>(w_gateup);
+  p.xq = xq;
+  p.dx = dx;
+  p.xs = d.hidden;
+  p.y = gu;
+  p.ldy = 2 * d.inter;
+  p.n = 2 * d.inter;
+  p.k = d.hidden;
+  p.m = m;
+  memcpy(p.cb, h->cbw, sizeof p.cb);
+  if ((rc = check_launch(launch_gemv(d.fmt_gateup, p, false, s), "gate|up gemv"))) return rc;
+  if ((rc = check_launch(launch_swiglu_q8(gu, 2 * d.inter, hh, hq, hd, hs, m, d.inter, s), "swiglu")))
+    return rc;
+  GemvProblem q = p;
+  q.w = static_cast<const uint8_t*>(w_down);
+  q.xq = hq;
+  q.dx = hd;
+  q.xs = d.inter;
+  q.y = y;
+  q.ldy = d.hidden;
+  q.n = d.hidden;
+  q.k = d.inter;
+  return check_launch(launch_gemv(d.fmt_down, q, false, s), "down gemv");
+}
+
+int qmoe_run(qgemv_t h, const float* w_router, const void* w_experts_gateup, const void* w_experts_down,
+             const void* w_shared_gateup, const void* w_shared_down, const float* x, float* y, int m,
+             void* ws, size_t ws_bytes, void* stream) {
+  if (!h || h->d.kind != QKIND_MOE) return fail(QGEMV_EINVAL, "qmoe_run: not a MoE plan");
+  if (!w_router || !w_experts_gateup || !w_experts_down || !w_shared_gateup || !w_shared_down || !x ||
+      !y || !ws)
+    return fail(QGEMV_EINVAL, "qmoe_run: null pointer");
+  if (!aligned(w_router, 16) || !aligned(w_experts_gateup, 16) || !aligned(w_experts_down, 16) ||
+      !aligned(w_shared_gateup, 16) || !aligned(w_shared_down, 16) || !aligned(x, 16) ||
+      !aligned(y, 4) || !aligned(ws, 256))
+    return fail(QGEMV_EALIGN, "qmoe_run: weights and x need 16-byte, y 4-byte, ws 256-byte alignment");
+  const qgemv_desc& d = h->d;
+  if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qmoe_run: m=%d not in 1..%d", m, d.max_m);
+  const int64_t gu_bytes = 2 * d.inter * fmt_row_bytes(d.fmt_expert, d.hidden);
+  const int64_t dn_bytes = d.hidden * fmt_row_bytes(d.fmt_expert, d.inter);
+  if (gu_bytes % 16 || dn_bytes % 16)
+    return fail(QGEMV_ESHAPE, "qmoe_run: expert matrices must be multiples of 16 bytes");
+  const Layout L = layout_of(h, m);
+  if (ws_bytes < L.total())
+    return fail(QGEMV_EWORKSPACE, "qmoe_run: workspace %zu < %zu bytes", ws_bytes, L.total());
+  if (fault_injected()) return fail(QGEMV_EHIP, "qmoe_run: launch failure injected (QGEMV_FAULT)");
+  MoeCall c;
+  c.router = w_router;
+  c.gu = static_cast<const uint8_t*>(w_experts_gateup);
+  c.dn = static_cast<const uint8_t*>(w_experts_down);
+  c.gu_shared = static_cast<const uint8_t*>(w_shared_gateup);
+  c.dn_shared = static_cast<const uint8_t*>(w_shared_down);
+  c.gu_stride = gu_bytes;
+  c.dn_stride = dn_bytes;
+  c.x = x;
+  c.y = y;
+  c.m = m;
+  c.hidden = d.hidden;
+  c.inter = d.inter;
+  c.n_experts = (int)d.n_experts;
+  c.top_k = d.top_k;
+  c.fmt = d.fmt_expert;
+  memcpy(c.cb, h->cbw, sizeof c.cb);
+  c.logits = region<float>(ws, L, "logits");
+  c.ids = region<int32_t>(ws, L, "ids");
+  c.wts = region<float>(ws, L, "wts");
+  c.xq = region<int8_t>(ws, L, "xq");
+  c.dx = region<float>(ws, L, "dx");
+  c.sx = region<int32_t>(ws, L, "sx");
+  c.gu_out = region<float>(ws, L, "gu");
+  c.h = region<float>(ws, L, "h");
+  c.hq = region<int8_t>(ws, L, "hq");
+  c.hd = region<float>(ws, L, "hd");
+  c.hs = region<int32_t>(ws, L, "hs");
+  c.out = region<float>(ws, L, "out");
+  c.tbl = region<int32_t>(ws, L, "tbl");
+  return check_launch(launch_moe(c, static_cast<hipStream_t>(stream)), "moe");
+}
+
+int qgemv_debug_quantize(const float* x, int8_t* xq, float* dx, int32_t* sx, int m, int64_t k, void* stream) {
+  if (!x || !xq || !dx || !sx) return fail(QGEMV_EINVAL, "qgemv_debug_quantize: null pointer");
+  if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(dx, 4) || !aligned(sx, 4))
+    return fail(QGEMV_EALIGN, "qgemv_debug_quantize: x needs 16-byte, outputs 4-byte alignment");
+  if (m < 1 || k < 32 || k % 32) return fail(QGEMV_ESHAPE, "qgemv_debug_quantize: bad m/k");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_quantize: launch failure injected");
+  return check_launch(launch_quant_q8(x, xq, dx, sx, (int64_t)m * (k / 32), static_cast<hipStream_t>(stream)),
+                      "quantize");
+}
+
+int qgemv_debug_block_dots(qgemv_t h, const void* w, const int8_t* xq, int32_t* dots, int m, void* stream) {
+  if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "qgemv_debug_block_dots: not a GEMV plan");
+  if (!w || !xq || !dots) return fail(QGEMV_EINVAL, "qgemv_debug_block_dots: null pointer");
+  if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(dots, 4))
+    return fail(QGEMV_EALIGN, "qgemv_debug_block_dots: w and xq need 16-byte alignment");
+  const qgemv_desc& d = h->d;
+  if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qgemv_debug_block_dots: m=%d not in 1..%d", m, d.max_m);
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots: launch failure injected");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m > kGemvMaxTokens && mfma_supported(d.fmt))
+    return check_launch(launch_gemm32_dots(d.fmt, static_cast<const uint8_t*>(w), xq, dots, d.n, d.k, m, s),
+                        "gemm32 dots");
+  GemvProblem p;
+  p.w = static_cast<const uint8_t*>(w);
+  p.xq = xq;
+  p.dx = nullptr;  // the integer epilogue never reads scales
+  p.xs = d.k;
+  p.dots = dots;
+  p.n = d.n;
+  p.k = d.k;
+  memcpy(p.cb, h->cbw, sizeof p.cb);
+  const int64_t per_tok = d.n * (d.k / (d.fmt == QFMT_Q6_K ? 16 : 32));
+  for (int t0 = 0; t0 < m; t0 += kGemvMaxTokens) {
+    GemvProblem c = p;
+    c.m = (m - t0) < kGemvMaxTokens ? (m - t0) : kGemvMaxTokens;
+    c.xq = xq + (int64_t)t0 * d.k;
+    c.dots = dots + (int64_t)t0 * per_tok;
+    int rc = check_launch(launch_gemv(d.fmt, c, true, s), "block dots");
+    if (rc) return rc;
+  }
+  return QGEMV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+enum Fmt { kF32 = 0, kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3, kQ6_K = 4, kIQ4_NL = 5 };
+
+// Elements and bytes of one block of each format (0 for F32).
+int fmt_block_elems(int fmt);
+int fmt_block_bytes(int fmt);
+int64_t fmt_row_bytes(int fmt, int64_t k);  // -1 if k is not a multiple of the block
+
+// One GEMV launch: y[t, r] = sum_k W[r, k] x_hat[t, k] for t < m, r < n.
+// Activations are already quantized (xq int8, token stride xs elements; dx
+// fp32, token stride xs/32).
+//
+// Grouped mode (tbl != nullptr, used by the MoE layer): grid.y runs over
+// `nprob` problems. tbl[0] holds the number of routed problems in use;
+// routed problem p is described at tbl + 1 + p * tbl_stride as
+// {expert, count, rows[count]} and uses matrix w + expert * w_stride; the
+// last problem (p == nprob - 1) is the shared expert w_shared applied to all
+// m tokens, whose rows are t * slots + slots - 1. For every problem, token j
+// reads activation row rows[j] / act_div and writes output row rows[j].
+struct GemvProblem {
+  const uint8_t* w = nullptr;
+  const int8_t* xq = nullptr;
+  const float* dx = nullptr;
+  int64_t xs = 0;
+  float* y = nullptr;
+  int64_t ldy = 0;
+  int32_t* dots = nullptr;  // checking epilogue output (int32)
+  int64_t n = 0;
+  int64_t k = 0;
+  int m = 1;
+  uint32_t cb[4] = {0, 0, 0, 0};  // IQ4_NL codebook, 16 int8 little-endian
+  const int32_t* tbl = nullptr;
+  int tbl_stride = 0;
+  int nprob = 1;
+  int64_t w_stride = 0;
+  const uint8_t* w_shared = nullptr;
+  int slots = 1;
+  int act_div = 1;
+};
+
+hipError_t launch_quant_q8(const float* x, int8_t* xq, float* dx, int32_t* sx,
+                           int64_t nblocks, hipStream_t s);
+
+// Row GEMV over packed blocks for m <= 16 tokens (chunks larger m on the
+// host). dots_epilogue selects the integer-store checking epilogue.
+hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStream_t s);
+
+// Largest token count one GEMV launch handles.
+constexpr int kGemvMaxTokens = 16;
+
+}  // namespace qg

@@ -1,0 +1,41 @@
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+// Buffers and shapes of one MoE layer call (all device pointers).
+struct MoeCall {
+  const float* router = nullptr;  // fp32 [n_experts, hidden]
+  const uint8_t *gu = nullptr, *dn = nullptr, *gu_shared = nullptr, *dn_shared = nullptr;
+  int64_t gu_stride = 0, dn_stride = 0;  // bytes between experts
+  const float* x = nullptr;              // fp32 [m, hidden]
+  float* y = nullptr;                    // fp32 [m, hidden]
+  int m = 1;
+  int64_t hidden = 0, inter = 0;
+  int n_experts = 0, top_k = 0, fmt = 0;
+  uint32_t cb[4] = {0, 0, 0, 0};
+  // workspace regions
+  float* logits = nullptr;   // [m, n_experts]
+  int32_t* ids = nullptr;    // [m, top_k]
+  float* wts = nullptr;      // [m, top_k]
+  int8_t* xq = nullptr;      // [m, hidden]
+  float* dx = nullptr;       // [m, hidden/32]
+  int32_t* sx = nullptr;
+  float* gu_out = nullptr;   // [m*(top_k+1), 2*inter] (slot rows)
+  float* h = nullptr;        // [m*(top_k+1), inter]
+  int8_t* hq = nullptr;
+  float* hd = nullptr;
+  int32_t* hs = nullptr;
+  float* out = nullptr;      // [m*(top_k+1), hidden]
+  int32_t* tbl = nullptr;    // grouping table, moe_table_ints(m, top_k) ints
+};
+
+// int32 entries of the expert grouping table for m tokens and top_k slots.
+int64_t moe_table_ints(int m, int top_k);
+
+hipError_t launch_moe(const MoeCall& c, hipStream_t s);
+
+}  // namespace qg

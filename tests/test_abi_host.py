@@ -1,0 +1,150 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every function include/qgemv.h declares, the descriptor layout matches the
+binding, and every validation error is reported before anything touches the
+device."""
+import ctypes
+import os
+import re
+import subprocess
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+qg = pytest.importorskip("block_quant_gemv_amd", reason="libqgemv.so not built")
+lib = qg._lib
+
+OK, EINVAL, EFORMAT, ESHAPE, EALIGN, EWORKSPACE, EVERSION, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.lib_path()], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_descriptor_layout_matches_c(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text(textwrap.dedent(f"""
+        #include <stdio.h>
+        #include <stddef.h>
+        #include "{HEADER}"
+        int main(void) {{
+          printf("%zu %zu %zu %zu %zu\\n", sizeof(qgemv_desc), offsetof(qgemv_desc, n),
+                 offsetof(qgemv_desc, hidden), offsetof(qgemv_desc, n_experts),
+                 offsetof(qgemv_desc, codebook16));
+          return 0;
+        }}"""))
+    exe = tmp_path / "sz"
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    D = qg._Desc
+    assert got == [ctypes.sizeof(D), D.n.offset, D.hidden.offset, D.n_experts.offset, D.codebook16.offset]
+
+
+def _desc(**kw):
+    d = qg._Desc()
+    d.kind, d.layout_version, d.fmt, d.max_m, d.n, d.k = 0, 1, 1, 1, 64, 256
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _create(d):
+    h = ctypes.c_void_p()
+    rc = lib.qgemv_create(ctypes.byref(h), ctypes.byref(d))
+    return rc, h
+
+
+def test_create_validation():
+    assert _create(_desc(layout_version=2))[0] == EVERSION
+    assert _create(_desc(fmt=0))[0] == EFORMAT
+    assert _create(_desc(fmt=9))[0] == EFORMAT
+    assert _create(_desc(k=48))[0] == ESHAPE
+    assert _create(_desc(fmt=3, k=128))[0] == ESHAPE          # Q4_K needs K % 256 == 0
+    assert _create(_desc(n=0))[0] == ESHAPE
+    assert _create(_desc(max_m=0))[0] == ESHAPE
+    assert _create(_desc(max_m=33))[0] == ESHAPE
+    assert _create(_desc(kind=7))[0] == EINVAL
+    assert _create(_desc(fmt=5))[0] == EINVAL                 # IQ4_NL without codebook
+    bad = (ctypes.c_int8 * 16)(*([5] * 16))
+    assert _create(_desc(fmt=5, codebook16=ctypes.cast(bad, ctypes.POINTER(ctypes.c_int8))))[0] == EINVAL
+    assert b"ascending" in lib.qgemv_last_error()
+    good = (ctypes.c_int8 * 16)(*range(-8, 8))
+    rc, h = _create(_desc(fmt=5, codebook16=ctypes.cast(good, ctypes.POINTER(ctypes.c_int8))))
+    assert rc == OK and h.value
+    lib.qgemv_destroy(h)
+    assert lib.qgemv_create(None, None) == EINVAL
+
+
+def test_ffn_and_moe_validation():
+    d = _desc(kind=1, fmt=0, fmt_gateup=3, fmt_down=4, hidden=4096, inter=12288)
+    rc, h = _create(d)
+    assert rc == OK
+    lib.qgemv_destroy(h)
+    assert _create(_desc(kind=1, fmt_gateup=3, fmt_down=4, hidden=4096, inter=12300))[0] == ESHAPE
+    assert _create(_desc(kind=1, fmt_gateup=3, fmt_down=4, hidden=4096, inter=12288, max_m=17))[0] == ESHAPE
+    m = dict(kind=2, hidden=2048, inter=512, n_experts=256, top_k=8, fmt_expert=1)
+    rc, h = _create(_desc(**m))
+    assert rc == OK
+    lib.qgemv_destroy(h)
+    assert _create(_desc(**{**m, "top_k": 0}))[0] == ESHAPE
+    assert _create(_desc(**{**m, "top_k": 17}))[0] == ESHAPE
+    assert _create(_desc(**{**m, "n_experts": 4, "top_k": 8}))[0] == ESHAPE
+
+
+def test_workspace_and_weight_sizes():
+    rc, h = _create(_desc(fmt=3, n=12288, k=4096, max_m=4))
+    assert rc == OK
+    b = ctypes.c_size_t()
+    assert lib.qgemv_workspace_size(h, 1, ctypes.byref(b)) == OK and b.value >= 4096 + 2 * 512
+    assert lib.qgemv_workspace_size(h, 5, ctypes.byref(b)) == ESHAPE
+    assert lib.qgemv_weight_bytes(h, 0, ctypes.byref(b)) == OK and b.value == 12288 * 2304
+    assert lib.qgemv_weight_bytes(h, 1, ctypes.byref(b)) == EINVAL
+    off = ctypes.c_size_t()
+    assert lib.qgemv_workspace_offset(h, 2, b"dx", ctypes.byref(off)) == OK and off.value % 256 == 0
+    assert lib.qgemv_workspace_offset(h, 2, b"nope", ctypes.byref(off)) == EINVAL
+    lib.qgemv_destroy(h)
+
+
+def test_run_validation_before_any_device_work(monkeypatch):
+    rc, h = _create(_desc(fmt=1, n=64, k=256, max_m=2))
+    assert rc == OK
+    ws = ctypes.c_size_t()
+    lib.qgemv_workspace_size(h, 1, ctypes.byref(ws))
+    A = 0x10000  # aligned fake addresses: validation never dereferences them
+    run = lambda w, x, y, m, p, n: lib.qgemv_run(h, w, x, y, m, p, n, None)
+    assert run(None, A, A, 1, A, ws.value) == EINVAL
+    assert run(A + 8, A, A, 1, A, ws.value) == EALIGN
+    assert run(A, A + 4, A, 1, A, ws.value) == EALIGN
+    assert run(A, A, A, 1, A + 16, ws.value) == EALIGN
+    assert run(A, A, A, 3, A, ws.value) == ESHAPE
+    assert run(A, A, A, 0, A, ws.value) == ESHAPE
+    assert run(A, A, A, 1, A, ws.value - 1) == EWORKSPACE
+    monkeypatch.setenv("QGEMV_FAULT", "launch")
+    assert run(A, A, A, 1, A, ws.value) == EHIP
+    assert b"injected" in lib.qgemv_last_error()
+    assert lib.qffn_run(h, A, A, A, A, 1, A, ws.value, None) == EINVAL   # wrong kind
+    lib.qgemv_destroy(h)
+    assert lib.qgemv_status_string(EWORKSPACE) == b"workspace too small"
+    assert lib.qgemv_status_string(-99) == b"unknown status"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    g = qg.GEMV("q4_0", 64, 256)
+    w = torch.zeros(g.weight_bytes(), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        g.run(w, torch.zeros(1, 256))

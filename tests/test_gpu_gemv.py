@@ -1,0 +1,150 @@
+"""GPU parity of the activation quantizer and the five GEMV kernels against
+the oracle: quantized activations bit-exact, per-block int32 dot products
+bit-exact, fp32 outputs within 2e-5 normwise relative error."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import gemv as og
+from oracle.quant import quantize_q8
+from tests.gpu_util import TOL, canary_ok, dev, guarded, host, normwise, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import block_quant_gemv_amd as qg  # noqa: E402
+
+CB_SEED = 77
+
+
+def _codebook():
+    return synth.codebook(CB_SEED)
+
+
+# ------------------------------------------------------------ quantizer --
+
+@pytest.mark.parametrize("seed,m,k", [(0, 1, 32), (1, 1, 2048), (2, 3, 4096), (3, 2, 12288), (4, 16, 2048)])
+def test_quantizer_bit_exact(seed, m, k):
+    say(f"quantizer seed={seed} m={m} k={k}")
+    x = synth.activations(seed, m, k)
+    x[0, :32] = np.float32(0)                       # zero block
+    if k >= 64:
+        x[0, 32:64] = np.float32(0.5) * np.arange(32, dtype=np.float32) - np.float32(7.5)  # ties
+        x[0, 63] = np.float32(127.0)
+    xq, dx, sx = qg.debug_quantize(dev(x))
+    torch.cuda.synchronize()
+    rq, rd, rs = quantize_q8(x)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(dx).view(np.int32), rd.view(np.int32))
+    assert np.array_equal(host(sx), rs)
+
+
+# ----------------------------------------------------------------- GEMV --
+
+SMALL = [
+    # fmt, n, k, m
+    ("q4_0", 2048, 2048, 1),      # the Q4_0 decode GEMV, full size
+    ("q4_0", 257, 288, 1),        # ragged: 9 blocks per row, odd rows
+    ("q4_0", 20, 32, 3),
+    ("q4_0", 1, 512, 2),
+    ("q8_0", 4096, 4096, 1),      # dense-layer shape
+    ("q8_0", 257, 288, 2),
+    ("q8_0", 33, 16384, 1),       # long rows: K-segmented steps
+    ("q4_k", 4096, 4096, 1),
+    ("q4_k", 20, 256, 3),
+    ("q4_k", 257, 768, 1),
+    ("q4_k", 9, 12288, 16),
+    ("q6_k", 4096, 12288, 1),     # FFN down shape
+    ("q6_k", 20, 256, 1),
+    ("q6_k", 257, 512, 4),
+    ("q6_k", 7, 16384, 2),        # long rows
+    ("iq4_nl", 4096, 4096, 1),
+    ("iq4_nl", 257, 288, 1),
+    ("iq4_nl", 20, 32, 8),
+]
+
+
+def _run_case(fmt, n, k, m, seed):
+    cb = _codebook() if fmt == "iq4_nl" else None
+    w = synth.weights(fmt, n, k, seed=seed)
+    x = synth.activations(seed + 1, m, k)
+    g = qg.GEMV(fmt, n, k, max_m=max(m, 1), codebook=cb)
+    wd = dev(w)
+    full, y = guarded(torch, m * n, torch.float32)
+    g.run(wd, dev(x), y.view(m, n))
+    xq, dx, sx = quantize_q8(x)
+    dots = g.block_dots(wd, dev(xq))
+    torch.cuda.synchronize()
+    return g, w, x, xq, dx, sx, host(y).reshape(m, n), host(dots), canary_ok(torch, full, m * n), cb
+
+
+@pytest.mark.parametrize("fmt,n,k,m", SMALL)
+def test_gemv_parity(fmt, n, k, m):
+    say(f"gemv {fmt} n={n} k={k} m={m}")
+    g, w, x, xq, dx, sx, y, dots, canary, cb = _run_case(fmt, n, k, m, seed=n + k + m)
+    assert canary, "output guard band overwritten"
+    ref_dots = og.block_dots(fmt, w, n, k, xq, cb)
+    assert dots.shape == ref_dots.shape
+    bad = np.argwhere(dots != ref_dots)
+    assert bad.size == 0, f"{len(bad)} block dots differ, first {bad[:3].tolist()}"
+    ref = og.gemv_dequant(fmt, w, n, k, xq, dx, cb)
+    e = normwise(y, ref)
+    say(f"  normwise error {e:.3e}")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("fmt,n,k", [("q8_0", 12288, 4096), ("q8_0", 24576, 4096),
+                                     ("q4_k", 12288, 4096), ("q4_k", 24576, 4096),
+                                     ("iq4_nl", 248320, 4096)])
+def test_gemv_full_size_sampled_rows(fmt, n, k):
+    say(f"gemv full size {fmt} n={n} k={k}")
+    cb = _codebook() if fmt == "iq4_nl" else None
+    w = synth.weights(fmt, n, k, seed=101)
+    x = synth.activations(102, 1, k)
+    g = qg.GEMV(fmt, n, k, codebook=cb)
+    wd = dev(w)
+    y = host(g.run(wd, dev(x)))
+    torch.cuda.synchronize()
+    xq, dx, _ = quantize_q8(x)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, n // 2, n - 2, n - 1], rng.integers(0, n, 2000)]))
+    ref = og.gemv_rows(fmt, w, n, k, rows, xq, dx, cb)
+    e = normwise(y[:, rows], ref)
+    say(f"  sampled normwise error {e:.3e} over {rows.size} rows")
+    assert e <= TOL
+    # per-row relative error on the sample
+    assert np.all(np.abs(y[0, rows] - ref[0]) <= 1e-4 * (np.abs(ref[0]) + np.abs(ref[0]).mean()))
+
+
+def test_gemv_deterministic_and_workspace_guard():
+    fmt, n, k = "q4_k", 4096, 4096
+    w = dev(synth.weights(fmt, n, k, seed=3))
+    x = dev(synth.activations(4, 2, k))
+    g = qg.GEMV(fmt, n, k, max_m=2)
+    wsz = g.workspace_size(2)
+    full, ws = guarded(torch, wsz, torch.uint8, pad=4096)
+    y1 = g.run(w, x, ws=ws).clone()
+    y2 = g.run(w, x, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert canary_ok(torch, full, wsz, pad=4096)
+
+
+def test_gemv_many_tokens_chunked():
+    # m = 32 with a format that has no MFMA path runs the VALU kernel in chunks.
+    fmt, n, k, m = "q8_0", 300, 512, 32
+    w = synth.weights(fmt, n, k, seed=8)
+    x = synth.activations(9, m, k)
+    g = qg.GEMV(fmt, n, k, max_m=m)
+    y = host(g.run(dev(w), dev(x)))
+    xq, dx, _ = quantize_q8(x)
+    assert normwise(y, og.gemv_dequant(fmt, w, n, k, xq, dx)) <= TOL
+
+
+def test_single_hip_runtime_loaded():
+    maps = open("/proc/self/maps").read()
+    libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(libs) == 1, libs
+    assert any("libqgemv.so" in ln for ln in maps.splitlines())
