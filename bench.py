@@ -69,6 +69,35 @@ def time_calls(fn, calls, warm=5):
     return e0.elapsed_time(e1) * 1e3 / calls
 
 
+def graph_of(fn, n):
+    """Capture fn(0..n-1) (launches on torch's current stream) in one HIP graph."""
+    import torch
+    for i in range(n):          # eager warm-up: one-time host set-up happens outside capture
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, n_inner, reps, warm=2):
+    """Mean microseconds per inner call over `reps` replays of graph g."""
+    import torch
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_inner)
+
+
 def cpu_baseline(mats, k, budget_s=12.0):
     """The oracle (dequantize to fp64, fp64 matvec) timed on this host's cores
     over a bounded sample: the first rows of each headline matrix."""
@@ -141,39 +170,50 @@ def main():
     dom_alg = dom_bytes + K + (K // 32) * 4 + mats[dom][1] * 4   # weights + xq + dx + y
     stream = torch.cuda.current_stream()
 
-    ev_pairs = []
-
-    def step(i, record):
+    def step(i):
         r = i % R
         for j, g in enumerate(plans):
-            g.quantize(xs[j], ws[j], stream=stream)
-            if record and j == dom:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                g.run_quantized(W[j][r], ws[j], 1, ys[j], stream=stream)
-                b.record(stream)
-                ev_pairs.append((a, b))
-            else:
-                g.run_quantized(W[j][r], ws[j], 1, ys[j], stream=stream)
+            g.run(W[j][r], xs[j], y=ys[j], ws=ws[j])
 
+    # One HIP graph holds R steps (one per weight copy); replaying it removes
+    # the Python/launch overhead between the kernels, not any of their work.
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
+    graph = graph_of(step, R)
+    reps = max(1, -(-args.steps // R))
+    steps = reps * R
+    log(f"timing {steps} steps ({reps} replays of a {R}-step graph)")
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, True)
-    e1.record(stream)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = e0.elapsed_time(e1) / steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    dom_us = sum(a.elapsed_time(b) for a, b in ev_pairs) * 1e3 / len(ev_pairs)
+    # Eager (no graph) step time, for reference.
+    eager_us = time_calls(lambda i: step(i), 3 * R, warm=R) if not args.no_extras else None
+
+    # Dominant kernel alone: its GEMV launches back to back (activations
+    # quantized once), HIP events around a graph of R launches.
+    dg = plans[dom]
+    dg.quantize(xs[dom], ws[dom])
+    gd = graph_of(lambda i: dg.run_quantized(W[dom][i % R], ws[dom], 1, ys[dom]), R)
+    dom_us = time_graph(gd, R, reps=max(4, 64 // R))
     achieved = dom_alg / (dom_us * 1e-6) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us ({wall / args.steps * 1e3:.3f} ms wall), {value:.0f} GB/s; "
+    log(f"step {ms_step * 1e3:.1f} us ({wall / steps * 1e3:.3f} ms wall), {value:.0f} GB/s; "
         f"Q8_0 24576x4096 GEMV kernel {dom_us:.2f} us -> {achieved:.0f} GB/s")
+
+    # Per-matrix call times (quantize + GEMV), graph-replayed.
+    per = {}
+    for j, (f, n) in enumerate(mats):
+        gj = graph_of(lambda i, j=j: plans[j].run(W[j][i % R], xs[j], y=ys[j], ws=ws[j]), R)
+        us = time_graph(gj, R, reps=max(4, 64 // R))
+        b = n * synth.row_bytes(f, K)
+        per[f"{f}_{n}x{K}"] = {"us": round(us, 3), "gbps": round(b / (us * 1e-6) / 1e9, 1)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -183,7 +223,8 @@ def main():
         "config": {"workload": "M=1 decode GEMVs, K=4096, Q8_0 and Q4_K weights, N=4096/12288/24576 "
                                "(activation quantizer + GEMV per call)",
                    "m": 1, "k": K, "n": [4096, 12288, 24576], "formats": ["q8_0", "q4_k"],
-                   "weight_bytes_per_step": step_bytes, "rotating_copies": R},
+                   "weight_bytes_per_step": step_bytes, "rotating_copies": R,
+                   "timing": "HIP graph of the step's launches, replayed"},
         "pct_hbm_peak": round(100 * value * 1e9 / HBM_PEAK, 2),
         "roofline": {"bound": "hbm", "kernel": "gemv Q8_0 N=24576 K=4096 M=1",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -191,6 +232,9 @@ def main():
                      "bytes_per_launch": dom_alg, "avg_kernel_us": round(dom_us, 3)},
     }
 
+    out["per_matrix"] = per
+    if eager_us is not None:
+        out["eager_step_us"] = round(eager_us, 2)
     if not args.no_extras:
         out["extras"] = extras(qg, synth, torch)
     if not args.no_cpu_baseline:
@@ -213,8 +257,10 @@ def extras(qg, synth, torch):
     x = dev(synth.activations(302, 1, H))
     y = torch.empty((1, H), dtype=torch.float32, device="cuda")
     ws = f.workspace(1)
-    us = time_calls(lambda i: f.run(gus[i % R], dns[i % R], x, y=y, ws=ws), 100)
+    g = graph_of(lambda i: f.run(gus[i % R], dns[i % R], x, y=y, ws=ws), R)
+    us = time_graph(g, R, reps=max(4, 128 // R))
     res["ffn_us"] = round(us, 3)
+    res["ffn_us_eager"] = round(time_calls(lambda i: f.run(gus[i % R], dns[i % R], x, y=y, ws=ws), 50), 3)
     res["ffn_weight_gbps"] = round((b_gu + b_dn) / (us * 1e-6) / 1e9, 1)
     log(f"ffn: {us:.2f} us per fused FFN, {res['ffn_weight_gbps']} GB/s")
     del gus, dns
@@ -227,7 +273,8 @@ def extras(qg, synth, torch):
     Ws = rotated(synth.weights("iq4_nl", N, 4096, seed=310), R)
     x = dev(synth.activations(311, 1, 4096))
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    us = time_calls(lambda i: g.run(Ws[i % R], x, y=y), 20, warm=2)
+    gg = graph_of(lambda i: g.run(Ws[i % R], x, y=y), R)
+    us = time_graph(gg, R, reps=8)
     res["lm_head_us"] = round(us, 2)
     res["lm_head_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
     log(f"lm_head: {us:.1f} us, {res['lm_head_gbps']} GB/s")
@@ -240,7 +287,8 @@ def extras(qg, synth, torch):
     Ws = [base] + [base.clone() for _ in range(R - 1)]
     x = dev(synth.activations(321, 1, 2048))
     y = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
-    us = time_calls(lambda i: g.run(Ws[i % R], x, y=y), 200)
+    gg = graph_of(lambda i: g.run(Ws[i % R], x, y=y), 64)
+    us = time_graph(gg, 64, reps=8)
     res["q4_0_2048_us"] = round(us, 3)
     res["q4_0_2048_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
     log(f"q4_0 2048x2048: {us:.2f} us, {res['q4_0_2048_gbps']} GB/s")
@@ -259,7 +307,8 @@ def extras(qg, synth, torch):
         x = dev(synth.activations(333 + m, m, Hm))
         y = torch.empty((m, Hm), dtype=torch.float32, device="cuda")
         ws = mo.workspace(m)
-        us = time_calls(lambda i: mo.run(wr, GU[i % R], DN[i % R], gsh, dsh, x, y=y, ws=ws), 100)
+        gm = graph_of(lambda i: mo.run(wr, GU[i % R], DN[i % R], gsh, dsh, x, y=y, ws=ws), R)
+        us = time_graph(gm, R, reps=16)
         res[f"moe_m{m}_us"] = round(us, 3)
         log(f"moe m={m}: {us:.2f} us")
     return res

@@ -161,7 +161,10 @@ class _Plan:
 
     def _check_w(self, w, which, name):
         _dev(w, torch.uint8, name)
-        need = self.weight_bytes(which)
+        cache = self.__dict__.setdefault("_wb", {})
+        need = cache.get(which)
+        if need is None:
+            need = cache[which] = self.weight_bytes(which)
         if w.numel() < need:
             raise ValueError(f"{name} has {w.numel()} bytes, needs {need}")
         return w.data_ptr()

@@ -253,6 +253,9 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t* bytes) {
 
 namespace {
 
+// Largest K for which qgemv_run fuses the activation quantizer into the GEMV.
+constexpr int64_t kFusedQuantMaxK = 2048;
+
 int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const char* fn) {
   if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);
   if (!ws) return fail(QGEMV_EINVAL, "%s: null workspace", fn);
@@ -313,8 +316,31 @@ int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* w
     return fail(QGEMV_EALIGN, "qgemv_run: w and x need 16-byte, y 4-byte alignment");
   if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run: launch failure injected (QGEMV_FAULT)");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
-  return gemv_from_quantized(h, w, y, m, ws, s);
+  const qgemv_desc& d = h->d;
+  if (m > kGemvMaxTokens || d.k > kFusedQuantMaxK) {
+    if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
+    return gemv_from_quantized(h, w, y, m, ws, s);
+  }
+  // Short rows: one launch, the GEMV kernel quantizes x in its prologue
+  // (same arithmetic as the standalone quantizer) and its first workgroup
+  // stores the codes in the workspace regions "xq", "dx", "sx". For longer
+  // rows every resident workgroup re-quantizing all of x costs more than the
+  // separate quantizer launch, so those take two launches.
+  const Layout L = layout_of(h, m);
+  GemvProblem p;
+  p.w = static_cast<const uint8_t*>(w);
+  p.xf = x;
+  p.xs = d.k;
+  p.xq_out = region<int8_t>(ws, L, "xq");
+  p.dx_out = region<float>(ws, L, "dx");
+  p.sx_out = region<int32_t>(ws, L, "sx");
+  p.y = y;
+  p.ldy = d.n;
+  p.n = d.n;
+  p.k = d.k;
+  p.m = m;
+  memcpy(p.cb, h->cbw, sizeof p.cb);
+  return check_launch(launch_gemv(d.fmt, p, false, s), "gemv");
 }
 
 int qgemv_quantize(qgemv_t h, const float* x, int m, void* ws, size_t ws_bytes, void* stream) {
@@ -359,12 +385,13 @@ int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x
   int8_t* hq = region<int8_t>(ws, L, "hq");
   float* hd = region<float>(ws, L, "hd");
   int32_t* hs = region<int32_t>(ws, L, "hs");
-  int rc = check_launch(launch_quant_q8(x, xq, dx, sx, (int64_t)m * (d.hidden / 32), s), "quantize");
-  if (rc) return rc;
+  int rc;
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w_gateup);
-  p.xq = xq;
-  p.dx = dx;
+  p.xf = x;  // quantized in the gate|up kernel's prologue, codes stored in ws
+  p.xq_out = xq;
+  p.dx_out = dx;
+  p.sx_out = sx;
   p.xs = d.hidden;
   p.y = gu;
   p.ldy = 2 * d.inter;
@@ -376,6 +403,10 @@ int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x
   if ((rc = check_launch(launch_swiglu_q8(gu, 2 * d.inter, hh, hq, hd, hs, m, d.inter, s), "swiglu")))
     return rc;
   GemvProblem q = p;
+  q.xf = nullptr;
+  q.xq_out = nullptr;
+  q.dx_out = nullptr;
+  q.sx_out = nullptr;
   q.w = static_cast<const uint8_t*>(w_down);
   q.xq = hq;
   q.dx = hd;

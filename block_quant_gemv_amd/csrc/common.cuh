@@ -51,9 +51,59 @@ QG_DEV uint32_t lds_u16(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint16_t*>(base + off);
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int CTRL>
+QG_DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of `width` lanes, width a power of two <= 16; every
+// lane of a group ends with its group's sum. DPP steps: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror -- each adds the partner
+// half of the next-larger group, so the order of additions is fixed.
+QG_DEV float group_sum16(float v, int width) {
+  if (width >= 2) v += dpp<0xB1>(v);
+  if (width >= 4) v += dpp<0x4E>(v);
+  if (width >= 8) v += dpp<0x141>(v);
+  if (width >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
+template <int CTRL>
+QG_DEV int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
+// Reductions over aligned groups of 8 lanes (one 32-element block, 4
+// elements per lane) with DPP only -- no LDS round trips.
+QG_DEV float max8(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  return fmaxf(v, dpp<0x141>(v));  // row_half_mirror: the other quad
+}
+// Sum over aligned groups of 4 lanes.
+QG_DEV int sum4(int v) {
+  v += dpp_i<0xB1>(v);
+  return v + dpp_i<0x4E>(v);
+}
+// Value of the mirrored lane in the other half of an 8-lane group.
+QG_DEV int other_quad(int v) { return dpp_i<0x141>(v); }
+
+QG_DEV float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over aligned groups of `width` lanes (power of two <= 64), result in
+// every lane of the group. Groups of 32 and 64 add their 16-lane rows with
+// readlane in a fixed order.
 QG_DEV float group_sum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = group_sum16(v, width);
+  if (width == 64) {
+    v = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+  } else if (width == 32) {
+    const float g0 = readlane_f(v, 0) + readlane_f(v, 16);
+    const float g1 = readlane_f(v, 32) + readlane_f(v, 48);
+    v = (__lane_id() < 32) ? g0 : g1;
+  }
   return v;
 }
 
@@ -69,24 +119,44 @@ QG_DEV float wave_sum(float v) {
   return v;
 }
 
+// Code of one element: round-half-away(fl32(x / d)), clamped to +-127, for a
+// block scale d = fl32(absmax / 127) > 0 (r = v_rcp(d)).
+//
+// fl32(x / d) is the correctly rounded quotient; computing it with the IEEE
+// division sequence for every element is the costly part of quantization.
+// Instead v' = fl32(x * rcp(d)) is used: v_rcp_f32 is within 1 ulp and the
+// product adds half an ulp, so |v' - x/d| <= 1.5 * 2^-23 * |x/d| < 2^-15.4
+// (|x/d| <= 127.0001), and fl32(x/d) is within 2^-18 of x/d. Rounding to an
+// integer only depends on which side of the nearest half-integer the value
+// lies, so whenever v' is at least 2^-14 away from every half-integer,
+// roundf(v') equals roundf(fl32(x/d)). Only within 2^-14 of a half-integer
+// (about 1 element in 8000) is the exact division taken. Tiny scales whose
+// reciprocal could be flushed also take the exact path.
+QG_DEV int q8_code(float x, float d, float r) {
+  float v = x * r;
+  const float m = fabsf(v);
+  const float f = m - floorf(m);
+  if (fabsf(f - 0.5f) < 0x1p-14f || d < 0x1p-100f) v = x / d;
+  const float q = fminf(fmaxf(roundf(v), -127.0f), 127.0f);
+  return (int)q;
+}
+
 // Q8 quantization of 4 consecutive elements of a 32-element block whose
 // absolute maximum is `amax`: d = amax / 127 (IEEE division), codes =
 // round-half-away(x / d) clamped to +-127; all zero when amax == 0.
-// Returns the 4 codes packed little-endian in one dword.
+// Returns the 4 codes packed little-endian in one dword and their sum.
 QG_DEV uint32_t q8_pack4(float4 v, float d, int& sum) {
-  float e[4] = {v.x, v.y, v.z, v.w};
+  const float e[4] = {v.x, v.y, v.z, v.w};
   uint32_t packed = 0;
   int s = 0;
+  if (d != 0.0f) {
+    const float r = __builtin_amdgcn_rcpf(d);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int q = 0;
-    if (d != 0.0f) {
-      float r = roundf(e[i] / d);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      q = (int)r;
+    for (int i = 0; i < 4; ++i) {
+      const int q = q8_code(e[i], d, r);
+      s += q;
+      packed |= ((uint32_t)(q & 0xff)) << (8 * i);
     }
-    s += q;
-    packed |= ((uint32_t)(q & 0xff)) << (8 * i);
   }
   sum = s;
   return packed;

@@ -32,11 +32,24 @@
 
 namespace qg {
 
-constexpr int kWavesPerWG = 4;
-constexpr int kTileCap = 10240;                 // packed bytes per step (max)
-constexpr int kTileBuf = kTileCap + 48;          // + alignment and over-read slack
+#ifndef QG_TILE_CAP
+#define QG_TILE_CAP 10240
+#endif
+#ifndef QG_WGS_PER_CU
+#define QG_WGS_PER_CU 0   // 0: as many workgroups as fit (occupancy query)
+#endif
+
+#ifndef QG_BALANCE
+#define QG_BALANCE 0      // 1: size the grid so every wave gets the same step count
+#endif
+#ifndef QG_WAVES_PER_WG
+#define QG_WAVES_PER_WG 4
+#endif
+
+constexpr int kWavesPerWG = QG_WAVES_PER_WG;
+constexpr int kTileCap = QG_TILE_CAP;           // packed bytes per step (max)
+// 16-byte chunks a step can span (alignment adds up to two), per lane.
 constexpr int kLoadsPerLane = (kTileCap + 32 + 1023) / 1024;
-constexpr int kMaxPasses = 8;                    // row passes per step (M = 1)
 constexpr int kLdsLimit = 160 * 1024;
 
 // ------------------------------------------------------------ activations --
@@ -250,12 +263,13 @@ template <> struct FmtOf<kQ6_K> { using T = FmtQ6_K; };
 struct GemvGeom {
   int U;          // 32-element units per row
   int LPR, RPP;   // lanes per row, rows per pass
-  int P;          // passes per step (rows per step = P * RPP)
+  int lpr_log;    // log2(LPR)
   int SU;         // units per step segment (== U when rows are whole)
   int nseg;       // segments per row
   int64_t rb;     // row bytes
   int64_t nrowtiles;
   int act_bytes;  // LDS bytes of staged activations
+  int tile_buf;   // LDS bytes of one wave's step buffer
 };
 
 struct GemvArgs {
@@ -266,10 +280,84 @@ struct GemvArgs {
 template <typename F>
 QG_DEV int64_t seg_bytes(int units) { return (int64_t)(units / F::kUPB) * F::kBB; }
 
-template <int FMT, int MT, bool DOTS>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
+// Stage the quantized activations of tokens t < mcnt in LDS. From int8 codes
+// (xq/dx) or, with FUSEQ, by quantizing fp32 x here: eight lanes per 32-element
+// unit, the same arithmetic as the standalone quantizer. Token slots past
+// mcnt are never read, so they are not staged.
+template <int MT, bool DOTS, bool FUSEQ, typename RowFn>
+QG_DEV void stage_activations(uint8_t* smem, const GemvProblem& p, int U, int mcnt, RowFn out_row,
+                              bool write_back) {
+  const int tokb = act_token_bytes(U);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (t >= mcnt) break;
+    const int64_t ar = out_row(t) / p.act_div;  // 32-bit operands: slot rows are small
+    uint8_t* tok = smem + t * tokb;
+    if constexpr (FUSEQ) {
+      // Batches of 4 tasks per thread: all loads of a batch are issued
+      // before any is used, so the batch costs one memory round trip.
+      const float4* xr = reinterpret_cast<const float4*>(p.xf + ar * p.xs);
+      const int ntask = U * 8;
+      for (int base = threadIdx.x; base < ntask; base += 4 * blockDim.x) {
+        float4 vb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = base + r * blockDim.x;
+          vb[r] = i < ntask ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = base + r * blockDim.x;
+          if (i < ntask) {  // whole 8-lane groups are in or out together
+            const float4 v = vb[r];
+            const int u = i >> 3, part = i & 7;
+            const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
+            int s;
+            const uint32_t packed = q8_pack4(v, d, s);
+            s = sum4(s);                          // lanes 0-3: sum of codes 0..15; 4-7: 16..31
+            const int other = other_quad(s);
+            if (part < 4) *reinterpret_cast<uint32_t*>(tok + 16 * u + 4 * part) = packed;
+            else *reinterpret_cast<uint32_t*>(tok + 16 * U + 16 * u + 4 * (part - 4)) = packed;
+            if (part == 0)
+              *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) =
+                  make_int2(__float_as_int(d), (s & 0xffff) | (other << 16));
+            if (write_back) {
+              reinterpret_cast<uint32_t*>(p.xq_out + ar * p.xs)[i] = packed;
+              if (part == 0) {
+                p.dx_out[ar * (p.xs / 32) + u] = d;
+                if (p.sx_out) p.sx_out[ar * (p.xs / 32) + u] = s + other;
+              }
+            }
+          }
+        }
+      }
+    } else {
+      const int4* src = reinterpret_cast<const int4*>(p.xq + ar * p.xs);
+      const float* dxr = DOTS ? nullptr : p.dx + ar * (p.xs / 32);
+      for (int u = threadIdx.x; u < U; u += blockDim.x) {
+        const int4 lo = src[2 * u];
+        const int4 hi = src[2 * u + 1];
+        float d = 0.0f;
+        if constexpr (!DOTS) d = dxr[u];
+        const int ones = 0x01010101;
+        const int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
+        const int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
+        *reinterpret_cast<int4*>(tok + 16 * u) = lo;
+        *reinterpret_cast<int4*>(tok + 16 * U + 16 * u) = hi;
+        *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) = make_int2(__float_as_int(d), (sa & 0xffff) | (sb << 16));
+      }
+    }
+  }
+}
+
+// FMT: block format; MT: token slots (activations staged per workgroup);
+// P: row passes per step (compile time, so every pass's LDS reads are issued
+// before any pass's arithmetic); DOTS: integer-store checking epilogue;
+// FUSEQ: quantize fp32 activations in the prologue.
+template <int FMT, int MT, int P, bool DOTS, bool FUSEQ>
+__global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs args) {
   using F = typename FmtOf<FMT>::T;
-  constexpr int PM = (MT == 1) ? kMaxPasses : ((32 / MT) < 1 ? 1 : (32 / MT));
   extern __shared__ __align__(16) uint8_t smem[];
   const GemvProblem& p = args.p;
   const GemvGeom& g = args.g;
@@ -278,57 +366,29 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
   // Resolve this problem's matrix, token count and row mapping.
   const uint8_t* W = p.w;
   int mcnt = p.m;
-  const int32_t* rows = nullptr;  // grouped mode: slot row of each token
+  const int32_t* rows = nullptr;  // grouped mode: output (slot) row of each token
   bool shared = false;
   if (p.tbl) {
-    if (prob == p.nprob - 1) {
-      W = p.w_shared;
-      shared = true;
-    } else {
-      if (prob >= p.tbl[0]) return;  // whole workgroup leaves before any barrier
-      const int32_t* e = p.tbl + 1 + (int64_t)prob * p.tbl_stride;
-      W = p.w + (int64_t)e[0] * p.w_stride;
-      mcnt = e[1];
-      rows = e + 2;
-    }
+    if (prob >= p.tbl[0]) return;  // whole workgroup leaves before any barrier
+    const int32_t* e = p.tbl + 1 + (int64_t)prob * p.tbl_stride;
+    shared = e[0] < 0;
+    W = shared ? p.w_shared : p.w + (int64_t)e[0] * p.w_stride;
+    mcnt = e[1];
+    rows = e + 2;
   }
-  auto out_row = [&](int t) __attribute__((always_inline)) -> int64_t {
-    if (!p.tbl) return t;
-    return shared ? (int64_t)t * p.slots + p.slots - 1 : (int64_t)rows[t];
-  };
+  auto out_row = [&](int t) __attribute__((always_inline)) -> int { return p.tbl ? rows[t] : t; };
 
-  // ---- stage activations (all tokens) in LDS
   const int U = g.U;
   const int tokb = act_token_bytes(U);
-  for (int idx = threadIdx.x; idx < MT * U; idx += blockDim.x) {
-    const int t = idx / U, u = idx - t * U;
-    uint8_t* tok = smem + t * tokb;
-    int4 lo = make_int4(0, 0, 0, 0), hi = make_int4(0, 0, 0, 0);
-    float d = 0.0f;
-    if (t < mcnt) {
-      const int64_t ar = out_row(t) / p.act_div;
-      const int4* src = reinterpret_cast<const int4*>(p.xq + ar * p.xs + 32 * u);
-      lo = src[0];
-      hi = src[1];
-      if constexpr (!DOTS) d = p.dx[ar * (p.xs / 32) + u];
-    }
-    const int ones = 0x01010101;
-    int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
-    int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
-    *reinterpret_cast<int4*>(tok + 16 * u) = lo;
-    *reinterpret_cast<int4*>(tok + 16 * U + 16 * u) = hi;
-    *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) =
-        make_int2(__float_as_int(d), (sa & 0xffff) | (sb << 16));
-  }
-  __syncthreads();
-
   const int wid = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  uint8_t* tile = smem + g.act_bytes + wid * kTileBuf;
+  uint8_t* tile = smem + g.act_bytes + wid * g.tile_buf;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerWG;
-  const int lam = lane % g.LPR;
-  const int rho = lane / g.LPR;
-  const int G = g.P * g.RPP;
+  const int LPR = g.LPR, RPP = g.RPP;  // powers of two: use shifts, not divisions
+  const int lpr_log = g.lpr_log, rpp_log = 6 - g.lpr_log;
+  const int lam = lane & (LPR - 1);
+  const int rho = lane >> lpr_log;
+  const int G = P * RPP;
 
   // Byte range of step (rt, seg), relative to W.
   auto step_range = [&](int64_t rt, int seg, int64_t& b0, int64_t& b1) __attribute__((always_inline)) {
@@ -345,6 +405,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
     }
   };
 
+  // This wave's steps: row tiles rt_first + i * nwaves, each in nseg
+  // K-segments. One register buffer holds the next step while the current
+  // one is decoded from LDS.
+  const int64_t rt_first = (int64_t)blockIdx.x * kWavesPerWG + wid;
   u32x4 buf[kLoadsPerLane];
   auto issue = [&](int64_t rt, int seg) __attribute__((always_inline)) {
     int64_t b0, b1;
@@ -358,17 +422,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
       if (c < nch) buf[i] = src[c];
     }
   };
+  // First weight step in flight before the activation staging, so the two
+  // memory round trips overlap.
+  if (rt_first < g.nrowtiles) issue(rt_first, 0);
 
-  float acc[PM][MT];
+  // With fused quantization, workgroup 0 of the plain problem (or of each
+  // shared-expert entry, which together cover every token once) stores the
+  // activation codes in the workspace.
+  stage_activations<MT, DOTS, FUSEQ>(smem, p, U, mcnt, out_row,
+                                     FUSEQ && p.xq_out && blockIdx.x == 0 && (!p.tbl || shared));
+  __syncthreads();
+
+  float acc[P][MT];
 #pragma unroll
-  for (int a = 0; a < PM; ++a)
+  for (int a = 0; a < P; ++a)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[a][t] = 0.0f;
 
-  int64_t rt = (int64_t)blockIdx.x * kWavesPerWG + wid;
+  int64_t rt = rt_first;
   int seg = 0;
-  if (rt < g.nrowtiles) issue(rt, seg);
-
   while (rt < g.nrowtiles) {
     int64_t b0, b1;
     step_range(rt, seg, b0, b1);
@@ -387,46 +459,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
     if (seg2 == g.nseg) { seg2 = 0; rt2 = rt + nwaves; }
     if (rt2 < g.nrowtiles) issue(rt2, seg2);
 
-    // ---- compute this step from LDS
+    // ---- decode this step from LDS and accumulate
     const int64_t r0 = rt * G;
     const int nrows = (int)((p.n - r0) < G ? (p.n - r0) : G);
     const int u0 = seg * g.SU;
     const int su = (U - u0) < g.SU ? (U - u0) : g.SU;
     const uint32_t base = (uint32_t)(b0 - a0);  // LDS offset of the step's first byte
-    for (int j = 0; lam + g.LPR * j < su; ++j) {
-      const int ul = lam + g.LPR * j;
-      const int ug = u0 + ul;
-      // Few tokens: keep every token's unit in registers across the passes;
-      // many tokens: re-read it from LDS per row to bound register use.
-      constexpr bool kActRegs = MT <= 4;
-      Act av[kActRegs ? MT : 1];
-      if constexpr (kActRegs) {
+    const int jmax = (su + LPR - 1) >> lpr_log;
+    for (int j = 0; j < jmax; ++j) {
+      const int ul = lam + LPR * j;
+      if (ul < su) {
+        const int ug = u0 + ul;
+        const uint32_t uoff = (uint32_t)((ul / F::kUPB) * F::kBB);
+        const int sub = ul % F::kUPB;
+        // All passes' weight units first (independent LDS reads in flight
+        // together); rows past the end re-read the last valid row and are
+        // never stored.
+        typename F::W wv[P];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) av[t] = load_act(smem + t * tokb, U, ug);
-      }
-      const uint32_t uoff = (uint32_t)((ul / F::kUPB) * F::kBB);
-      const int sub = ul % F::kUPB;
+        for (int pp = 0; pp < P; ++pp) {
+          int rl = pp * RPP + rho;
+          rl = rl < nrows ? rl : nrows - 1;
+          wv[pp] = F::load(tile, base + (uint32_t)(rl * g.rb) + uoff, sub, p.cb);
+        }
 #pragma unroll
-      for (int pp = 0; pp < PM; ++pp) {
-        const int rl = pp * g.RPP + rho;
-        if (pp < g.P && rl < nrows) {
-          const typename F::W wv = F::load(tile, base + (uint32_t)(rl * g.rb) + uoff, sub, p.cb);
-          if constexpr (DOTS) {
+        for (int t = 0; t < MT; ++t) {
+          if (t < mcnt) {  // wave-uniform: skips padded tokens
+            const Act a = load_act(smem + t * tokb, U, ug);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              if (t < mcnt) {
-                int32_t* o = p.dots + (out_row(t) * p.n + r0 + rl) * ((int64_t)U * F::kDotsPerUnit) +
-                             (int64_t)ug * F::kDotsPerUnit;
-                if constexpr (kActRegs) F::dots(wv, av[t], o);
-                else F::dots(wv, load_act(smem + t * tokb, U, ug), o);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              if (t < mcnt) {  // wave-uniform: skips padded tokens
-                if constexpr (kActRegs) acc[pp][t] = F::fma(wv, av[t], acc[pp][t]);
-                else acc[pp][t] = F::fma(wv, load_act(smem + t * tokb, U, ug), acc[pp][t]);
+            for (int pp = 0; pp < P; ++pp) {
+              if constexpr (DOTS) {
+                const int rl = pp * RPP + rho;
+                if (rl < nrows) {
+                  int32_t* o = p.dots + ((int64_t)out_row(t) * p.n + r0 + rl) * ((int64_t)U * F::kDotsPerUnit) +
+                               (int64_t)ug * F::kDotsPerUnit;
+                  F::dots(wv[pp], a, o);
+                }
+              } else {
+                acc[pp][t] = F::fma(wv[pp], a, acc[pp][t]);
               }
             }
           }
@@ -435,16 +505,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs args) {
     }
 
     if (!DOTS && seg == g.nseg - 1) {
+      // Row sums: lanes of a group add up; lane pp*RPP + rho then holds row
+      // r0 + pp*RPP + rho, so each token's rows go out in one store.
 #pragma unroll
-      for (int pp = 0; pp < PM; ++pp) {
-        if (pp < g.P) {
-          const int rl = pp * g.RPP + rho;
+      for (int t = 0; t < MT; ++t) {
+        if (t < mcnt) {
+          float outv = 0.0f;
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const float v = group_sum(acc[pp][t], g.LPR);
-            if (lam == 0 && rl < nrows && t < mcnt) p.y[out_row(t) * p.ldy + r0 + rl] = v;
+          for (int pp = 0; pp < P; ++pp) {
+            const float sum = group_sum(acc[pp][t], LPR);
+            float v;
+            if (RPP == 1) v = sum;
+            else v = __shfl(sum, (lane & (RPP - 1)) << lpr_log, kWave);
+            if ((lane >> rpp_log) == pp) outv = v;
             acc[pp][t] = 0.0f;
           }
+          if (lane < nrows) p.y[(int64_t)out_row(t) * p.ldy + r0 + lane] = outv;
         }
       }
     }
@@ -499,81 +575,133 @@ static int device_cus() {
   return cus;
 }
 
-// Choose the step geometry for a format, shape and token tile.
-static GemvGeom plan_geom(int fmt, int64_t n, int64_t k, int MT) {
-  GemvGeom g{};
+// Largest passes-per-step the kernels are instantiated for, per token tile.
+static int max_passes(int mt) { return mt <= 2 ? 8 : mt == 4 ? 4 : mt == 8 ? 2 : 1; }
+
+// Choose the step geometry for a format, shape and token tile; returns P.
+static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom& g) {
+  g = GemvGeom{};
   const int upb = (fmt == kQ4_K || fmt == kQ6_K) ? 8 : 1;
   const int bb = fmt_block_bytes(fmt);
   g.U = (int)(k / 32);
   g.rb = fmt_row_bytes(fmt, k);
   g.LPR = g.U >= kWave ? kWave : floor_pow2(g.U);
   g.RPP = kWave / g.LPR;
-  const int PM = (MT == 1) ? kMaxPasses : ((32 / MT) < 1 ? 1 : (32 / MT));
+  g.lpr_log = 0;
+  while ((1 << g.lpr_log) < g.LPR) ++g.lpr_log;
+  int P = 1;
   if (g.rb * g.RPP <= kTileCap) {
     g.nseg = 1;
     g.SU = g.U;
-    int P = (int)(kTileCap / (g.rb * g.RPP));
-    if (P > PM) P = PM;
-    if (P < 1) P = 1;
+    const int pm = dots ? 1 : max_passes(MT);
+    while (P * 2 <= pm && g.rb * g.RPP * P * 2 <= kTileCap) P *= 2;
     // Keep enough steps to spread the matrix over the whole chip.
-    const int64_t want_waves = (int64_t)device_cus() * 4;
+    const int64_t want_waves = (int64_t)device_cus() * 8;
     while (P > 1 && (n + (int64_t)P * g.RPP - 1) / ((int64_t)P * g.RPP) < want_waves) P >>= 1;
-    g.P = P;
   } else {
     // Long rows: one row per step, split into K-segments of whole
     // super-blocks that are a multiple of 64 units.
-    g.P = 1;
     const int64_t unit_bytes_x64 = (int64_t)64 * bb / upb;  // bytes of 64 units
     int su = (int)(kTileCap / unit_bytes_x64) * 64;
     if (su < 64) su = 64;
     g.SU = su;
     g.nseg = (g.U + su - 1) / su;
   }
-  const int64_t G = (int64_t)g.P * g.RPP;
+  const int64_t G = (int64_t)P * g.RPP;
   g.nrowtiles = (n + G - 1) / G;
   g.act_bytes = MT * act_token_bytes(g.U);
-  return g;
+  const int64_t step_max = g.nseg == 1 ? G * g.rb : (int64_t)(g.SU / upb) * bb;
+  g.tile_buf = (int)((step_max + 32 + 15) / 16 * 16 + 16);  // + alignment chunks + over-read
+  return P;
 }
 
-template <int FMT, int MT, bool DOTS>
+template <int FMT, int MT, int P, bool DOTS, bool FUSEQ>
 static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.g.act_bytes + (size_t)kWavesPerWG * kTileBuf;
+  auto kern = gemv_kernel<FMT, MT, P, DOTS, FUSEQ>;
+  const size_t lds = (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf;
   static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<FMT, MT, DOTS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  int64_t wgs = (a.g.nrowtiles + kWavesPerWG - 1) / kWavesPerWG;
-  const int64_t cap = (int64_t)device_cus() * 8;
-  if (wgs > cap) wgs = cap;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, DOTS>), dim3((unsigned)wgs, (unsigned)a.p.nprob),
-                     dim3(256), lds, s, a);
+  // Persistent grid: no more workgroups than can be resident at once, so
+  // every wave walks its share of the steps without a second launch round.
+  // Resident workgroups per CU depend on the LDS size (activations vary with
+  // K); cache the occupancy answer per LDS size for this kernel.
+  static size_t cached_lds[8] = {0};
+  static int cached_nb[8] = {0};
+  int per_cu = 0;
+  for (int i = 0; i < 8; ++i)
+    if (cached_lds[i] == lds && cached_nb[i] > 0) per_cu = cached_nb[i];
+  if (!per_cu) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kWavesPerWG * 64, lds) != hipSuccess || nb < 1) nb = 1;
+    per_cu = QG_WGS_PER_CU > 0 && QG_WGS_PER_CU < nb ? QG_WGS_PER_CU : nb;
+    for (int i = 0; i < 8; ++i)
+      if (cached_nb[i] == 0) { cached_lds[i] = lds; cached_nb[i] = per_cu; break; }
+  }
+  // Waves available to each problem, then the fewest waves that still give
+  // every wave the same number of row tiles (ceil), so no wave runs a
+  // lone extra step at the end.
+  // Grouped launches split the resident waves among their problems.
+  const int64_t cap_waves = (int64_t)device_cus() * per_cu * kWavesPerWG;
+  int64_t wmax = cap_waves / a.p.nprob;
+  if (wmax < kWavesPerWG) wmax = kWavesPerWG;
+#if QG_BALANCE
+  const int64_t per_wave = (a.g.nrowtiles + wmax - 1) / wmax;
+  const int64_t waves = (a.g.nrowtiles + per_wave - 1) / per_wave;
+#else
+  const int64_t waves = a.g.nrowtiles < wmax ? a.g.nrowtiles : wmax;
+#endif
+  const int64_t wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs, (unsigned)a.p.nprob), dim3(kWavesPerWG * 64), lds, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, bool DOTS>
-static hipError_t launch_mt(const GemvArgs& a, int mt, hipStream_t s) {
-  switch (mt) {
-    case 1: return launch_t<FMT, 1, DOTS>(a, s);
-    case 2: return launch_t<FMT, 2, DOTS>(a, s);
-    case 4: return launch_t<FMT, 4, DOTS>(a, s);
-    case 8: return launch_t<FMT, 8, DOTS>(a, s);
-    default: return launch_t<FMT, 16, DOTS>(a, s);
+template <int FMT, int MT, bool DOTS, bool FUSEQ>
+static hipError_t launch_p(const GemvArgs& a, int P, hipStream_t s) {
+  if constexpr (DOTS) {
+    return launch_t<FMT, MT, 1, true, false>(a, s);
+  } else {
+    switch (P) {
+      case 8: if constexpr (MT <= 2) return launch_t<FMT, MT, 8, false, FUSEQ>(a, s); break;
+      case 4: if constexpr (MT <= 4) return launch_t<FMT, MT, 4, false, FUSEQ>(a, s); break;
+      case 2: if constexpr (MT <= 8) return launch_t<FMT, MT, 2, false, FUSEQ>(a, s); break;
+      default: break;
+    }
+    return launch_t<FMT, MT, 1, false, FUSEQ>(a, s);
   }
 }
 
-template <bool DOTS>
-static hipError_t launch_fmt(int fmt, const GemvArgs& a, int mt, hipStream_t s) {
+template <int FMT, bool DOTS, bool FUSEQ>
+static hipError_t launch_mt(const GemvArgs& a, int mt, int P, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_p<FMT, 1, DOTS, FUSEQ>(a, P, s);
+    case 2: return launch_p<FMT, 2, DOTS, FUSEQ>(a, P, s);
+    case 4: return launch_p<FMT, 4, DOTS, FUSEQ>(a, P, s);
+    case 8: return launch_p<FMT, 8, DOTS, FUSEQ>(a, P, s);
+    default: return launch_p<FMT, 16, DOTS, FUSEQ>(a, P, s);
+  }
+}
+
+template <bool DOTS, bool FUSEQ>
+static hipError_t launch_fmt(int fmt, const GemvArgs& a, int mt, int P, hipStream_t s) {
   switch (fmt) {
-    case kQ4_0: return launch_mt<kQ4_0, DOTS>(a, mt, s);
-    case kQ8_0: return launch_mt<kQ8_0, DOTS>(a, mt, s);
-    case kQ4_K: return launch_mt<kQ4_K, DOTS>(a, mt, s);
-    case kQ6_K: return launch_mt<kQ6_K, DOTS>(a, mt, s);
-    case kIQ4_NL: return launch_mt<kIQ4_NL, DOTS>(a, mt, s);
+    case kQ4_0: return launch_mt<kQ4_0, DOTS, FUSEQ>(a, mt, P, s);
+    case kQ8_0: return launch_mt<kQ8_0, DOTS, FUSEQ>(a, mt, P, s);
+    case kQ4_K: return launch_mt<kQ4_K, DOTS, FUSEQ>(a, mt, P, s);
+    case kQ6_K: return launch_mt<kQ6_K, DOTS, FUSEQ>(a, mt, P, s);
+    case kIQ4_NL: return launch_mt<kIQ4_NL, DOTS, FUSEQ>(a, mt, P, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+static hipError_t launch_any(int fmt, const GemvArgs& a, int mt, int P, bool dots, hipStream_t s) {
+  if (dots) return launch_fmt<true, false>(fmt, a, mt, P, s);
+  if (a.p.xf) return launch_fmt<false, true>(fmt, a, mt, P, s);
+  return launch_fmt<false, false>(fmt, a, mt, P, s);
 }
 
 static int token_tile(int m) {
@@ -586,29 +714,33 @@ static int token_tile(int m) {
 
 hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStream_t s) {
   if (p.m < 1 || p.m > kGemvMaxTokens || p.n < 1) return hipErrorInvalidValue;
-  if (p.tbl && p.m > kGemvMaxTokens) return hipErrorInvalidValue;
-  int mt = token_tile(p.m);
+  if (p.xf && dots_epilogue) return hipErrorInvalidValue;
+  int mt = token_tile(p.tbl ? kGroupTokens : p.m);
   GemvArgs a;
   a.p = p;
-  a.g = plan_geom(fmt, p.n, p.k, mt);
+  int P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, a.g);
   // Keep the staged activations within LDS; fall back to smaller token tiles.
-  while ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * kTileBuf > (size_t)kLdsLimit && mt > 1) {
+  while ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit && mt > 1) {
     mt >>= 1;
-    a.g = plan_geom(fmt, p.n, p.k, mt);
+    P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, a.g);
   }
-  if ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * kTileBuf > (size_t)kLdsLimit)
+  if ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit)
     return hipErrorInvalidValue;
-  if (p.tbl && mt < p.m) return hipErrorInvalidValue;  // grouped problems cannot be split
-  if (mt >= p.m || p.tbl) return dots_epilogue ? launch_fmt<true>(fmt, a, mt, s) : launch_fmt<false>(fmt, a, mt, s);
+  if (p.tbl && mt < kGroupTokens) return hipErrorInvalidValue;  // entries cannot be split
+  if (mt >= p.m || p.tbl) return launch_any(fmt, a, mt, P, dots_epilogue, s);
   // Token chunks of mt.
   for (int t0 = 0; t0 < p.m; t0 += mt) {
     GemvArgs c = a;
     c.p.m = (p.m - t0) < mt ? (p.m - t0) : mt;
-    c.p.xq = p.xq + (int64_t)t0 * p.xs;
+    if (p.xf) c.p.xf = p.xf + (int64_t)t0 * p.xs;
+    if (p.xq) c.p.xq = p.xq + (int64_t)t0 * p.xs;
     if (p.dx) c.p.dx = p.dx + (int64_t)t0 * (p.xs / 32);
+    if (p.xq_out) c.p.xq_out = p.xq_out + (int64_t)t0 * p.xs;
+    if (p.dx_out) c.p.dx_out = p.dx_out + (int64_t)t0 * (p.xs / 32);
+    if (p.sx_out) c.p.sx_out = p.sx_out + (int64_t)t0 * (p.xs / 32);
     if (p.y) c.p.y = p.y + (int64_t)t0 * p.ldy;
     if (p.dots) c.p.dots = p.dots + (int64_t)t0 * p.n * (p.k / (fmt == kQ6_K ? 16 : 32));
-    hipError_t e = dots_epilogue ? launch_fmt<true>(fmt, c, mt, s) : launch_fmt<false>(fmt, c, mt, s);
+    hipError_t e = launch_any(fmt, c, mt, P, dots_epilogue, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

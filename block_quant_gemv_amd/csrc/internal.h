@@ -18,18 +18,26 @@ int64_t fmt_row_bytes(int fmt, int64_t k);  // -1 if k is not a multiple of the 
 // Activations are already quantized (xq int8, token stride xs elements; dx
 // fp32, token stride xs/32).
 //
-// Grouped mode (tbl != nullptr, used by the MoE layer): grid.y runs over
-// `nprob` problems. tbl[0] holds the number of routed problems in use;
-// routed problem p is described at tbl + 1 + p * tbl_stride as
-// {expert, count, rows[count]} and uses matrix w + expert * w_stride; the
-// last problem (p == nprob - 1) is the shared expert w_shared applied to all
-// m tokens, whose rows are t * slots + slots - 1. For every problem, token j
+// Grouped mode (tbl != nullptr, used by the MoE layer): grid.y runs over up
+// to `nprob` table entries; tbl[0] holds the number of entries in use. Entry
+// e is stored at tbl + 1 + e * tbl_stride as {expert, count, rows[count]}
+// with count <= kGroupTokens: expert >= 0 uses matrix w + expert *
+// w_stride, expert == -1 the shared matrix w_shared. Token j of an entry
 // reads activation row rows[j] / act_div and writes output row rows[j].
+constexpr int kGroupTokens = 4;
+
 struct GemvProblem {
   const uint8_t* w = nullptr;
   const int8_t* xq = nullptr;
   const float* dx = nullptr;
   int64_t xs = 0;
+  // Fused quantization: with xf set, each workgroup quantizes the fp32
+  // activations xf (token stride xs) itself instead of reading xq/dx; the
+  // first workgroup also writes the codes to xq_out/dx_out/sx_out if set.
+  const float* xf = nullptr;
+  int8_t* xq_out = nullptr;
+  float* dx_out = nullptr;
+  int32_t* sx_out = nullptr;
   float* y = nullptr;
   int64_t ldy = 0;
   int32_t* dots = nullptr;  // checking epilogue output (int32)
@@ -42,7 +50,6 @@ struct GemvProblem {
   int nprob = 1;
   int64_t w_stride = 0;
   const uint8_t* w_shared = nullptr;
-  int slots = 1;
   int act_div = 1;
 };
 

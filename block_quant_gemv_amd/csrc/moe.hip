@@ -16,8 +16,8 @@
 //                     the selected logits, then a table that groups the
 //                     (token, slot) pairs by expert so each selected expert's
 //                     weights are read once for all tokens that chose it
-//   quantize          x -> Q8 blocks
-//   grouped GEMV      gate|up of every used expert and of the shared expert
+//   grouped GEMV      gate|up of every used expert and of the shared expert,
+//                     quantizing x to Q8 blocks in its prologue
 //   swiglu_q8         h = silu(g) * u per (token, slot), re-quantized
 //   grouped GEMV      down of every used expert and of the shared expert
 //   combine_kernel    y[t] = sum_k w[t, k] out[t, k] (slot order) + shared
@@ -67,10 +67,13 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
 
 // One workgroup of 64 * m threads. Wave t selects token t's top_k experts and
 // their softmax weights; then the (token, slot) pairs are grouped by expert
-// into the table read by the grouped GEMV:
-//   tbl[0] = number of distinct experts used;
-//   tbl[1 + p * (2 + m) ...] = {expert, count, slot rows in token order}
-// with problems p ordered by first occurrence (token-major, slot order).
+// into the table read by the grouped GEMV (entries of at most kGroupTokens
+// tokens, so each expert's weights are read once per 4 tokens that chose it):
+//   tbl[0] = number of entries;
+//   tbl[1 + e * (2 + kGroupTokens) ...] = {expert, count, slot rows}
+// Routed entries come first, ordered by the expert's first occurrence
+// (token-major, slot order), tokens ascending; then ceil(m / 4) entries of
+// the shared expert (expert = -1) covering every token.
 __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                              float* __restrict__ wts, int32_t* __restrict__ tbl, int n_experts,
                              int top_k, int m) {
@@ -81,8 +84,9 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
   int32_t* taken = sh;                              // [m * n_experts]
   int32_t* s_ids = taken + m * n_experts;           // [npairs]
   int32_t* first = s_ids + npairs;                  // [npairs] first occurrence index
-  int32_t* isfirst = first + npairs;                // [npairs]
-  int32_t* rank = isfirst + npairs;                 // [npairs]
+  int32_t* nchunk = first + npairs;                 // [npairs] chunks of a first occurrence, else 0
+  int32_t* rank = nchunk + npairs;                  // [npairs] earlier pairs with the same expert
+  int32_t* cnt = rank + npairs;                     // [npairs] total pairs of the expert (first only)
 
   for (int i = tid; i < m * n_experts; i += blockDim.x) taken[i] = 0;
   __syncthreads();
@@ -122,7 +126,6 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
   }
   __syncthreads();
 
-  const int tstride = 2 + m;
   for (int p = tid; p < npairs; p += blockDim.x) {
     const int e = s_ids[p];
     int f = p, r = 0;
@@ -134,27 +137,41 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
     }
     first[p] = f;
     rank[p] = r;
-    isfirst[p] = (f == p);
+    int c = 0;
+    if (f == p)
+      for (int q = p; q < npairs; ++q) c += (s_ids[q] == e);
+    cnt[p] = c;
+    nchunk[p] = (c + kGroupTokens - 1) / kGroupTokens;
   }
   __syncthreads();
+  const int tstride = 2 + kGroupTokens;
   for (int p = tid; p < npairs; p += blockDim.x) {
     const int f = first[p];
-    int prob = 0;
-    for (int q = 0; q < f; ++q) prob += isfirst[q];
-    int32_t* ent = tbl + 1 + (int64_t)prob * tstride;
+    int base = 0;
+    for (int q = 0; q < f; ++q) base += nchunk[q];
+    const int r = rank[p];
+    int32_t* ent = tbl + 1 + (int64_t)(base + r / kGroupTokens) * tstride;
     const int tok = p / top_k, k = p - tok * top_k;
-    ent[2 + rank[p]] = tok * (top_k + 1) + k;
-    if (f == p) {
-      int cnt = 0;
-      for (int q = p; q < npairs; ++q) cnt += (s_ids[q] == s_ids[p]);
+    ent[2 + r % kGroupTokens] = tok * (top_k + 1) + k;
+    if (r % kGroupTokens == 0) {
       ent[0] = s_ids[p];
-      ent[1] = cnt;
+      const int left = cnt[f] - r;
+      ent[1] = left < kGroupTokens ? left : kGroupTokens;
     }
   }
   if (tid == 0) {
-    int used = 0;
-    for (int q = 0; q < npairs; ++q) used += isfirst[q];
-    tbl[0] = used;
+    int routed = 0;
+    for (int q = 0; q < npairs; ++q) routed += nchunk[q];
+    const int nsh = (m + kGroupTokens - 1) / kGroupTokens;
+    for (int c = 0; c < nsh; ++c) {
+      int32_t* ent = tbl + 1 + (int64_t)(routed + c) * tstride;
+      const int t0 = c * kGroupTokens;
+      const int n = (m - t0) < kGroupTokens ? (m - t0) : kGroupTokens;
+      ent[0] = -1;
+      ent[1] = n;
+      for (int j = 0; j < n; ++j) ent[2 + j] = (t0 + j) * (top_k + 1) + top_k;
+    }
+    tbl[0] = routed + nsh;
   }
 }
 
@@ -172,7 +189,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   y[i] = acc + o[(int64_t)top_k * hidden];
 }
 
-int64_t moe_table_ints(int m, int top_k) { return 1 + (int64_t)m * top_k * (2 + m); }
+// Entries: at most one per (token, slot) pair plus the shared-expert chunks.
+static int64_t moe_max_entries(int m, int top_k) { return (int64_t)m * top_k + (m + kGroupTokens - 1) / kGroupTokens; }
+int64_t moe_table_ints(int m, int top_k) { return 1 + moe_max_entries(m, top_k) * (2 + kGroupTokens); }
 
 hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (c.m < 1 || c.m > kRouterMaxTok || c.top_k > 16) return hipErrorInvalidValue;
@@ -183,27 +202,28 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (e != hipSuccess) return e;
   // 2. top-k, softmax and grouping
   const int npairs = c.m * c.top_k;
-  const size_t lds = ((size_t)c.m * c.n_experts + 4 * (size_t)npairs) * 4;
+  const size_t lds = ((size_t)c.m * c.n_experts + 6 * (size_t)npairs) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(64 * c.m), lds, s, c.logits, c.ids, c.wts, c.tbl,
                      c.n_experts, c.top_k, c.m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // 3. quantize x
-  if ((e = launch_quant_q8(c.x, c.xq, c.dx, c.sx, (int64_t)c.m * (c.hidden / 32), s)) != hipSuccess) return e;
-  // 4. gate|up of the used experts and the shared expert
+  // 3. gate|up of the used experts and the shared expert; the kernel
+  // quantizes x in its prologue and the shared-expert workgroup 0 stores the
+  // codes in the workspace
   const int slots = c.top_k + 1;
-  const int maxprob = (npairs < c.n_experts ? npairs : c.n_experts) + 1;
+  const int maxprob = (int)moe_max_entries(c.m, c.top_k);
   GemvProblem g;
   g.w = c.gu;
   g.w_stride = c.gu_stride;
   g.w_shared = c.gu_shared;
   g.tbl = c.tbl;
-  g.tbl_stride = 2 + c.m;
+  g.tbl_stride = 2 + kGroupTokens;
   g.nprob = maxprob;
-  g.slots = slots;
   g.act_div = slots;
-  g.xq = c.xq;
-  g.dx = c.dx;
+  g.xf = c.x;
+  g.xq_out = c.xq;
+  g.dx_out = c.dx;
+  g.sx_out = c.sx;
   g.xs = c.hidden;
   g.y = c.gu_out;
   g.ldy = 2 * c.inter;
@@ -212,12 +232,16 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   g.m = c.m;
   for (int i = 0; i < 4; ++i) g.cb[i] = c.cb[i];
   if ((e = launch_gemv(c.fmt, g, false, s)) != hipSuccess) return e;
-  // 5. SwiGLU + re-quantization for every slot row
+  // 4. SwiGLU + re-quantization for every slot row
   if ((e = launch_swiglu_q8(c.gu_out, 2 * c.inter, c.h, c.hq, c.hd, c.hs, (int64_t)c.m * slots, c.inter,
                             s)) != hipSuccess)
     return e;
-  // 6. down of the used experts and the shared expert
+  // 5. down of the used experts and the shared expert
   GemvProblem d = g;
+  d.xf = nullptr;
+  d.xq_out = nullptr;
+  d.dx_out = nullptr;
+  d.sx_out = nullptr;
   d.w = c.dn;
   d.w_stride = c.dn_stride;
   d.w_shared = c.dn_shared;
@@ -230,7 +254,7 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   d.n = c.hidden;
   d.k = c.inter;
   if ((e = launch_gemv(c.fmt, d, false, s)) != hipSuccess) return e;
-  // 7. weighted combine
+  // 6. weighted combine
   const int64_t total = (int64_t)c.m * c.hidden;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, c.out, c.wts,
                      c.y, c.hidden, c.m, c.top_k);

@@ -22,20 +22,17 @@ __global__ __launch_bounds__(256) void quant_q8_kernel(const float* __restrict__
   const int64_t blk = gt >> 3;
   const int part = (int)(gt & 7);
   // Whole groups of 8 lanes are either all in range or all out of range, so
-  // the shuffles below always see valid partners.
+  // the DPP reductions below always read active partner lanes.
   if (blk >= nblocks) return;
   const float4 v = reinterpret_cast<const float4*>(x)[blk * 8 + part];
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = fmaxf(a, __shfl_xor(a, 1, 8));
-  a = fmaxf(a, __shfl_xor(a, 2, 8));
-  a = fmaxf(a, __shfl_xor(a, 4, 8));
+  a = max8(a);
   const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
   int s;
   const uint32_t packed = q8_pack4(v, d, s);
   reinterpret_cast<uint32_t*>(xq)[blk * 8 + part] = packed;
-  s += __shfl_xor(s, 1, 8);
-  s += __shfl_xor(s, 2, 8);
-  s += __shfl_xor(s, 4, 8);
+  s = sum4(s);
+  s += other_quad(s);
   if (part == 0) {
     dx[blk] = d;
     if (sx) sx[blk] = s;

@@ -36,16 +36,13 @@ __global__ __launch_bounds__(256) void swiglu_q8_kernel(const float* __restrict_
   v.w = g.w / (1.0f + expf(-g.w)) * u.w;
   *reinterpret_cast<float4*>(h + r * inter + col) = v;
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = fmaxf(a, __shfl_xor(a, 1, 8));
-  a = fmaxf(a, __shfl_xor(a, 2, 8));
-  a = fmaxf(a, __shfl_xor(a, 4, 8));
+  a = max8(a);
   const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
   int s;
   const uint32_t packed = q8_pack4(v, d, s);
   *reinterpret_cast<uint32_t*>(hq + r * inter + col) = packed;
-  s += __shfl_xor(s, 1, 8);
-  s += __shfl_xor(s, 2, 8);
-  s += __shfl_xor(s, 4, 8);
+  s = sum4(s);
+  s += other_quad(s);
   if (part == 0) {
     hd[r * nbr + b] = d;
     hs[r * nbr + b] = s;

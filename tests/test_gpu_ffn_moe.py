@@ -153,3 +153,36 @@ def test_moe_staged(E, H, I, K, m):
     ref = omoe.moe_ref(wr, gu_all, dn_all, gu_sh, dn_sh, x, H, I, K)
     say(f"  M5 {e5:.2e}  independent {normwise(y, ref['y']):.2e}")
     assert e5 <= TOL
+
+
+def test_graph_replays_match_eager():
+    # The library only enqueues kernels (no memsets, no host sync), so its
+    # calls can be captured in a HIP graph. Replay several times with eager
+    # work and synchronisations in between; every replay must equal eager.
+    H, I, E, K, m = 512, 128, 16, 4, 3
+    wr, gu_all, dn_all, gu_sh, dn_sh = _moe_inputs(E, H, I, seed=41)
+    x = dev(synth.activations(42, m, H))
+    mo = qg.MoE(H, I, E, K, "q4_0", max_m=m)
+    args = [dev(a) for a in (wr, gu_all, dn_all, gu_sh, dn_sh)]
+    g = qg.GEMV("q4_k", 512, 2048)
+    wg = dev(synth.weights("q4_k", 512, 2048, seed=43))
+    xg = dev(synth.activations(44, 1, 2048))
+    y_moe = torch.empty((m, H), dtype=torch.float32, device="cuda")
+    y_gemv = torch.empty((1, 512), dtype=torch.float32, device="cuda")
+    mo.run(*args, x, y=y_moe)
+    g.run(wg, xg, y=y_gemv)
+    torch.cuda.synchronize()
+    ref_moe, ref_gemv = y_moe.clone(), y_gemv.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mo.run(*args, x, y=y_moe)
+        g.run(wg, xg, y=y_gemv)
+    for rep in range(4):
+        y_moe.zero_()
+        y_gemv.zero_()
+        g.run(wg, dev(synth.activations(45 + rep, 1, 2048)))   # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_moe, ref_moe), f"replay {rep}: MoE differs"
+        assert torch.equal(y_gemv, ref_gemv), f"replay {rep}: GEMV differs"

@@ -41,6 +41,67 @@ def test_quantizer_bit_exact(seed, m, k):
     assert np.array_equal(host(sx), rs)
 
 
+def _near_tie_blocks():
+    """Blocks whose elements sit at, and a few ulps around, the fp32 values
+    closest to (k + 1/2) * d for many k and several scales d: the cases where
+    the code depends on the correctly rounded quotient."""
+    rows = []
+    for a in (np.float32(127.0), np.float32(100.0), np.float32(3.1), np.float32(0.017), np.float32(5e-30)):
+        d = np.float32(a) / np.float32(127)
+        ks = np.arange(-126, 126)
+        base = ((ks + 0.5) * np.float64(d)).astype(np.float32)
+        cands = [base]
+        for step in (1, 2, 3):
+            up = base.copy()
+            dn = base.copy()
+            for _ in range(step):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+            cands += [up, dn]
+        vals = np.concatenate(cands)
+        vals = vals[np.abs(vals) < a]
+        nblk = -(-vals.size // 31)
+        blk = np.zeros((nblk, 32), np.float32)
+        flat = np.zeros(nblk * 31, np.float32)
+        flat[: vals.size] = vals
+        blk[:, 1:] = flat.reshape(nblk, 31)
+        blk[:, 0] = a
+        rows.append(blk.reshape(-1))
+    x = np.concatenate(rows)
+    pad = (-x.size) % 32
+    return np.concatenate([x, np.zeros(pad, np.float32)])[None, :]
+
+
+def test_quantizer_near_ties_bit_exact():
+    x = _near_tie_blocks()
+    say(f"quantizer near ties: {x.size} elements")
+    xq, dx, sx = qg.debug_quantize(dev(x))
+    torch.cuda.synchronize()
+    rq, rd, rs = quantize_q8(x)
+    assert np.array_equal(host(dx).view(np.int32), rd.view(np.int32))
+    bad = np.argwhere(host(xq) != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, e.g. {bad[:5].tolist()}"
+    assert np.array_equal(host(sx), rs)
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q6_k"])
+def test_fused_quantize_writes_workspace_codes(fmt):
+    # qgemv_run quantizes inside the GEMV kernel; the codes it leaves in the
+    # workspace must equal the standalone rule bit for bit.
+    x = _near_tie_blocks()[:, :2048]
+    k = x.shape[1]
+    n = 64
+    w = synth.weights(fmt, n, k, seed=2)
+    g = qg.GEMV(fmt, n, k)
+    ws = g.workspace(1)
+    g.run(dev(w), dev(x), ws=ws)
+    torch.cuda.synchronize()
+    rq, rd, rs = quantize_q8(x)
+    assert np.array_equal(host(g.ws_view(ws, 1, "xq", torch.int8, k)), rq[0])
+    assert np.array_equal(host(g.ws_view(ws, 1, "dx", torch.float32, k // 32)).view(np.int32), rd[0].view(np.int32))
+    assert np.array_equal(host(g.ws_view(ws, 1, "sx", torch.int32, k // 32)), rs[0])
+
+
 # ----------------------------------------------------------------- GEMV --
 
 SMALL = [
