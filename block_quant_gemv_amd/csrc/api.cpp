@@ -77,6 +77,7 @@ Layout layout_of(const qgemv_plan* h, int m) {
     L.add("xq", (size_t)m * d.k);
     L.add("dx", (size_t)m * (d.k / 32) * 4);
     L.add("sx", (size_t)m * (d.k / 32) * 4);
+    if (m > kGemvMaxTokens && mfma_supported(d.fmt)) L.add("partials", gemm32_partials_bytes(d.n, d.k));
   } else if (d.kind == QKIND_FFN) {
     L.add("xq", (size_t)m * d.hidden);
     L.add("dx", (size_t)m * (d.hidden / 32) * 4);
@@ -281,7 +282,8 @@ int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* w
   const float* dx = region<float>(wsm, L, "dx");
   const int32_t* sx = region<int32_t>(wsm, L, "sx");
   if (m > kGemvMaxTokens && mfma_supported(d.fmt))
-    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y, d.n, d.k, m, s),
+    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y,
+                                      region<float>(wsm, L, "partials"), d.n, d.k, m, s),
                         "gemm32");
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w);

@@ -209,3 +209,31 @@ def test_single_hip_runtime_loaded():
     libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(libs) == 1, libs
     assert any("libqgemv.so" in ln for ln in maps.splitlines())
+
+
+# ------------------------------------------------------- M = 32, int8 MFMA --
+
+@pytest.mark.parametrize("fmt,n,k,m", [("q4_k", 12288, 4096, 32),    # batched shape, Q4_K
+                                       ("q6_k", 4096, 12288, 32),    # batched shape, Q6_K
+                                       ("q4_k", 100, 512, 17),       # ragged rows, odd tokens
+                                       ("q6_k", 33, 1280, 20),       # K not a multiple of the split
+                                       ("q4_k", 64, 256, 32)])
+def test_mfma_batched_parity(fmt, n, k, m):
+    say(f"mfma {fmt} n={n} k={k} m={m}")
+    w = synth.weights(fmt, n, k, seed=n + m)
+    x = synth.activations(k + m, m, k)
+    g = qg.GEMV(fmt, n, k, max_m=32)
+    wd = dev(w)
+    full, y = guarded(torch, m * n, torch.float32)
+    g.run(wd, dev(x), y.view(m, n))
+    xq, dx, sx = quantize_q8(x)
+    dots = host(g.block_dots(wd, dev(xq)))
+    torch.cuda.synchronize()
+    assert canary_ok(torch, full, m * n)
+    ref_dots = og.block_dots(fmt, w, n, k, xq)
+    bad = np.argwhere(dots != ref_dots)
+    assert bad.size == 0, f"{len(bad)} MFMA block dots differ, first {bad[:3].tolist()}"
+    ref = og.gemv_dequant(fmt, w, n, k, xq, dx)
+    e = normwise(host(y).reshape(m, n), ref)
+    say(f"  normwise error {e:.3e}")
+    assert e <= TOL
