@@ -98,6 +98,86 @@ def time_graph(g, n_inner, reps, warm=2):
     return e0.elapsed_time(e1) * 1e3 / (reps * n_inner)
 
 
+GEMV_SOURCES = ("gemv.hip", "common.cuh", "internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_q8_0_k4096.json")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "block_quant_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from recorded counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counts), or None when
+    none is recorded or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 256 * 2 ** 20    # one --calibrate-copy launch reads and writes this many bytes
+
+
+def _pmc_rows(path, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc output: its
+    SQLite database (*_results.db, view counters_collection) or its
+    counter_collection CSV."""
+    if path.endswith(".db"):
+        import sqlite3
+        con = sqlite3.connect(path)
+        try:
+            rows = con.execute("SELECT kernel_name, value FROM counters_collection WHERE counter_name = ?",
+                               (counter,)).fetchall()
+        finally:
+            con.close()
+        return [(n, float(v)) for n, v in rows]
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def record_traffic(fetch_out, write_out, copy_fetch_out, copy_write_out):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the Q8_0 GEMV kernel,
+    each scaled by what the same counter reads for a plain device copy of
+    COPY_BYTES (its largest dispatch), summed into HBM bytes per launch."""
+    def scale(rows):
+        kib = max(v for _, v in rows)
+        return COPY_BYTES / (kib * 1024.0)
+
+    def gemv_mean(rows):
+        # --only-dominant runs no GEMV kernel other than the Q8_0 one
+        vals = [v for name, v in rows if "gemv_kernel" in name]
+        return sum(vals) / len(vals), len(vals)
+
+    fs = scale(_pmc_rows(copy_fetch_out, "FETCH_SIZE"))
+    ws_ = scale(_pmc_rows(copy_write_out, "WRITE_SIZE"))
+    fk, nf = gemv_mean(_pmc_rows(fetch_out, "FETCH_SIZE"))
+    wk, nw = gemv_mean(_pmc_rows(write_out, "WRITE_SIZE"))
+    rec = {"kernel_source_digest": kernel_source_digest(),
+           "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+           "fetch_scale": round(fs, 4), "write_scale": round(ws_, 4), "dispatches": [nf, nw],
+           "hbm_bytes_per_launch": round(fk * 1024 * fs + wk * 1024 * ws_)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(mats, k, budget_s=12.0):
     """The oracle (dequantize to fp64, fp64 matvec) timed on this host's cores
     over a bounded sample: the first rows of each headline matrix."""
@@ -140,7 +220,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only-dominant", action="store_true",
+                    help="run only the dominant GEMV kernel back to back (for counter runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 256 MiB device copy a few times (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn rocprofv3 --pmc counter files into the recorded HBM traffic (no GPU use)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path).", file=sys.stderr)
@@ -152,6 +240,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 8 x 256 MiB")
+        return 0
     K = 4096
     mats = [(f, n) for f in ("q8_0", "q4_k") for n in (4096, 12288, 24576)]
     step_bytes = sum(n * synth.row_bytes(f, K) for f, n in mats)
@@ -164,16 +260,35 @@ def main():
         ws.append(g.workspace(1))
         xs.append(dev(synth.activations(200 + j, 1, K)))
         ys.append(torch.empty((1, n), dtype=torch.float32, device="cuda"))
-        W.append(rotated(synth.weights(f, n, K, seed=100 + j), R))
-    dom = mats.index(("q8_0", 24576))
-    dom_bytes = mats[dom][1] * synth.row_bytes("q8_0", K)
-    dom_alg = dom_bytes + K + (K // 32) * 4 + mats[dom][1] * 4   # weights + xq + dx + y
-    stream = torch.cuda.current_stream()
+        skip = args.only_dominant and f != "q8_0"
+        W.append(None if skip else rotated(synth.weights(f, n, K, seed=100 + j), R))
+    # The dominant kernel is the Q8_0 GEMV (the largest share of the step's
+    # time). It is launched at the three Q8_0 shapes of the step in equal
+    # numbers, here and in the step, so its average launch carries the mean
+    # of their algorithmic bytes: packed weights + int8 codes + fp32 scales of
+    # x + fp32 outputs.
+    dom = [j for j, (f, _) in enumerate(mats) if f == "q8_0"]
+    dom_alg = sum(mats[j][1] * synth.row_bytes("q8_0", K) + K + (K // 32) * 4 + mats[j][1] * 4
+                  for j in dom) / len(dom)
 
     def step(i):
         r = i % R
         for j, g in enumerate(plans):
             g.run(W[j][r], xs[j], y=ys[j], ws=ws[j])
+
+    def dom_launches(i):
+        # the dominant kernel's launches of one step, on already-quantized x
+        for j in dom:
+            plans[j].run_quantized(W[j][i % R], ws[j], 1, ys[j])
+
+    for j in dom:
+        plans[j].quantize(xs[j], ws[j])
+    if args.only_dominant:
+        for i in range(args.steps):
+            dom_launches(i)
+        torch.cuda.synchronize()
+        log(f"ran the Q8_0 GEMV launches of {args.steps} steps")
+        return 0
 
     # One HIP graph holds R steps (one per weight copy); replaying it removes
     # the Python/launch overhead between the kernels, not any of their work.
@@ -197,15 +312,16 @@ def main():
     # Eager (no graph) step time, for reference.
     eager_us = time_calls(lambda i: step(i), 3 * R, warm=R) if not args.no_extras else None
 
-    # Dominant kernel alone: its GEMV launches back to back (activations
-    # quantized once), HIP events around a graph of R launches.
-    dg = plans[dom]
-    dg.quantize(xs[dom], ws[dom])
-    gd = graph_of(lambda i: dg.run_quantized(W[dom][i % R], ws[dom], 1, ys[dom]), R)
-    dom_us = time_graph(gd, R, reps=max(4, 64 // R))
+    # Dominant kernel alone: its launches back to back (activations quantized
+    # once), HIP events on the library's stream around a graph of R steps'
+    # worth of them.
+    for j in dom:
+        plans[j].quantize(xs[j], ws[j])
+    gd = graph_of(dom_launches, R)
+    dom_us = time_graph(gd, R * len(dom), reps=max(4, 64 // R))
     achieved = dom_alg / (dom_us * 1e-6) / 1e9
     log(f"step {ms_step * 1e3:.1f} us ({wall / steps * 1e3:.3f} ms wall), {value:.0f} GB/s; "
-        f"Q8_0 24576x4096 GEMV kernel {dom_us:.2f} us -> {achieved:.0f} GB/s")
+        f"Q8_0 GEMV kernel {dom_us:.2f} us per launch -> {achieved:.0f} GB/s")
 
     # Per-matrix call times (quantize + GEMV), graph-replayed.
     per = {}
@@ -215,6 +331,7 @@ def main():
         b = n * synth.row_bytes(f, K)
         per[f"{f}_{n}x{K}"] = {"us": round(us, 3), "gbps": round(b / (us * 1e-6) / 1e9, 1)}
 
+    traffic = recorded_traffic()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -226,10 +343,11 @@ def main():
                    "weight_bytes_per_step": step_bytes, "rotating_copies": R,
                    "timing": "HIP graph of the step's launches, replayed"},
         "pct_hbm_peak": round(100 * value * 1e9 / HBM_PEAK, 2),
-        "roofline": {"bound": "hbm", "kernel": "gemv Q8_0 N=24576 K=4096 M=1",
+        "roofline": {"bound": "hbm",
+                     "kernel": "gemv_kernel<Q8_0> (M=1, K=4096, N=4096/12288/24576 in equal numbers)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
-                     "bytes_per_launch": dom_alg, "avg_kernel_us": round(dom_us, 3)},
+                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
+                     "bytes_per_launch": round(dom_alg), "avg_kernel_us": round(dom_us, 3)},
     }
 
     out["per_matrix"] = per
@@ -293,6 +411,23 @@ def extras(qg, synth, torch):
     res["q4_0_2048_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
     log(f"q4_0 2048x2048: {us:.2f} us, {res['q4_0_2048_gbps']} GB/s")
     del Ws
+    # M=32 batched GEMMs on int8 MFMA (Q4_K 4096 -> 12288, Q6_K 12288 -> 4096)
+    for fmt, n, k in (("q4_k", 12288, 4096), ("q6_k", 4096, 12288)):
+        g = qg.GEMV(fmt, n, k, max_m=32)
+        b = n * synth.row_bytes(fmt, k)
+        R = copies_for(b, cap=64)
+        Ws = rotated(synth.weights(fmt, n, k, seed=340), R)
+        x = dev(synth.activations(341, 32, k))
+        y = torch.empty((32, n), dtype=torch.float32, device="cuda")
+        ws = g.workspace(32)
+        gg = graph_of(lambda i: g.run(Ws[i % R], x, y=y, ws=ws), R)
+        us = time_graph(gg, R, reps=max(2, 64 // R))
+        ops = 2.0 * 32 * n * k
+        res[f"m32_{fmt}_{n}x{k}_us"] = round(us, 2)
+        res[f"m32_{fmt}_{n}x{k}_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+        res[f"m32_{fmt}_{n}x{k}_mfma_util"] = round(ops / (us * 1e-6) / 5.0e15, 4)
+        log(f"m=32 {fmt} {n}x{k}: {us:.2f} us, {res[f'm32_{fmt}_{n}x{k}_gbps']} GB/s")
+        del Ws
     # MoE
     E, Hm, Im, Kt = 256, 2048, 512, 8
     gu_all, dn_all = synth.moe_experts(330, E, Hm, Im)

@@ -77,7 +77,7 @@ Layout layout_of(const qgemv_plan* h, int m) {
     L.add("xq", (size_t)m * d.k);
     L.add("dx", (size_t)m * (d.k / 32) * 4);
     L.add("sx", (size_t)m * (d.k / 32) * 4);
-    if (m > kGemvMaxTokens && mfma_supported(d.fmt)) L.add("partials", gemm32_partials_bytes(d.n, d.k));
+    if (m >= kMfmaMinTokens && mfma_supported(d.fmt)) L.add("partials", gemm32_partials_bytes(d.n, d.k));
   } else if (d.kind == QKIND_FFN) {
     L.add("xq", (size_t)m * d.hidden);
     L.add("dx", (size_t)m * (d.hidden / 32) * 4);
@@ -281,7 +281,7 @@ int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* w
   const int8_t* xq = region<int8_t>(wsm, L, "xq");
   const float* dx = region<float>(wsm, L, "dx");
   const int32_t* sx = region<int32_t>(wsm, L, "sx");
-  if (m > kGemvMaxTokens && mfma_supported(d.fmt))
+  if (m >= kMfmaMinTokens && mfma_supported(d.fmt))
     return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y,
                                       region<float>(wsm, L, "partials"), d.n, d.k, m, s),
                         "gemm32");
@@ -319,7 +319,7 @@ int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* w
   if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run: launch failure injected (QGEMV_FAULT)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const qgemv_desc& d = h->d;
-  if (m > kGemvMaxTokens || d.k > kFusedQuantMaxK) {
+  if (m > kGemvMaxTokens || d.k > kFusedQuantMaxK || (m >= kMfmaMinTokens && mfma_supported(d.fmt))) {
     if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
     return gemv_from_quantized(h, w, y, m, ws, s);
   }
@@ -493,7 +493,7 @@ int qgemv_debug_block_dots(qgemv_t h, const void* w, const int8_t* xq, int32_t* 
   if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qgemv_debug_block_dots: m=%d not in 1..%d", m, d.max_m);
   if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots: launch failure injected");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m > kGemvMaxTokens && mfma_supported(d.fmt))
+  if (m >= kMfmaMinTokens && mfma_supported(d.fmt))
     return check_launch(launch_gemm32_dots(d.fmt, static_cast<const uint8_t*>(w), xq, dots, d.n, d.k, m, s),
                         "gemm32 dots");
   GemvProblem p;

@@ -62,5 +62,8 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
 
 // Largest token count one GEMV launch handles.
 constexpr int kGemvMaxTokens = 16;
+// From this many tokens on, Q4_K and Q6_K GEMVs run on int8 MFMA (the VALU
+// dot-product kernel's cost grows with the token count, the MFMA one's not).
+constexpr int kMfmaMinTokens = 9;
 
 }  // namespace qg

@@ -1,5 +1,5 @@
-// Batched (17..32 tokens) GEMM over packed Q4_K / Q6_K weights with int8
-// MFMA, gfx950.
+// Batched (9..32 tokens per launch tile) GEMM over packed Q4_K / Q6_K
+// weights with int8 MFMA, gfx950.
 //
 // With 32 tokens the work is a real dense contraction: the vector int8 dot
 // products of the decode GEMV would make the VALU the bottleneck, so the
@@ -28,6 +28,10 @@
 namespace qg {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+
+#ifndef QG_MFMA_UNROLL
+#define QG_MFMA_UNROLL 2   // scale groups of a super-block decoded together
+#endif
 
 constexpr int kMT = 32;        // token tile
 constexpr int kRowsPerWave = 32;
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm32_kernel(const uint8_t* __re
       dmin = half_bits(h.x >> 16);
       const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
       const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
-#pragma unroll
+#pragma unroll QG_MFMA_UNROLL
       for (int j = 0; j < 8; ++j) {
         const u32x4 q = *reinterpret_cast<const u32x4*>(blk + 16 + 16 * j);
         u32x4 a = {0u, 0u, 0u, 0u};
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm32_kernel(const uint8_t* __re
       }
     } else {  // Q6_K
       d = half_bits(*reinterpret_cast<const uint16_t*>(blk));
-#pragma unroll
+#pragma unroll QG_MFMA_UNROLL
       for (int grp = 0; grp < 8; ++grp) {
         // ql[8g .. 8g+7] and qh[0..7] of this 32-element group; the block is
         // only 2-byte aligned, so read 16-bit halves.

@@ -156,8 +156,12 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t *bytes);
 
 /* y[m, n] = W . x for a QKIND_GEMV plan (decode GEMV, 1 <= m <= max_m).
  * x: fp32 [m, k], 16-byte aligned. y: fp32 [m, n]. ws: workspace of at
- * least qgemv_workspace_size(h, m) bytes, 256-byte aligned. Two launches
- * (activation quantizer, then the format's GEMV kernel) on `stream`. */
+ * least qgemv_workspace_size(h, m) bytes, 256-byte aligned. Launches on
+ * `stream`: for k <= 2048 and m <= 16 one GEMV kernel that quantizes x in its
+ * prologue; otherwise the activation quantizer, then the format's GEMV
+ * kernel. For Q4_K and Q6_K with m >= 9 the block dots run on int8 matrix
+ * cores over 32-token tiles (a K-split GEMM plus a fixed-order reduction);
+ * results follow the same rounding contract either way. */
 int qgemv_run(qgemv_t h, const void *w, const float *x, float *y, int m,
               void *ws, size_t ws_bytes, void *stream);
 
