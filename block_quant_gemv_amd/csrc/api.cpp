@@ -255,7 +255,10 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t* bytes) {
 namespace {
 
 // Largest K for which qgemv_run fuses the activation quantizer into the GEMV.
-constexpr int64_t kFusedQuantMaxK = 2048;
+#ifndef QG_FUSED_MAXK
+#define QG_FUSED_MAXK 2048
+#endif
+constexpr int64_t kFusedQuantMaxK = QG_FUSED_MAXK;
 
 int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const char* fn) {
   if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);

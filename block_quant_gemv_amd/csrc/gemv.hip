@@ -33,7 +33,7 @@
 namespace qg {
 
 #ifndef QG_TILE_CAP
-#define QG_TILE_CAP 10240
+#define QG_TILE_CAP 0     // > 0: one step-size cap for every format (tuning)
 #endif
 #ifndef QG_WGS_PER_CU
 #define QG_WGS_PER_CU 0   // 0: as many workgroups as fit (occupancy query)
@@ -42,15 +42,31 @@ namespace qg {
 #ifndef QG_BALANCE
 #define QG_BALANCE 0      // 1: size the grid so every wave gets the same step count
 #endif
+#ifndef QG_WLOAD_AUX
+#define QG_WLOAD_AUX 2    // cache-policy bits of the weight loads (2: non-temporal, read once)
+#endif
+#ifndef QG_PREFETCH
+#define QG_PREFETCH 1     // weight steps in flight per wave (1 or 2)
+#endif
 #ifndef QG_WAVES_PER_WG
 #define QG_WAVES_PER_WG 4
 #endif
 
 constexpr int kWavesPerWG = QG_WAVES_PER_WG;
-constexpr int kTileCap = QG_TILE_CAP;           // packed bytes per step (max)
+// Packed bytes per step (max), per format. Measured on MI355X: smaller steps
+// give each wave more steps (a shorter pipeline tail after its last load)
+// and leave LDS for more resident waves; below ~2.5 KB the per-step overhead
+// wins. Q8_0 rows (4352 B at K=4096) are then split into K-segments.
+constexpr int tile_cap(int fmt) {
+  return QG_TILE_CAP > 0 ? QG_TILE_CAP
+         : fmt == kQ8_0 ? 2560 : fmt == kQ4_K ? 5120 : fmt == kIQ4_NL ? 4608 : 3584;
+}
 // 16-byte chunks a step can span (alignment adds up to two), per lane.
-constexpr int kLoadsPerLane = (kTileCap + 32 + 1023) / 1024;
+template <int FMT> constexpr int loads_per_lane() { return (tile_cap(FMT) + 32 + 1023) / 1024; }
 constexpr int kLdsLimit = 160 * 1024;
+// Word 3 of a raw (unswizzled, unformatted) buffer resource on gfx9-family
+// GPUs, gfx950 included.
+constexpr int kBufferDword3 = 0x00020000;
 
 // ------------------------------------------------------------ activations --
 
@@ -284,9 +300,39 @@ QG_DEV int64_t seg_bytes(int units) { return (int64_t)(units / F::kUPB) * F::kBB
 // (xq/dx) or, with FUSEQ, by quantizing fp32 x here: eight lanes per 32-element
 // unit, the same arithmetic as the standalone quantizer. Token slots past
 // mcnt are never read, so they are not staged.
+// The first batch of token 0's staging input, loaded before the first
+// weight step is requested: vector loads return in issue order, so inputs
+// requested after the weights could only be used once the weights arrived.
+struct StagePre {
+  float4 v[4];   // FUSEQ: fp32 x, tasks threadIdx.x + r * blockDim.x
+  int4 lo, hi;   // otherwise: codes of unit threadIdx.x
+  float d;
+};
+
+template <bool DOTS, bool FUSEQ>
+QG_DEV void stage_prefetch(StagePre& pre, const GemvProblem& p, int U, int64_t ar) {
+  if constexpr (FUSEQ) {
+    const float4* xr = reinterpret_cast<const float4*>(p.xf + ar * p.xs);
+    const int ntask = U * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = threadIdx.x + r * blockDim.x;
+      pre.v[r] = i < ntask ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    const int u = threadIdx.x;
+    if (u < U) {
+      const int4* src = reinterpret_cast<const int4*>(p.xq + ar * p.xs);
+      pre.lo = src[2 * u];
+      pre.hi = src[2 * u + 1];
+      pre.d = DOTS ? 0.0f : p.dx[ar * (p.xs / 32) + u];
+    }
+  }
+}
+
 template <int MT, bool DOTS, bool FUSEQ, typename RowFn>
 QG_DEV void stage_activations(uint8_t* smem, const GemvProblem& p, int U, int mcnt, RowFn out_row,
-                              bool write_back) {
+                              bool write_back, const StagePre& pre) {
   const int tokb = act_token_bytes(U);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -300,10 +346,15 @@ QG_DEV void stage_activations(uint8_t* smem, const GemvProblem& p, int U, int mc
       const int ntask = U * 8;
       for (int base = threadIdx.x; base < ntask; base += 4 * blockDim.x) {
         float4 vb[4];
+        if (t == 0 && base == (int)threadIdx.x) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = base + r * blockDim.x;
-          vb[r] = i < ntask ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int r = 0; r < 4; ++r) vb[r] = pre.v[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = base + r * blockDim.x;
+            vb[r] = i < ntask ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -336,10 +387,17 @@ QG_DEV void stage_activations(uint8_t* smem, const GemvProblem& p, int U, int mc
       const int4* src = reinterpret_cast<const int4*>(p.xq + ar * p.xs);
       const float* dxr = DOTS ? nullptr : p.dx + ar * (p.xs / 32);
       for (int u = threadIdx.x; u < U; u += blockDim.x) {
-        const int4 lo = src[2 * u];
-        const int4 hi = src[2 * u + 1];
+        int4 lo, hi;
         float d = 0.0f;
-        if constexpr (!DOTS) d = dxr[u];
+        if (t == 0 && u == (int)threadIdx.x) {
+          lo = pre.lo;
+          hi = pre.hi;
+          d = pre.d;
+        } else {
+          lo = src[2 * u];
+          hi = src[2 * u + 1];
+          if constexpr (!DOTS) d = dxr[u];
+        }
         const int ones = 0x01010101;
         const int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
         const int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
@@ -380,7 +438,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
 
   const int U = g.U;
   const int tokb = act_token_bytes(U);
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   uint8_t* tile = smem + g.act_bytes + wid * g.tile_buf;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerWG;
@@ -409,28 +467,49 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
   // K-segments. One register buffer holds the next step while the current
   // one is decoded from LDS.
   const int64_t rt_first = (int64_t)blockIdx.x * kWavesPerWG + wid;
-  u32x4 buf[kLoadsPerLane];
-  auto issue = [&](int64_t rt, int seg) __attribute__((always_inline)) {
-    int64_t b0, b1;
-    step_range(rt, seg, b0, b1);
+  constexpr int kLPL = loads_per_lane<FMT>();
+  // Loads go through a buffer resource that spans exactly the step's 16-byte
+  // chunks: lanes past the end (and a whole wave past the last step) read
+  // zeros with no memory access. Every load is issued unconditionally, so the
+  // compiler can wait for earlier loads without draining these.
+  auto issue = [&](u32x4(&buf)[kLPL], int64_t rt, int seg) __attribute__((always_inline)) {
+    const bool ok = rt < g.nrowtiles;
+    int64_t b0 = 0, b1 = 0;
+    if (ok) step_range(rt, seg, b0, b1);
     const int64_t a0 = b0 & ~(int64_t)15;
-    const int nch = (int)((((b1 + 15) & ~(int64_t)15) - a0) >> 4);
-    const u32x4* src = reinterpret_cast<const u32x4*>(W + a0);
+    const int nch = ok ? (int)((((b1 + 15) & ~(int64_t)15) - a0) >> 4) : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + a0), 0, nch * 16, kBufferDword3);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerLane; ++i) {
-      const int c = lane + kWave * i;
-      if (c < nch) buf[i] = src[c];
-    }
+    for (int i = 0; i < kLPL; ++i)
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + kWave * i) * 16, 0, QG_WLOAD_AUX);
   };
-  // First weight step in flight before the activation staging, so the two
-  // memory round trips overlap.
-  if (rt_first < g.nrowtiles) issue(rt_first, 0);
+  // Staging input first, then the first weight step: both round trips
+  // overlap, and the staging arithmetic runs while the weights are in flight.
+  StagePre pre;
+  if (mcnt > 0) stage_prefetch<DOTS, FUSEQ>(pre, p, U, out_row(0) / p.act_div);
+  // The step after (rt, seg) in this wave's sequence.
+  auto next_step = [&](int64_t rt, int seg, int64_t& rt2, int& seg2) __attribute__((always_inline)) {
+    rt2 = rt;
+    seg2 = seg + 1;
+    if (seg2 == g.nseg) { seg2 = 0; rt2 = rt + nwaves; }
+  };
+  u32x4 bufA[kLPL];
+  issue(bufA, rt_first, 0);
+#if QG_PREFETCH > 1
+  // A second step in flight while the first is decoded.
+  u32x4 bufB[kLPL];
+  int64_t rtn;
+  int segn;
+  next_step(rt_first, 0, rtn, segn);
+  issue(bufB, rtn, segn);
+#endif
 
   // With fused quantization, workgroup 0 of the plain problem (or of each
   // shared-expert entry, which together cover every token once) stores the
   // activation codes in the workspace.
   stage_activations<MT, DOTS, FUSEQ>(smem, p, U, mcnt, out_row,
-                                     FUSEQ && p.xq_out && blockIdx.x == 0 && (!p.tbl || shared));
+                                     FUSEQ && p.xq_out && blockIdx.x == 0 && (!p.tbl || shared), pre);
   __syncthreads();
 
   float acc[P][MT];
@@ -439,25 +518,21 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[a][t] = 0.0f;
 
-  int64_t rt = rt_first;
-  int seg = 0;
-  while (rt < g.nrowtiles) {
+  // One step: move its bytes from registers to the wave's LDS buffer, reuse
+  // the registers for step (rtq, segq), then decode and accumulate.
+  auto process = [&](u32x4(&buf)[kLPL], int64_t rt, int seg, int64_t rtq, int segq) __attribute__((always_inline)) {
     int64_t b0, b1;
     step_range(rt, seg, b0, b1);
     const int64_t a0 = b0 & ~(int64_t)15;
     {
       const int nch = (int)((((b1 + 15) & ~(int64_t)15) - a0) >> 4);
 #pragma unroll
-      for (int i = 0; i < kLoadsPerLane; ++i) {
+      for (int i = 0; i < kLPL; ++i) {
         const int c = lane + kWave * i;
         if (c < nch) *reinterpret_cast<u32x4*>(tile + 16 * c) = buf[i];
       }
     }
-    // Prefetch the next step of this wave.
-    int64_t rt2 = rt;
-    int seg2 = seg + 1;
-    if (seg2 == g.nseg) { seg2 = 0; rt2 = rt + nwaves; }
-    if (rt2 < g.nrowtiles) issue(rt2, seg2);
+    issue(buf, rtq, segq);
 
     // ---- decode this step from LDS and accumulate
     const int64_t r0 = rt * G;
@@ -524,9 +599,34 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
         }
       }
     }
+  };
+
+  int64_t rt = rt_first;
+  int seg = 0;
+#if QG_PREFETCH > 1
+  // bufA holds (rt, seg), bufB the step after it; each buffer is refilled
+  // with the step two ahead as soon as it has been copied to LDS.
+  while (rt < g.nrowtiles) {
+    int64_t rt3;
+    int seg3;
+    next_step(rtn, segn, rt3, seg3);
+    process(bufA, rt, seg, rt3, seg3);
+    rt = rtn; seg = segn; rtn = rt3; segn = seg3;
+    if (rt >= g.nrowtiles) break;
+    next_step(rtn, segn, rt3, seg3);
+    process(bufB, rt, seg, rt3, seg3);
+    rt = rtn; seg = segn; rtn = rt3; segn = seg3;
+  }
+#else
+  while (rt < g.nrowtiles) {
+    int64_t rt2;
+    int seg2;
+    next_step(rt, seg, rt2, seg2);
+    process(bufA, rt, seg, rt2, seg2);
     rt = rt2;
     seg = seg2;
   }
+#endif
 }
 
 // ------------------------------------------------------------- launchers --
@@ -590,11 +690,12 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom&
   g.lpr_log = 0;
   while ((1 << g.lpr_log) < g.LPR) ++g.lpr_log;
   int P = 1;
-  if (g.rb * g.RPP <= kTileCap) {
+  const int cap = tile_cap(fmt);
+  if (g.rb * g.RPP <= cap) {
     g.nseg = 1;
     g.SU = g.U;
     const int pm = dots ? 1 : max_passes(MT);
-    while (P * 2 <= pm && g.rb * g.RPP * P * 2 <= kTileCap) P *= 2;
+    while (P * 2 <= pm && g.rb * g.RPP * P * 2 <= cap) P *= 2;
     // Keep enough steps to spread the matrix over the whole chip.
     const int64_t want_waves = (int64_t)device_cus() * 8;
     while (P > 1 && (n + (int64_t)P * g.RPP - 1) / ((int64_t)P * g.RPP) < want_waves) P >>= 1;
@@ -602,7 +703,7 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom&
     // Long rows: one row per step, split into K-segments of whole
     // super-blocks that are a multiple of 64 units.
     const int64_t unit_bytes_x64 = (int64_t)64 * bb / upb;  // bytes of 64 units
-    int su = (int)(kTileCap / unit_bytes_x64) * 64;
+    int su = (int)(cap / unit_bytes_x64) * 64;
     if (su < 64) su = 64;
     g.SU = su;
     g.nseg = (g.U + su - 1) / su;
@@ -612,6 +713,9 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom&
   g.act_bytes = MT * act_token_bytes(g.U);
   const int64_t step_max = g.nseg == 1 ? G * g.rb : (int64_t)(g.SU / upb) * bb;
   g.tile_buf = (int)((step_max + 32 + 15) / 16 * 16 + 16);  // + alignment chunks + over-read
+  // A step's 16-byte chunks (two more for alignment) must fit the per-lane
+  // register buffer the kernel is compiled with.
+  if ((step_max + 15) / 16 + 2 > (int64_t)kWave * ((cap + 32 + 1023) / 1024)) return 0;
   return P;
 }
 
@@ -724,7 +828,7 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
     mt >>= 1;
     P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, a.g);
   }
-  if ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit)
+  if (P == 0 || (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit)
     return hipErrorInvalidValue;
   if (p.tbl && mt < kGroupTokens) return hipErrorInvalidValue;  // entries cannot be split
   if (mt >= p.m || p.tbl) return launch_any(fmt, a, mt, P, dots_epilogue, s);
