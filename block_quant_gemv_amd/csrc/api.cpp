@@ -393,10 +393,18 @@ int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x
   int rc;
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w_gateup);
-  p.xf = x;  // quantized in the gate|up kernel's prologue, codes stored in ws
-  p.xq_out = xq;
-  p.dx_out = dx;
-  p.sx_out = sx;
+  if (d.hidden <= kFusedQuantMaxK) {
+    p.xf = x;  // quantized in the gate|up kernel's prologue, codes stored in ws
+    p.xq_out = xq;
+    p.dx_out = dx;
+    p.sx_out = sx;
+  } else {
+    // Long rows: one quantizer launch is cheaper than every workgroup of the
+    // gate|up GEMV quantizing x again.
+    if ((rc = check_launch(launch_quant_q8(x, xq, dx, sx, (int64_t)m * d.hidden / 32, s), "quantize"))) return rc;
+    p.xq = xq;
+    p.dx = dx;
+  }
   p.xs = d.hidden;
   p.y = gu;
   p.ldy = 2 * d.inter;

@@ -60,6 +60,13 @@ hipError_t launch_quant_q8(const float* x, int8_t* xq, float* dx, int32_t* sx,
 // host). dots_epilogue selects the integer-store checking epilogue.
 hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStream_t s);
 
+// Single-token Q4_K GEMV that loads the 16-byte-aligned super-block fields
+// straight into registers (no LDS); applies when q4k_direct_ok(p): m == 1,
+// quantized activations given, no grouping, K a multiple of 2048 up to 8192.
+// dots selects the integer-store checking epilogue (p.dots, int32 [n, K/32]).
+bool q4k_direct_ok(const GemvProblem& p, bool dots);
+hipError_t launch_q4k_direct(const GemvProblem& p, bool dots, hipStream_t s);
+
 // Largest token count one GEMV launch handles.
 constexpr int kGemvMaxTokens = 16;
 // From this many tokens on, Q4_K and Q6_K GEMVs run on int8 MFMA (the VALU

@@ -1,0 +1,221 @@
+// Single-token GEMV over Q4_K super-blocks read straight into registers.
+//
+// A Q4_K super-block is 144 bytes, a multiple of 16, so every field a lane
+// needs -- the 16-byte header (d, dmin, the twelve bytes of 6-bit scales and
+// mins) and the 16 bytes of one 32-element sub-block's codes -- is an aligned
+// 128-bit load. Lane l of a wave owns sub-blocks l, l + 64, ... of every row
+// (K = 2048 * JU), so the eight lanes of one super-block read its header (the
+// same 16 bytes) and its eight code chunks (128 contiguous bytes): the wave
+// covers whole super-blocks, every byte once. The weights go from HBM to
+// registers with no LDS hop, and the quantized activations of the lane's
+// sub-blocks stay in registers for the whole kernel, so the main loop uses
+// no LDS at all. This is the K-quant in-register decode with scale and min
+// correction terms ("Why expert caching can't save dense models", xhh.club,
+// Q&A on computing GGUF blocks without FP16 expansion).
+//
+// Per (row, sub-block j of super-block b): D = sum xq * q over the 32 codes
+// (q in 0..15) and s = sum xq (the activation block sum), then
+// y += dx * (d * sc_j) * D - dx * (dmin * m_j) * s, accumulated in fp32 per
+// lane; the 64 lanes of a row are summed in a fixed order (DPP, readlane).
+#include "common.cuh"
+#include "internal.h"
+
+#ifndef QG_Q4K_DIRECT_PF
+#define QG_Q4K_DIRECT_PF 1   // row groups in flight per wave (1 or 2)
+#endif
+
+namespace qg {
+
+namespace {
+
+constexpr int kDirectWaves = 4;             // waves per workgroup (independent)
+constexpr int kBufDword3 = 0x00020000;      // raw buffer resource, gfx9 family
+constexpr int kNonTemporal = 2;             // weights are read once
+
+// 6-bit field starting at bit `sh` of the 64-bit value {hi:lo} (sh < 32).
+QG_DEV uint32_t field6(uint32_t hi, uint32_t lo, uint32_t sh) {
+  return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
+}
+
+// R rows per iteration; JU sub-blocks per lane per row. DOTS: store the
+// exact per-sub-block integer dots D (int32 [n, 64 JU]) instead of y.
+template <int JU, int R, bool DOTS>
+__global__ __launch_bounds__(kDirectWaves * 64) void q4k_direct_kernel(const uint8_t* __restrict__ W,
+                                                                     const int8_t* __restrict__ xq,
+                                                                     const float* __restrict__ dx,
+                                                                     float* __restrict__ y,
+                                                                     int32_t* __restrict__ dots, int64_t n,
+                                                                     int64_t rb) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * kDirectWaves + wid;
+  const int64_t nw = (int64_t)gridDim.x * kDirectWaves;
+  const int64_t ngroups = (n + R - 1) / R;
+
+  // Activations of this lane's sub-blocks u = lane + 64 j: codes, scale and
+  // code sum.
+  int xa[JU][8];
+  float xd[JU];
+  int xsum[JU];
+#pragma unroll
+  for (int j = 0; j < JU; ++j) {
+    const int u = lane + 64 * j;
+    const int4 lo = reinterpret_cast<const int4*>(xq)[2 * u];
+    const int4 hi = reinterpret_cast<const int4*>(xq)[2 * u + 1];
+    xa[j][0] = lo.x; xa[j][1] = lo.y; xa[j][2] = lo.z; xa[j][3] = lo.w;
+    xa[j][4] = hi.x; xa[j][5] = hi.y; xa[j][6] = hi.z; xa[j][7] = hi.w;
+    xd[j] = DOTS ? 0.0f : dx[u];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4(xa[j][i], 0x01010101, s);
+    xsum[j] = s;
+  }
+  // Sub-block g = lane % 8 of its super-block. Scale field sc_g sits at bit
+  // 6g of the 96-bit stream (header dwords 1..3), min m_g at bit 48 + 6g.
+  const int g = lane & 7;
+  const bool sc_low = g < 6;     // sc_g within dwords {1, 2}, else {2, 3}
+  const uint32_t sc_sh = sc_low ? 6 * g : 6 * g - 32;
+  const bool m_low = g < 3;      // m_g within dwords {2, 3}, else dword 3
+  const uint32_t m_sh = m_low ? 16 + 6 * g : 6 * g - 16;
+  uint32_t hoff[JU], qoff[JU];
+#pragma unroll
+  for (int j = 0; j < JU; ++j) {
+    const uint32_t b = (uint32_t)(lane >> 3) + 8u * j;  // super-block of sub-block lane + 64 j
+    hoff[j] = b * 144u;
+    qoff[j] = b * 144u + 16u + 16u * g;
+  }
+
+  // Loads of one row group through a buffer resource spanning exactly its
+  // rows: a group past the end reads zeros without touching memory.
+  auto load = [&](u32x4 (&h)[R][JU], u32x4 (&q)[R][JU], int64_t grp) __attribute__((always_inline)) {
+    const int64_t r0 = grp * R;
+    const int64_t rows = grp < ngroups ? ((n - r0) < R ? (n - r0) : R) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W + (rows > 0 ? r0 * rb : 0)), 0, (int)(rows * rb), kBufDword3);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < JU; ++j) {
+        h[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(hoff[j] + r * rb), 0, kNonTemporal);
+        q[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(qoff[j] + r * rb), 0, kNonTemporal);
+      }
+  };
+
+  auto consume = [&](const u32x4 (&h)[R][JU], const u32x4 (&q)[R][JU], int64_t grp) __attribute__((always_inline)) {
+    const int64_t r0 = grp * R;
+    float outv = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < JU; ++j) {
+        const u32x4 hh = h[r][j];
+        const u32x4 qq = q[r][j];
+        int D = 0;
+        D = dot4((int)(qq.x & 0x0F0F0F0Fu), xa[j][0], D);
+        D = dot4((int)((qq.x >> 4) & 0x0F0F0F0Fu), xa[j][4], D);
+        D = dot4((int)(qq.y & 0x0F0F0F0Fu), xa[j][1], D);
+        D = dot4((int)((qq.y >> 4) & 0x0F0F0F0Fu), xa[j][5], D);
+        D = dot4((int)(qq.z & 0x0F0F0F0Fu), xa[j][2], D);
+        D = dot4((int)((qq.z >> 4) & 0x0F0F0F0Fu), xa[j][6], D);
+        D = dot4((int)(qq.w & 0x0F0F0F0Fu), xa[j][3], D);
+        D = dot4((int)((qq.w >> 4) & 0x0F0F0F0Fu), xa[j][7], D);
+        if constexpr (DOTS) {
+          if (r0 + r < n) dots[(r0 + r) * (64 * JU) + lane + 64 * j] = D;
+          continue;
+        }
+        const float d = half_bits(hh.x & 0xffffu);
+        const float dmin = half_bits(hh.x >> 16);
+        const uint32_t sc = sc_low ? field6(hh.z, hh.y, sc_sh) : field6(hh.w, hh.z, sc_sh);
+        const uint32_t mn = m_low ? field6(hh.w, hh.z, m_sh) : field6(hh.w, hh.w, m_sh);
+        const float dsc = d * (float)sc;
+        const float dmm = dmin * (float)mn;
+        acc = fmaf(xd[j] * dsc, (float)D, acc);
+        acc = fmaf(-(xd[j] * dmm), (float)xsum[j], acc);
+      }
+      if constexpr (!DOTS) {
+        const float sum = group_sum(acc, 64);
+        if (lane == r) outv = sum;
+      }
+    }
+    if constexpr (!DOTS) {
+      const int64_t rows = (n - r0) < R ? (n - r0) : R;
+      if (lane < rows) y[r0 + lane] = outv;
+    }
+  };
+
+#if QG_Q4K_DIRECT_PF > 1
+  // Two row groups in flight per wave: A holds group grp, B the next one;
+  // each buffer is refilled with the group two ahead once consumed.
+  u32x4 hA[R][JU], qA[R][JU], hB[R][JU], qB[R][JU];
+  load(hA, qA, gw);
+  load(hB, qB, gw + nw);
+  for (int64_t grp = gw; grp < ngroups; grp += 2 * nw) {
+    consume(hA, qA, grp);
+    load(hA, qA, grp + 2 * nw);
+    if (grp + nw >= ngroups) break;
+    consume(hB, qB, grp + nw);
+    load(hB, qB, grp + 3 * nw);
+  }
+#else
+  // One row group in flight per wave; other resident waves cover the wait.
+  u32x4 hA[R][JU], qA[R][JU];
+  for (int64_t grp = gw; grp < ngroups; grp += nw) {
+    load(hA, qA, grp);
+    consume(hA, qA, grp);
+  }
+#endif
+}
+
+template <int JU, int R, bool DOTS>
+hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
+  auto kern = q4k_direct_kernel<JU, R, DOTS>;
+  static int per_cu = 0;  // resident workgroups per CU (occupancy query, once)
+  static int cus = 0;
+  if (!per_cu) {
+    int dev = 0, nb = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kDirectWaves * 64, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    cus = c;
+    per_cu = nb;
+  }
+  const int64_t ngroups = (p.n + R - 1) / R;
+  int64_t waves = (int64_t)cus * per_cu * kDirectWaves;
+  if (waves > ngroups) waves = ngroups;
+  const int64_t wgs = (waves + kDirectWaves - 1) / kDirectWaves;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kDirectWaves * 64), 0, s, p.w, p.xq, p.dx, p.y, p.dots,
+                     p.n, fmt_row_bytes(kQ4_K, p.k));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+
+bool q4k_direct_ok(const GemvProblem& p, bool dots) {
+  return p.m == 1 && !p.tbl && !p.xf && p.xq && (dots ? p.dots != nullptr : (p.dx && p.y)) &&
+         p.k % 2048 == 0 && p.k / 2048 >= 1 && p.k / 2048 <= 4 && p.n >= 1;
+}
+
+template <int R, bool DOTS>
+static hipError_t launch_ju(const GemvProblem& p, hipStream_t s) {
+  switch (p.k / 2048) {
+    case 1: return launch_t<1, R, DOTS>(p, s);
+    case 2: return launch_t<2, R, DOTS>(p, s);
+    case 3: return launch_t<3, R, DOTS>(p, s);
+    default: return launch_t<4, R, DOTS>(p, s);
+  }
+}
+
+hipError_t launch_q4k_direct(const GemvProblem& p, bool dots, hipStream_t s) {
+  if (!q4k_direct_ok(p, dots)) return hipErrorInvalidValue;
+  // Rows per wave iteration, measured on MI355X: four rows (more bytes in
+  // flight per wave) once there are enough rows to still give every CU
+  // several waves, one row for smaller matrices (more waves).
+  if (p.n >= 8192) return dots ? launch_ju<4, true>(p, s) : launch_ju<4, false>(p, s);
+  return dots ? launch_ju<1, true>(p, s) : launch_ju<1, false>(p, s);
+}
+
+}  // namespace qg

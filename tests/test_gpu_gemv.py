@@ -117,6 +117,10 @@ SMALL = [
     ("q4_k", 20, 256, 3),
     ("q4_k", 257, 768, 1),
     ("q4_k", 9, 12288, 16),
+    ("q4_k", 333, 2048, 1),       # register-direct single-token kernel: K = 2048 ... 8192
+    ("q4_k", 3, 6144, 1),
+    ("q4_k", 4097, 8192, 1),
+    ("q4_k", 8195, 4096, 1),      # four-row groups with a ragged last group
     ("q6_k", 4096, 12288, 1),     # FFN down shape
     ("q6_k", 20, 256, 1),
     ("q6_k", 257, 512, 4),
