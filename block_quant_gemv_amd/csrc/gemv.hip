@@ -682,7 +682,9 @@ static int device_cus() {
 static int max_passes(int mt) { return mt <= 2 ? 8 : mt == 4 ? 4 : mt == 8 ? 2 : 1; }
 
 // Choose the step geometry for a format, shape and token tile; returns P.
-static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom& g) {
+// nprob: problems sharing the launch (grouped mode), which together spread
+// over the chip.
+static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, int nprob, GemvGeom& g) {
   g = GemvGeom{};
   const int upb = (fmt == kQ4_K || fmt == kQ6_K) ? 8 : 1;
   const int bb = fmt_block_bytes(fmt);
@@ -701,7 +703,7 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, GemvGeom&
     while (P * 2 <= pm && g.rb * g.RPP * P * 2 <= cap) P *= 2;
     // Keep enough steps to spread the matrix over the whole chip.
     const int64_t want_waves = (int64_t)device_cus() * 8;
-    while (P > 1 && (n + (int64_t)P * g.RPP - 1) / ((int64_t)P * g.RPP) < want_waves) P >>= 1;
+    while (P > 1 && nprob * ((n + (int64_t)P * g.RPP - 1) / ((int64_t)P * g.RPP)) < want_waves) P >>= 1;
   } else {
     // Long rows: one row per step, split into K-segments of whole
     // super-blocks that are a multiple of 64 units.
@@ -762,7 +764,14 @@ static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
 #else
   const int64_t waves = a.g.nrowtiles < wmax ? a.g.nrowtiles : wmax;
 #endif
-  const int64_t wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
+  int64_t wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
+  // Grouped launches: never more workgroups than fit at once in all, so no
+  // problem waits for a second round.
+  if (a.p.nprob > 1) {
+    int64_t fit = cap_waves / kWavesPerWG / a.p.nprob;
+    if (fit < 1) fit = 1;
+    if (wgs > fit) wgs = fit;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs, (unsigned)a.p.nprob), dim3(kWavesPerWG * 64), lds, s, a);
   return hipGetLastError();
 }
@@ -828,11 +837,11 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
   int mt = token_tile(p.tbl ? kGroupTokens : p.m);
   GemvArgs a;
   a.p = p;
-  int P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, a.g);
+  int P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.tbl ? p.nprob : 1, a.g);
   // Keep the staged activations within LDS; fall back to smaller token tiles.
   while ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit && mt > 1) {
     mt >>= 1;
-    P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, a.g);
+    P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.tbl ? p.nprob : 1, a.g);
   }
   if (P == 0 || (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit)
     return hipErrorInvalidValue;

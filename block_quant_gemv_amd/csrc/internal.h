@@ -24,7 +24,15 @@ int64_t fmt_row_bytes(int fmt, int64_t k);  // -1 if k is not a multiple of the 
 // with count <= kGroupTokens: expert >= 0 uses matrix w + expert *
 // w_stride, expert == -1 the shared matrix w_shared. Token j of an entry
 // reads activation row rows[j] / act_div and writes output row rows[j].
-constexpr int kGroupTokens = 4;
+// Tokens per grouped entry. Measured on MI355X at 16 tokens x top-8 of 256
+// experts: one token per entry (the leanest kernel, 8 waves per SIMD) beats
+// grouping 2 or 4 tokens per entry, whose token slots cost registers and
+// occupancy, even though an expert chosen by several tokens is then read
+// once per token (often from the last-level cache).
+#ifndef QG_GROUP_TOKENS
+#define QG_GROUP_TOKENS 1
+#endif
+constexpr int kGroupTokens = QG_GROUP_TOKENS;
 
 struct GemvProblem {
   const uint8_t* w = nullptr;

@@ -11,13 +11,13 @@
 // ledger items ⑩ and ⑪).
 //
 // Launch sequence on one stream (no host synchronisation):
-//   router_kernel     logits[t, e] = W_r[e] . x[t] (fp32, unquantized x)
+//   router_kernel     logits[t, e] = W_r[e] . x[t] (fp32, unquantized x);
+//                     the same workgroups quantize x to Q8 blocks
 //   route_kernel      top-k per token (ties to the lower index), softmax over
 //                     the selected logits, then a table that groups the
 //                     (token, slot) pairs by expert so each selected expert's
 //                     weights are read once for all tokens that chose it
-//   grouped GEMV      gate|up of every used expert and of the shared expert,
-//                     quantizing x to Q8 blocks in its prologue
+//   grouped GEMV      gate|up of every used expert and of the shared expert
 //   swiglu_q8         h = silu(g) * u per (token, slot), re-quantized
 //   grouped GEMV      down of every used expert and of the shared expert
 //   combine_kernel    y[t] = sum_k w[t, k] out[t, k] (slot order) + shared
@@ -32,21 +32,27 @@ namespace qg {
 
 constexpr int kRouterMaxTok = 16;
 
-// One wave per expert row; each lane accumulates float4 chunks of the row
-// against the same chunks of every token, then the wave reduces.
+// One workgroup per expert row: its 256 threads split the row into float4
+// chunks, each thread accumulates its chunks against the same chunks of every
+// token, and the workgroup adds the partial sums in a fixed order (DPP within
+// a wave, then the four waves in order). The router's workgroups also
+// quantize x to Q8 blocks for the expert GEMVs (block b by workgroup b mod
+// grid, eight lanes per block as in the activation quantizer), so no
+// separate quantizer launch is needed.
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ wr,
                                                      const float* __restrict__ x,
-                                                     float* __restrict__ logits, int n_experts,
-                                                     int64_t hidden, int m) {
-  const int lane = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= n_experts) return;
+                                                     float* __restrict__ logits, int8_t* __restrict__ xq,
+                                                     float* __restrict__ dx, int32_t* __restrict__ sx,
+                                                     int n_experts, int64_t hidden, int m) {
+  __shared__ float part[4][kRouterMaxTok];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t e = blockIdx.x;
   const float4* wrow = reinterpret_cast<const float4*>(wr + e * hidden);
   const int64_t nch = hidden / 4;
   float acc[kRouterMaxTok];
 #pragma unroll
   for (int t = 0; t < kRouterMaxTok; ++t) acc[t] = 0.0f;
-  for (int64_t c = lane; c < nch; c += 64) {
+  for (int64_t c = threadIdx.x; c < nch; c += blockDim.x) {
     const float4 w = wrow[c];
 #pragma unroll
     for (int t = 0; t < kRouterMaxTok; ++t) {
@@ -59,21 +65,83 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
 #pragma unroll
   for (int t = 0; t < kRouterMaxTok; ++t) {
     if (t < m) {
-      const float s = wave_sum(acc[t]);
-      if (lane == 0) logits[(int64_t)t * n_experts + e] = s;
+      const float s = group_sum(acc[t], 64);
+      if (lane == 0) part[wid][t] = s;
     }
   }
+  // Q8 blocks of x: 32 blocks per workgroup pass, eight lanes each.
+  const int64_t nblocks = (int64_t)m * (hidden / 32);
+  for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks;
+       blk += (int64_t)gridDim.x * 32) {
+    // whole 8-lane groups are in or out together
+    const int part8 = threadIdx.x & 7;
+    const float4 v = reinterpret_cast<const float4*>(x)[blk * 8 + part8];
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = max8(a);
+    const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
+    int sum;
+    const uint32_t packed = q8_pack4(v, d, sum);
+    reinterpret_cast<uint32_t*>(xq)[blk * 8 + part8] = packed;
+    sum = sum4(sum);
+    sum += other_quad(sum);
+    if (part8 == 0) {
+      dx[blk] = d;
+      sx[blk] = sum;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < m) {
+    const int t = threadIdx.x;
+    logits[(int64_t)t * n_experts + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+  }
+}
+
+// Order-preserving 64-bit key of (logit, expert): larger logit first, then
+// the lower expert index.
+QG_DEV uint64_t route_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0x7fffffff - e);
+}
+
+template <int CTRL>
+QG_DEV uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+QG_DEV uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of the wave, in every lane (DPP within rows of 16, then the
+// four rows).
+QG_DEV uint64_t wave_max_key(uint64_t k) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(k); k = o > k ? o : k;    // quad_perm [1,0,3,2]
+  o = dpp_u64<0x4E>(k); k = o > k ? o : k;    // quad_perm [2,3,0,1]
+  o = dpp_u64<0x141>(k); k = o > k ? o : k;   // row_half_mirror
+  o = dpp_u64<0x140>(k); k = o > k ? o : k;   // row_mirror
+  const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
+  const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
 }
 
 // One workgroup of 64 * m threads. Wave t selects token t's top_k experts and
 // their softmax weights; then the (token, slot) pairs are grouped by expert
-// into the table read by the grouped GEMV (entries of at most kGroupTokens
-// tokens, so each expert's weights are read once per 4 tokens that chose it):
+// into the table read by the grouped GEMV, in entries of at most
+// kGroupTokens tokens (each entry reads its expert's weights once):
 //   tbl[0] = number of entries;
 //   tbl[1 + e * (2 + kGroupTokens) ...] = {expert, count, slot rows}
 // Routed entries come first, ordered by the expert's first occurrence
-// (token-major, slot order), tokens ascending; then ceil(m / 4) entries of
-// the shared expert (expert = -1) covering every token.
+// (token-major, slot order), tokens ascending; then ceil(m / kGroupTokens)
+// entries of the shared expert (expert = -1) covering every token.
+// NPL: logits held per lane (experts lane + 64 i), n_experts <= 64 * NPL.
+template <int NPL>
 __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restrict__ ids,
                              float* __restrict__ wts, int32_t* __restrict__ tbl, int n_experts,
                              int top_k, int m) {
@@ -81,39 +149,47 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
   const int tid = threadIdx.x;
   const int t = tid >> 6, lane = tid & 63;
   const int npairs = m * top_k;
-  int32_t* taken = sh;                              // [m * n_experts]
-  int32_t* s_ids = taken + m * n_experts;           // [npairs]
-  int32_t* first = s_ids + npairs;                  // [npairs] first occurrence index
-  int32_t* nchunk = first + npairs;                 // [npairs] chunks of a first occurrence, else 0
-  int32_t* rank = nchunk + npairs;                  // [npairs] earlier pairs with the same expert
-  int32_t* cnt = rank + npairs;                     // [npairs] total pairs of the expert (first only)
+  uint32_t* sel = reinterpret_cast<uint32_t*>(sh);  // [n_experts] tokens that chose the expert
+  int32_t* ebase = sh + n_experts;                  // [n_experts] first table entry of the expert
+  int32_t* s_ids = ebase + n_experts;               // [npairs] expert of pair p = token * top_k + slot
+  int32_t* nch = s_ids + npairs;                    // [npairs] entries of the expert at its first pair
+  int32_t* scan = nch + npairs;                     // [npairs] exclusive prefix sum of nch
+  int32_t* routed = scan + npairs;                  // [1] routed entries in all
 
-  for (int i = tid; i < m * n_experts; i += blockDim.x) taken[i] = 0;
+  for (int i = tid; i < n_experts; i += blockDim.x) sel[i] = 0u;
   __syncthreads();
 
   if (t < m) {
+    // This lane's logits, loaded once; selection works on registers.
     const float* lg = logits + (int64_t)t * n_experts;
-    int32_t* tk = taken + t * n_experts;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < n_experts ? lg[e] : 0.0f;
+    }
+    uint64_t taken = 0;  // bit i: expert lane + 64 i already selected (or absent)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i >= n_experts) taken |= 1ull << i;
     float my_v = -INFINITY;  // lane k keeps the k-th selection
     int my_i = 0;
     for (int k = 0; k < top_k; ++k) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int e = lane; e < n_experts; e += 64) {
-        const float v = lg[e];
-        // The first untaken expert always beats the sentinel, so a winner
-        // exists even for non-finite logits.
-        if (!tk[e] && (bi == 0x7fffffff || v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
-      }
+      uint64_t best = 0;  // below every real key
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+      for (int i = 0; i < NPL; ++i) {
+        const uint64_t key = route_key(v[i], lane + 64 * i);
+        if (!((taken >> i) & 1ull) && key > best) best = key;
       }
-      // Every lane now holds the same winner (largest logit, lowest index).
-      if (lane == 0) tk[bi] = 1;
-      if (lane == k) { my_v = bv; my_i = bi; }
+      best = wave_max_key(best);
+      const int bi = 0x7fffffff - (int)(uint32_t)best;
+      if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
+      if (lane == k) {
+        uint32_t b = (uint32_t)(best >> 32);
+        b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
+        my_v = __uint_as_float(b);
+        my_i = bi;
+      }
     }
     const float v0 = __shfl(my_v, 0, 64);
     const float ez = (lane < top_k) ? expf(my_v - v0) : 0.0f;
@@ -122,56 +198,75 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
       ids[t * top_k + lane] = my_i;
       wts[t * top_k + lane] = ez / den;
       s_ids[t * top_k + lane] = my_i;
+      atomicOr(&sel[my_i], 1u << t);  // a token selects an expert at most once
     }
   }
   __syncthreads();
 
+  // Rank of a pair among the expert's tokens (tokens ascending) and, at the
+  // expert's first pair, the number of table entries the expert needs.
   for (int p = tid; p < npairs; p += blockDim.x) {
-    const int e = s_ids[p];
-    int f = p, r = 0;
-    for (int q = 0; q < p; ++q) {
-      if (s_ids[q] == e) {
-        if (r == 0) f = q;
-        ++r;
-      }
-    }
-    first[p] = f;
-    rank[p] = r;
-    int c = 0;
-    if (f == p)
-      for (int q = p; q < npairs; ++q) c += (s_ids[q] == e);
-    cnt[p] = c;
-    nchunk[p] = (c + kGroupTokens - 1) / kGroupTokens;
+    const uint32_t sm = sel[s_ids[p]];
+    const int tt = p / top_k;
+    const int r = __popc(sm & ((1u << tt) - 1u));
+    nch[p] = r == 0 ? (__popc(sm) + kGroupTokens - 1) / kGroupTokens : 0;
   }
+  __syncthreads();
+  // Entries in order of the experts' first pairs: exclusive scan of nch by
+  // wave 0, four pairs per lane (npairs <= 256).
+  if (t == 0) {
+    int vals[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = 4 * lane + j;
+      vals[j] = idx < npairs ? nch[idx] : 0;
+      loc += vals[j];
+    }
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    int ex = inc - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = 4 * lane + j;
+      if (idx < npairs) scan[idx] = ex;
+      ex += vals[j];
+    }
+    if (lane == 63) routed[0] = inc;
+  }
+  __syncthreads();
+  for (int p = tid; p < npairs; p += blockDim.x)
+    if (nch[p] > 0) ebase[s_ids[p]] = scan[p];
   __syncthreads();
   const int tstride = 2 + kGroupTokens;
   for (int p = tid; p < npairs; p += blockDim.x) {
-    const int f = first[p];
-    int base = 0;
-    for (int q = 0; q < f; ++q) base += nchunk[q];
-    const int r = rank[p];
-    int32_t* ent = tbl + 1 + (int64_t)(base + r / kGroupTokens) * tstride;
+    const int e = s_ids[p];
+    const uint32_t sm = sel[e];
     const int tok = p / top_k, k = p - tok * top_k;
+    const int r = __popc(sm & ((1u << tok) - 1u));
+    int32_t* ent = tbl + 1 + (int64_t)(ebase[e] + r / kGroupTokens) * tstride;
     ent[2 + r % kGroupTokens] = tok * (top_k + 1) + k;
     if (r % kGroupTokens == 0) {
-      ent[0] = s_ids[p];
-      const int left = cnt[f] - r;
+      ent[0] = e;
+      const int left = __popc(sm) - r;
       ent[1] = left < kGroupTokens ? left : kGroupTokens;
     }
   }
   if (tid == 0) {
-    int routed = 0;
-    for (int q = 0; q < npairs; ++q) routed += nchunk[q];
+    const int nr = routed[0];
     const int nsh = (m + kGroupTokens - 1) / kGroupTokens;
     for (int c = 0; c < nsh; ++c) {
-      int32_t* ent = tbl + 1 + (int64_t)(routed + c) * tstride;
+      int32_t* ent = tbl + 1 + (int64_t)(nr + c) * tstride;
       const int t0 = c * kGroupTokens;
       const int n = (m - t0) < kGroupTokens ? (m - t0) : kGroupTokens;
       ent[0] = -1;
       ent[1] = n;
       for (int j = 0; j < n; ++j) ent[2 + j] = (t0 + j) * (top_k + 1) + top_k;
     }
-    tbl[0] = routed + nsh;
+    tbl[0] = nr + nsh;
   }
 }
 
@@ -195,21 +290,27 @@ int64_t moe_table_ints(int m, int top_k) { return 1 + moe_max_entries(m, top_k) 
 
 hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (c.m < 1 || c.m > kRouterMaxTok || c.top_k > 16) return hipErrorInvalidValue;
-  // 1. router
-  hipLaunchKernelGGL(router_kernel, dim3((unsigned)((c.n_experts + 3) / 4)), dim3(256), 0, s, c.router,
-                     c.x, c.logits, c.n_experts, c.hidden, c.m);
+  if (c.n_experts < 1 || c.n_experts > 4096 || c.hidden % 32) return hipErrorInvalidValue;
+  // 1. router logits, and x quantized to Q8 blocks
+  hipLaunchKernelGGL(router_kernel, dim3((unsigned)c.n_experts), dim3(256), 0, s, c.router, c.x, c.logits,
+                     c.xq, c.dx, c.sx, c.n_experts, c.hidden, c.m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 2. top-k, softmax and grouping
   const int npairs = c.m * c.top_k;
-  const size_t lds = ((size_t)c.m * c.n_experts + 6 * (size_t)npairs) * 4;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(64 * c.m), lds, s, c.logits, c.ids, c.wts, c.tbl,
-                     c.n_experts, c.top_k, c.m);
+  const size_t lds = (2 * (size_t)c.n_experts + 3 * (size_t)npairs + 1) * 4;
+  if (c.n_experts <= 256)
+    hipLaunchKernelGGL(route_kernel<4>, dim3(1), dim3(64 * c.m), lds, s, c.logits, c.ids, c.wts, c.tbl,
+                       c.n_experts, c.top_k, c.m);
+  else if (c.n_experts <= 1024)
+    hipLaunchKernelGGL(route_kernel<16>, dim3(1), dim3(64 * c.m), lds, s, c.logits, c.ids, c.wts, c.tbl,
+                       c.n_experts, c.top_k, c.m);
+  else
+    hipLaunchKernelGGL(route_kernel<64>, dim3(1), dim3(64 * c.m), lds, s, c.logits, c.ids, c.wts, c.tbl,
+                       c.n_experts, c.top_k, c.m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // 3. gate|up of the used experts and the shared expert; the kernel
-  // quantizes x in its prologue and the shared-expert workgroup 0 stores the
-  // codes in the workspace
+  // 3. gate|up of the used experts and the shared expert, on the codes the
+  // router kernel wrote
   const int slots = c.top_k + 1;
   const int maxprob = (int)moe_max_entries(c.m, c.top_k);
   GemvProblem g;
@@ -220,10 +321,8 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   g.tbl_stride = 2 + kGroupTokens;
   g.nprob = maxprob;
   g.act_div = slots;
-  g.xf = c.x;
-  g.xq_out = c.xq;
-  g.dx_out = c.dx;
-  g.sx_out = c.sx;
+  g.xq = c.xq;
+  g.dx = c.dx;
   g.xs = c.hidden;
   g.y = c.gu_out;
   g.ldy = 2 * c.inter;
@@ -238,10 +337,6 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
     return e;
   // 5. down of the used experts and the shared expert
   GemvProblem d = g;
-  d.xf = nullptr;
-  d.xq_out = nullptr;
-  d.dx_out = nullptr;
-  d.sx_out = nullptr;
   d.w = c.dn;
   d.w_stride = c.dn_stride;
   d.w_shared = c.dn_shared;

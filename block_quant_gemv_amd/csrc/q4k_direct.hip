@@ -20,6 +20,9 @@
 #include "common.cuh"
 #include "internal.h"
 
+#ifndef QG_DIRECT_WGS_PER_CU
+#define QG_DIRECT_WGS_PER_CU 0   // > 0: cap on resident workgroups per CU
+#endif
 #ifndef QG_Q4K_DIRECT_PF
 #define QG_Q4K_DIRECT_PF 1   // row groups in flight per wave (1 or 2)
 #endif
@@ -180,7 +183,7 @@ hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kDirectWaves * 64, 0) != hipSuccess || nb < 1)
       nb = 1;
     cus = c;
-    per_cu = nb;
+    per_cu = QG_DIRECT_WGS_PER_CU > 0 && QG_DIRECT_WGS_PER_CU < nb ? QG_DIRECT_WGS_PER_CU : nb;
   }
   const int64_t ngroups = (p.n + R - 1) / R;
   int64_t waves = (int64_t)cus * per_cu * kDirectWaves;
