@@ -64,7 +64,7 @@ _lib.qgemv_status_string.argtypes = [_i32]
 _lib.qgemv_status_string.restype = ctypes.c_char_p
 _lib.qgemv_last_error.restype = ctypes.c_char_p
 _lib.qgemv_debug_quantize.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
-_lib.qgemv_debug_block_dots.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp]
+_lib.qgemv_debug_block_dots.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_size_t, _vp]
 for _f in ("qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
@@ -223,8 +223,10 @@ class GEMV(_Plan):
         g = 16 if self.fmt == FORMATS["q6_k"] else 32
         dots = torch.empty((m, self.n, self.k // g), dtype=torch.int32, device=xq.device)
         wp = self._check_w(w, 0, "w")
+        ws = self.workspace(m, device=xq.device)
         _check(_lib.qgemv_debug_block_dots(self._h, wp, _dev(xq, torch.int8, "xq"),
-                                           _dev(dots, torch.int32, "dots"), m, _stream(stream)),
+                                           _dev(dots, torch.int32, "dots"), m, ws.data_ptr(), ws.numel(),
+                                           _stream(stream)),
                "qgemv_debug_block_dots")
         return dots
 

@@ -26,6 +26,9 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"--offload-arch={ARCH}"]
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras. mfma.hip: matrix-core results in ordinary VGPRs (gfx950
+# has one register file), so the fp32 epilogue reads them without copies.
+EXTRA = {"mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():
@@ -42,6 +45,7 @@ def _compile(src: str) -> str:
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
         cmd += DEVICE_ONLY
+    cmd += EXTRA.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

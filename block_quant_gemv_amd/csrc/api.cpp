@@ -77,7 +77,14 @@ Layout layout_of(const qgemv_plan* h, int m) {
     L.add("xq", (size_t)m * d.k);
     L.add("dx", (size_t)m * (d.k / 32) * 4);
     L.add("sx", (size_t)m * (d.k / 32) * 4);
-    if (m >= kMfmaMinTokens && mfma_supported(d.fmt)) L.add("partials", gemm32_partials_bytes(d.n, d.k));
+    if (m >= kMfmaMinTokens) {
+      // token-tiled codes for the batched matrix-core path, written by the
+      // quantizer for every plan so that plans with the same k share a
+      // quantized workspace
+      L.add("xqt", gemm32_tiled_act_bytes(d.k));
+      const size_t part = mfma_supported(d.fmt) ? gemm32_partials_bytes(d.n, d.k) : 0;
+      if (part) L.add("partials", part);
+    }
   } else if (d.kind == QKIND_FFN) {
     L.add("xq", (size_t)m * d.hidden);
     L.add("dx", (size_t)m * (d.hidden / 32) * 4);
@@ -272,8 +279,10 @@ int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const 
 
 int gemv_quantize(qgemv_t h, const float* x, int m, void* ws, hipStream_t s) {
   const Layout L = layout_of(h, m);
+  int8_t* xqt = m >= kMfmaMinTokens ? region<int8_t>(ws, L, "xqt") : nullptr;
   return check_launch(launch_quant_q8(x, region<int8_t>(ws, L, "xq"), region<float>(ws, L, "dx"),
-                                      region<int32_t>(ws, L, "sx"), (int64_t)m * (h->d.k / 32), s),
+                                      region<int32_t>(ws, L, "sx"), (int64_t)m * (h->d.k / 32), s, xqt,
+                                      (int)(h->d.k / 32)),
                       "quantize");
 }
 
@@ -284,10 +293,12 @@ int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* w
   const int8_t* xq = region<int8_t>(wsm, L, "xq");
   const float* dx = region<float>(wsm, L, "dx");
   const int32_t* sx = region<int32_t>(wsm, L, "sx");
-  if (m >= kMfmaMinTokens && mfma_supported(d.fmt))
-    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y,
-                                      region<float>(wsm, L, "partials"), d.n, d.k, m, s),
+  if (m >= kMfmaMinTokens && mfma_supported(d.fmt)) {
+    float* part = gemm32_partials_bytes(d.n, d.k) ? region<float>(wsm, L, "partials") : nullptr;
+    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), region<int8_t>(wsm, L, "xqt"), dx,
+                                      sx, y, part, d.n, d.k, m, s),
                         "gemm32");
+  }
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w);
   p.xq = xq;
@@ -495,18 +506,27 @@ int qgemv_debug_quantize(const float* x, int8_t* xq, float* dx, int32_t* sx, int
                       "quantize");
 }
 
-int qgemv_debug_block_dots(qgemv_t h, const void* w, const int8_t* xq, int32_t* dots, int m, void* stream) {
+int qgemv_debug_block_dots(qgemv_t h, const void* w, const int8_t* xq, int32_t* dots, int m, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "qgemv_debug_block_dots: not a GEMV plan");
   if (!w || !xq || !dots) return fail(QGEMV_EINVAL, "qgemv_debug_block_dots: null pointer");
   if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(dots, 4))
     return fail(QGEMV_EALIGN, "qgemv_debug_block_dots: w and xq need 16-byte alignment");
   const qgemv_desc& d = h->d;
   if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qgemv_debug_block_dots: m=%d not in 1..%d", m, d.max_m);
-  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots: launch failure injected");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m >= kMfmaMinTokens && mfma_supported(d.fmt))
-    return check_launch(launch_gemm32_dots(d.fmt, static_cast<const uint8_t*>(w), xq, dots, d.n, d.k, m, s),
+  if (m >= kMfmaMinTokens && mfma_supported(d.fmt)) {
+    // The batched path reads the token-tiled codes from the workspace.
+    int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_debug_block_dots");
+    if (rc) return rc;
+    if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots: launch failure injected");
+    const Layout L = layout_of(h, m);
+    int8_t* xqt = region<int8_t>(ws, L, "xqt");
+    if ((rc = check_launch(launch_tile_codes(xq, xqt, m, (int)(d.k / 32), s), "tile codes"))) return rc;
+    return check_launch(launch_gemm32_dots(d.fmt, static_cast<const uint8_t*>(w), xqt, dots, d.n, d.k, m, s),
                         "gemm32 dots");
+  }
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots: launch failure injected");
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w);
   p.xq = xq;

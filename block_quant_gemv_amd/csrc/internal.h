@@ -61,12 +61,18 @@ struct GemvProblem {
   int act_div = 1;
 };
 
+// Q8 quantizer over nblocks 32-element blocks (token-major). With xqt set it
+// also writes the codes as [block][token][32] for at most 32 tokens of
+// kblocks blocks each.
 hipError_t launch_quant_q8(const float* x, int8_t* xq, float* dx, int32_t* sx,
-                           int64_t nblocks, hipStream_t s);
+                           int64_t nblocks, hipStream_t s, int8_t* xqt = nullptr, int kblocks = 0);
 
 // Row GEMV over packed blocks for m <= 16 tokens (chunks larger m on the
 // host). dots_epilogue selects the integer-store checking epilogue.
 hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStream_t s);
+
+// Codes xq [m, k] (m <= 32) copied to the token-tiled layout [block][token][32].
+hipError_t launch_tile_codes(const int8_t* xq, int8_t* xqt, int m, int kblocks, hipStream_t s);
 
 // Single-token Q4_K GEMV that loads the 16-byte-aligned super-block fields
 // straight into registers (no LDS); applies when q4k_direct_ok(p): m == 1,

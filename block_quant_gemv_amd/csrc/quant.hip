@@ -13,10 +13,14 @@
 
 namespace qg {
 
+// xqt (optional): a second copy of the codes for the batched matrix-core
+// path, laid out [block][token][32] for up to 32 tokens, so that the 32
+// tokens' codes of one block are 1 KB of contiguous memory.
 __global__ __launch_bounds__(256) void quant_q8_kernel(const float* __restrict__ x,
                                                        int8_t* __restrict__ xq,
                                                        float* __restrict__ dx,
                                                        int32_t* __restrict__ sx,
+                                                       int8_t* __restrict__ xqt, int kblocks,
                                                        int64_t nblocks) {
   const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk = gt >> 3;
@@ -31,6 +35,10 @@ __global__ __launch_bounds__(256) void quant_q8_kernel(const float* __restrict__
   int s;
   const uint32_t packed = q8_pack4(v, d, s);
   reinterpret_cast<uint32_t*>(xq)[blk * 8 + part] = packed;
+  if (xqt) {
+    const int64_t t = blk / kblocks, b = blk - t * kblocks;
+    reinterpret_cast<uint32_t*>(xqt)[(b * 32 + t) * 8 + part] = packed;
+  }
   s = sum4(s);
   s += other_quad(s);
   if (part == 0) {
@@ -40,12 +48,33 @@ __global__ __launch_bounds__(256) void quant_q8_kernel(const float* __restrict__
 }
 
 hipError_t launch_quant_q8(const float* x, int8_t* xq, float* dx, int32_t* sx,
-                           int64_t nblocks, hipStream_t s) {
+                           int64_t nblocks, hipStream_t s, int8_t* xqt, int kblocks) {
   if (nblocks <= 0) return hipSuccess;
+  if (xqt && (kblocks <= 0 || nblocks / kblocks > 32 || nblocks % kblocks)) return hipErrorInvalidValue;
   const int64_t threads = nblocks * 8;
   const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(quant_q8_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, xq, dx, sx,
+  hipLaunchKernelGGL(quant_q8_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, xq, dx, sx, xqt, kblocks,
                      nblocks);
+  return hipGetLastError();
+}
+
+// Copy of already-quantized codes xq [m, k] into the token-tiled layout
+// [block][token][32] (m <= 32), for the checking export of the batched path.
+__global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t* __restrict__ xq, int8_t* __restrict__ xqt,
+                                                         int m, int kblocks) {
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte half-block each
+  if (gt >= (int64_t)m * kblocks * 2) return;
+  const int64_t blk = gt >> 1;
+  const int64_t t = blk / kblocks, b = blk - t * kblocks;
+  const int half = (int)(gt & 1);
+  reinterpret_cast<int4*>(xqt)[(b * 32 + t) * 2 + half] = reinterpret_cast<const int4*>(xq)[blk * 2 + half];
+}
+
+hipError_t launch_tile_codes(const int8_t* xq, int8_t* xqt, int m, int kblocks, hipStream_t s) {
+  if (m < 1 || m > 32 || kblocks < 1) return hipErrorInvalidValue;
+  const int64_t threads = (int64_t)m * kblocks * 2;
+  hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, xq, xqt, m,
+                     kblocks);
   return hipGetLastError();
 }
 

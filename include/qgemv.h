@@ -144,7 +144,11 @@ int qgemv_workspace_size(qgemv_t h, int m, size_t *bytes);
  * for a given layout version). Returns QGEMV_EINVAL for a name the plan does
  * not have. Names: "xq" (int8 [m, K]), "dx" (fp32 [m, K/32]), "sx" (int32
  * [m, K/32]); FFN adds "gu" (fp32 [m, 2*inter]), "h" (fp32 [m, inter]), "hq",
- * "hd", "hs"; MoE adds "logits" (fp32 [m, n_experts]), "ids" (int32
+ * "hd", "hs"; a GEMV workspace for m >= 9 adds "xqt" (the codes again,
+ * int8 [k/32][32][32]: block, token, element -- the layout of the batched
+ * matrix-core path, written by the quantizer) and, for Q4_K and Q6_K plans
+ * whose K is split across workgroups, "partials" (fp32); MoE adds "logits"
+ * (fp32 [m, n_experts]), "ids" (int32
  * [m, top_k]), "wts" (fp32 [m, top_k]), "gu" (fp32 [m, top_k + 1, 2*inter]),
  * "h", "hq", "hd", "hs" (per token and slot, shared expert last). */
 int qgemv_workspace_offset(qgemv_t h, int m, const char *name, size_t *offset);
@@ -219,10 +223,14 @@ int qgemv_debug_quantize(const float *x, int8_t *xq, float *dx, int32_t *sx,
  * quantized activations xq int8 [m, k]: dots int32 [m, n, k/32] with
  * Q4_0: sum xq*(q-8); Q8_0: sum xq*q; IQ4_NL: sum xq*cb[q]; Q4_K: sum xq*q
  * per 32-element sub-block; and for Q6_K dots int32 [m, n, k/16] =
- * sum xq*(q-32) per 16-element sub-block. Runs the production GEMV kernel's
- * staging and decode with an integer-store epilogue. */
+ * sum xq*(q-32) per 16-element sub-block. Runs the production kernel the
+ * plan uses for m tokens (staging and decode) with an integer-store
+ * epilogue. ws/ws_bytes: a workspace of qgemv_workspace_size(h, m) bytes,
+ * used (its "xqt" region) only when m >= 9 and the format is Q4_K or Q6_K;
+ * may be NULL/0 otherwise. */
 int qgemv_debug_block_dots(qgemv_t h, const void *w, const int8_t *xq,
-                           int32_t *dots, int m, void *stream);
+                           int32_t *dots, int m, void *ws, size_t ws_bytes,
+                           void *stream);
 
 #ifdef __cplusplus
 }
