@@ -36,7 +36,7 @@ namespace qg {
 #define QG_TILE_CAP 0     // > 0: one step-size cap for every format (tuning)
 #endif
 #ifndef QG_WGS_PER_CU
-#define QG_WGS_PER_CU 0   // 0: as many workgroups as fit (occupancy query)
+#define QG_WGS_PER_CU 5   // cap on resident workgroups per CU for one matrix (measured on Q8_0)
 #endif
 
 #ifndef QG_BALANCE
@@ -747,10 +747,13 @@ static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   if (!per_cu) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kWavesPerWG * 64, lds) != hipSuccess || nb < 1) nb = 1;
-    per_cu = QG_WGS_PER_CU > 0 && QG_WGS_PER_CU < nb ? QG_WGS_PER_CU : nb;
+    per_cu = nb;
     for (int i = 0; i < 8; ++i)
       if (cached_nb[i] == 0) { cached_lds[i] = lds; cached_nb[i] = per_cu; break; }
   }
+  // A single matrix streams best with fewer resident workgroups than fit;
+  // grouped launches (many small problems) use all of them.
+  if (a.p.nprob == 1 && QG_WGS_PER_CU > 0 && QG_WGS_PER_CU < per_cu) per_cu = QG_WGS_PER_CU;
   // Waves available to each problem, then the fewest waves that still give
   // every wave the same number of row tiles (ceil), so no wave runs a
   // lone extra step at the end.

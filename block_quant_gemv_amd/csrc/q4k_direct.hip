@@ -21,7 +21,10 @@
 #include "internal.h"
 
 #ifndef QG_DIRECT_WGS_PER_CU
-#define QG_DIRECT_WGS_PER_CU 0   // > 0: cap on resident workgroups per CU
+#define QG_DIRECT_WGS_PER_CU 3   // cap on resident workgroups per CU (measured: 3 beats 6)
+#endif
+#ifndef QG_Q4K_RBIG
+#define QG_Q4K_RBIG 4            // rows per wave iteration for large matrices
 #endif
 #ifndef QG_Q4K_DIRECT_PF
 #define QG_Q4K_DIRECT_PF 1   // row groups in flight per wave (1 or 2)
@@ -217,7 +220,7 @@ hipError_t launch_q4k_direct(const GemvProblem& p, bool dots, hipStream_t s) {
   // Rows per wave iteration, measured on MI355X: four rows (more bytes in
   // flight per wave) once there are enough rows to still give every CU
   // several waves, one row for smaller matrices (more waves).
-  if (p.n >= 8192) return dots ? launch_ju<4, true>(p, s) : launch_ju<4, false>(p, s);
+  if (p.n >= 8192) return dots ? launch_ju<QG_Q4K_RBIG, true>(p, s) : launch_ju<QG_Q4K_RBIG, false>(p, s);
   return dots ? launch_ju<1, true>(p, s) : launch_ju<1, false>(p, s);
 }
 
