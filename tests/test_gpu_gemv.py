@@ -84,13 +84,14 @@ def test_quantizer_near_ties_bit_exact():
     assert np.array_equal(host(sx), rs)
 
 
-@pytest.mark.parametrize("fmt", ["q8_0", "q6_k"])
-def test_fused_quantize_writes_workspace_codes(fmt):
-    # qgemv_run quantizes inside the GEMV kernel; the codes it leaves in the
-    # workspace must equal the standalone rule bit for bit.
-    x = _near_tie_blocks()[:, :2048]
-    k = x.shape[1]
-    n = 64
+@pytest.mark.parametrize("fmt,k,n", [("q8_0", 2048, 64), ("q6_k", 2048, 64), ("q8_0", 4096, 4096),
+                                     ("q4_k", 4096, 4096), ("q6_k", 12288, 1024)])
+def test_fused_quantize_writes_workspace_codes(fmt, k, n):
+    # qgemv_run quantizes x (inside the GEMV kernel for short rows, in a
+    # launch of its own for long ones); the codes it leaves in the workspace
+    # must equal the standalone rule bit for bit.
+    ties = _near_tie_blocks()
+    x = np.concatenate([ties, synth.activations(3, 1, max(0, k - ties.shape[1]))], axis=1)[:, :k]
     w = synth.weights(fmt, n, k, seed=2)
     g = qg.GEMV(fmt, n, k)
     ws = g.workspace(1)
@@ -128,6 +129,13 @@ SMALL = [
     ("iq4_nl", 4096, 4096, 1),
     ("iq4_nl", 257, 288, 1),
     ("iq4_nl", 20, 32, 8),
+    # K > 2048 with several tokens, token chunks and tiny grids
+    ("q8_0", 2048, 4096, 4),
+    ("iq4_nl", 1500, 6144, 3),
+    ("q6_k", 1024, 12288, 8),
+    ("q8_0", 1000, 4096, 16),
+    ("q4_0", 700, 8192, 2),
+    ("q8_0", 8, 4096, 1),
 ]
 
 
@@ -183,6 +191,61 @@ def test_gemv_full_size_sampled_rows(fmt, n, k):
     assert np.all(np.abs(y[0, rows] - ref[0]) <= 1e-4 * (np.abs(ref[0]) + np.abs(ref[0]).mean()))
 
 
+def test_repeated_calls_shared_workspace():
+    # Plans with different kernels and grids take turns on one workspace;
+    # every call must see its own codes.
+    k = 4096
+    cases = [("q8_0", 4096), ("q4_k", 8195), ("iq4_nl", 300), ("q8_0", 8)]
+    cb = _codebook()
+    plans, weights = [], []
+    for i, (fmt, n) in enumerate(cases):
+        plans.append(qg.GEMV(fmt, n, k, codebook=cb if fmt == "iq4_nl" else None))
+        weights.append(synth.weights(fmt, n, k, seed=40 + i))
+    wsz = max(p.workspace_size(1) for p in plans)
+    assert all(p.workspace_size(1) == wsz for p in plans)
+    ws = torch.zeros(wsz, dtype=torch.uint8, device="cuda")
+    wds = [dev(w) for w in weights]
+    for it in range(2):
+        for i, ((fmt, n), g) in enumerate(zip(cases, plans)):
+            say(f"shared workspace round {it} {fmt} n={n}")
+            x = synth.activations(600 + 10 * it + i, 1, k)
+            y = host(g.run(wds[i], dev(x), ws=ws))
+            torch.cuda.synchronize()
+            xq, dx, sx = quantize_q8(x)
+            assert np.array_equal(host(g.ws_view(ws, 1, "xq", torch.int8, k)), xq[0])
+            assert np.array_equal(host(g.ws_view(ws, 1, "sx", torch.int32, k // 32)), sx[0])
+            rows = np.unique(np.linspace(0, n - 1, min(n, 600)).astype(np.int64))
+            ref = og.gemv_rows(fmt, weights[i], n, k, rows, xq, dx, cb if fmt == "iq4_nl" else None)
+            assert normwise(y[:, rows], ref) <= TOL
+
+
+def test_graph_replays_match_eager():
+    # Captured once, replayed with new inputs, with eager calls on the same
+    # workspace in between: every replay matches the eager result bit for bit.
+    fmt, n, k = "q8_0", 4096, 4096
+    w = dev(synth.weights(fmt, n, k, seed=50))
+    g = qg.GEMV(fmt, n, k)
+    ws = g.workspace(1)
+    xs = [dev(synth.activations(700 + i, 1, k)) for i in range(3)]
+    eager = [g.run(w, x, ws=ws).clone() for x in xs]
+    x_in = xs[0].clone()
+    y_out = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    g.run(w, x_in, y=y_out, ws=ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        g.run(w, x_in, y=y_out, ws=ws)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            x_in.copy_(xs[i])
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_out, eager[i]), f"replay {rep} input {i}"
+            other = g.run(w, xs[(i + 1) % 3], ws=ws)  # eager call between replays
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager[(i + 1) % 3])
+
+
 def test_gemv_deterministic_and_workspace_guard():
     fmt, n, k = "q4_k", 4096, 4096
     w = dev(synth.weights(fmt, n, k, seed=3))
@@ -190,6 +253,7 @@ def test_gemv_deterministic_and_workspace_guard():
     g = qg.GEMV(fmt, n, k, max_m=2)
     wsz = g.workspace_size(2)
     full, ws = guarded(torch, wsz, torch.uint8, pad=4096)
+    ws.zero_()  # a workspace starts zero-filled
     y1 = g.run(w, x, ws=ws).clone()
     y2 = g.run(w, x, ws=ws).clone()
     torch.cuda.synchronize()
