@@ -14,7 +14,8 @@ precision:
 * `quant.quantize_q8`: the on-device activation quantizer (32-element int8
   blocks with an fp32 scale), whose decisions are taken in fp32 as the method
   states them.
-* `formats`: the five block layouts, byte-level decode and encode.
+* `formats`: the seven block layouts (five from the decode workloads, plus
+  Q5_K and IQ4_XS), byte-level decode and encode.
 * `gemv`: the GEMV y = W_hat . x_hat in two independent forms -- the
   dequantize-then-accumulate form (fp64 matmul of decoded weights) and the
   integer block-dot form -- plus the exact per-block integer dot products.

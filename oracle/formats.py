@@ -1,4 +1,4 @@
-"""The five block formats: byte layout, decode and encode (oracle side).
+"""The seven block formats: byte layout, decode and encode (oracle side).
 
 Value formulas are those of the decode-GEMV workloads:
   Q4_0    value = d * (q - 8),          q in 0..15, 32-element blocks
@@ -8,6 +8,15 @@ Value formulas are those of the decode-GEMV workloads:
           super-blocks of eight 32-element sub-blocks j with 6-bit sc_j, m_j
   Q6_K    value = d * sc_j * (q - 32),  q in 0..63, 256-element super-blocks
           of sixteen 16-element sub-blocks j with int8 sc_j
+  Q5_K    value = d * sc_j * q - dmin * m_j, q in 0..31 (Q4_K with a fifth
+          code bit), 256-element super-blocks
+  IQ4_XS  value = d * (ls_j - 32) * cb[q], q in 0..15 indexing the IQ4_NL
+          codebook, 256-element super-blocks of eight 32-element sub-blocks
+          with 6-bit unsigned sub-scales ls_j
+The last two are the formats whose single-matrix bandwidth the pages report
+("Why expert caching can't save dense models", xhh.club, summary of the
+measurements: IQ4_XS, Q5_K and Q6_K matrices); the pages name them but give
+no field layout, so theirs below is this library's own reading.
 The method reads these blocks in place, with the correction terms of the
 K-quant super-blocks and a small codebook for the non-linear 4-bit format
 ("Why expert caching can't save dense models", xhh.club, Q&A on computing
@@ -30,13 +39,26 @@ The pages do not give the byte order inside a block. The reading used here
       i = 0..31): low 4 bits from ql[16g + (i mod 16)] (low nibble if i < 16,
       else high nibble); high 2 bits are bits 2*(i div 8) and 2*(i div 8)+1 of
       qh[8g + (i mod 8)]; q = low | high << 4; sub-block j = e div 16.
+  Q5_K (176 B): bytes 0-1 d, 2-3 dmin, 4..15 scales[12] as in Q4_K;
+      bytes 16..47 = qh[32]; bytes 48..175 = qs[128] with Q4_K's sub-block
+      and nibble order for the low 4 bits. The fifth bit of element
+      e = 32j + i (i = 0..31) is bit (i div 4) of qh[4j + (i mod 4)], i.e.
+      sub-block j's 32 fifth bits form the little-endian word qh[4j..4j+3]
+      with element i at bit 8 (i mod 4) + (i div 4); q = low | fifth << 4.
+  IQ4_XS (136 B): bytes 0-1 d; bytes 2-3 scales_h (uint16); bytes 4..7
+      scales_l[4]; bytes 8..135 qs[128] with Q4_K's sub-block and nibble
+      order. Sub-scale ls_j (0..63) = low 4 bits from scales_l[j div 2]
+      (low nibble for even j) | bits 2j, 2j+1 of scales_h as bits 4, 5.
 """
 from __future__ import annotations
 
 import numpy as np
 
-BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "iq4_nl": 32, "q4_k": 256, "q6_k": 256}
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210}
+BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "iq4_nl": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256,
+               "iq4_xs": 256}
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176,
+               "iq4_xs": 136}
+CODEBOOK_FORMATS = ("iq4_nl", "iq4_xs")
 FORMATS = tuple(BLOCK_BYTES)
 
 
@@ -78,22 +100,36 @@ def decode(fmt, raw, n, k, codebook=None):
     Shapes: nb = blocks per row.
       q4_0 / iq4_nl: d[n, nb], q[n, nb, 32]
       q8_0:          d[n, nb], q[n, nb, 32]
-      q4_k:          d[n, nb], dmin[n, nb], sc[n, nb, 8], m[n, nb, 8], q[n, nb, 256]
+      q4_k / q5_k:   d[n, nb], dmin[n, nb], sc[n, nb, 8], m[n, nb, 8], q[n, nb, 256]
       q6_k:          d[n, nb], sc[n, nb, 16], q[n, nb, 256]
+      iq4_xs:        d[n, nb], ls[n, nb, 8], q[n, nb, 256]
     """
     b = _blocks(fmt, raw, n, k)
     if fmt in ("q4_0", "iq4_nl"):
         return {"d": _fp16(b, 0), "q": _nibbles32(b[..., 2:18])}
     if fmt == "q8_0":
         return {"d": _fp16(b, 0), "q": b[..., 2:34].view(np.int8).astype(np.int64)}
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         bits = np.unpackbits(b[..., 4:16], axis=-1, bitorder="little")      # [.., 96]
         fields = (bits.reshape(*bits.shape[:-1], 16, 6).astype(np.int64)
                   * (1 << np.arange(6))).sum(-1)                             # [.., 16]
-        qs = b[..., 16:144].reshape(n, -1, 8, 16)
-        q = _nibbles32(qs).reshape(n, -1, 256)
+        q0 = 16 if fmt == "q4_k" else 48
+        qs = b[..., q0:q0 + 128].reshape(n, -1, 8, 16)
+        q = _nibbles32(qs)                                                   # [n, nb, 8, 32]
+        if fmt == "q5_k":
+            qh = b[..., 16:48].reshape(n, -1, 8, 4).astype(np.int64)         # [n, nb, 8, 4]
+            i = np.arange(32)
+            fifth = (qh[..., i % 4] >> (i // 4)) & 1                         # [n, nb, 8, 32]
+            q = q | (fifth << 4)
         return {"d": _fp16(b, 0), "dmin": _fp16(b, 2), "sc": fields[..., :8],
-                "m": fields[..., 8:], "q": q}
+                "m": fields[..., 8:], "q": q.reshape(n, -1, 256)}
+    if fmt == "iq4_xs":
+        sh = b[..., 2:4].copy().view("<u2")[..., 0].astype(np.int64)        # [n, nb]
+        sl = b[..., 4:8].astype(np.int64)                                    # [n, nb, 4]
+        j = np.arange(8)
+        ls = ((sl[..., j // 2] >> (4 * (j % 2))) & 0xF) | (((sh[..., None] >> (2 * j)) & 3) << 4)
+        q = _nibbles32(b[..., 8:136].reshape(n, -1, 8, 16)).reshape(n, -1, 256)
+        return {"d": _fp16(b, 0), "ls": ls, "q": q}
     if fmt == "q6_k":
         sc = b[..., 2:18].view(np.int8).astype(np.int64)
         ql = b[..., 18:146].astype(np.int64)
@@ -119,10 +155,14 @@ def values(fmt, raw, n, k, codebook=None):
     elif fmt == "iq4_nl":
         cb = np.asarray(codebook, np.int64)
         v = f["d"][..., None] * cb[f["q"]]
-    elif fmt == "q4_k":
+    elif fmt in ("q4_k", "q5_k"):
         q = f["q"].reshape(n, -1, 8, 32)
         v = (f["d"][..., None, None] * f["sc"][..., None] * q
              - f["dmin"][..., None, None] * f["m"][..., None])
+    elif fmt == "iq4_xs":
+        cb = np.asarray(codebook, np.int64)
+        q = f["q"].reshape(n, -1, 8, 32)
+        v = f["d"][..., None, None] * (f["ls"][..., None] - 32) * cb[q]
     elif fmt == "q6_k":
         q = f["q"].reshape(n, -1, 16, 16)
         v = f["d"][..., None, None] * f["sc"][..., None] * (q - 32)
@@ -147,14 +187,32 @@ def encode(fmt, fields):
         out[..., 2:18] = _pack_nibbles32(q)
     elif fmt == "q8_0":
         out[..., 2:34] = q.astype(np.int8).view(np.uint8)
-    elif fmt == "q4_k":
+    elif fmt in ("q4_k", "q5_k"):
         dm = np.asarray(fields["dmin"]).astype(np.float16)
         out[..., 2:4] = dm.astype("<f2").view(np.uint8).reshape(n, nb, 2)
         f16 = np.concatenate([np.asarray(fields["sc"], np.int64),
                               np.asarray(fields["m"], np.int64)], axis=-1)   # [n, nb, 16]
         bits = ((f16[..., None] >> np.arange(6)) & 1).reshape(n, nb, 96).astype(np.uint8)
         out[..., 4:16] = np.packbits(bits, axis=-1, bitorder="little")
-        out[..., 16:144] = _pack_nibbles32(q.reshape(n, nb, 8, 32)).reshape(n, nb, 128)
+        qg = q.reshape(n, nb, 8, 32)
+        q0 = 16 if fmt == "q4_k" else 48
+        out[..., q0:q0 + 128] = _pack_nibbles32(qg & 0xF).reshape(n, nb, 128)
+        if fmt == "q5_k":
+            fifth = qg >> 4                                                  # [n, nb, 8, 32]
+            qh = np.zeros((n, nb, 8, 4), np.int64)
+            for i in range(32):
+                qh[..., i % 4] |= fifth[..., i] << (i // 4)
+            out[..., 16:48] = qh.reshape(n, nb, 32).astype(np.uint8)
+    elif fmt == "iq4_xs":
+        ls = np.asarray(fields["ls"], np.int64)                              # [n, nb, 8]
+        sh = np.zeros((n, nb), np.int64)
+        sl = np.zeros((n, nb, 4), np.int64)
+        for j in range(8):
+            sh |= (ls[..., j] >> 4) << (2 * j)
+            sl[..., j // 2] |= (ls[..., j] & 0xF) << (4 * (j % 2))
+        out[..., 2:4] = sh.astype("<u2").view(np.uint8).reshape(n, nb, 2)
+        out[..., 4:8] = sl.astype(np.uint8)
+        out[..., 8:136] = _pack_nibbles32(q.reshape(n, nb, 8, 32)).reshape(n, nb, 128)
     elif fmt == "q6_k":
         out[..., 2:18] = np.asarray(fields["sc"], np.int64).astype(np.int8).view(np.uint8)
         qg = q.reshape(n, nb, 8, 32)

@@ -25,6 +25,10 @@ Per-block integer quantities (int64 here; all fit in int32):
   q4_k    D = sum xq * q              per 32-element sub-block  [m, n, k/32]
           (the min term uses the activation block sum sx)
   q6_k    P = sum xq * (q - 32)       per 16-element sub-block  [m, n, k/16]
+  q5_k    D = sum xq * q              per 32-element sub-block  [m, n, k/32]
+          (q in 0..31; the min term as for q4_k)
+  iq4_xs  D = sum xq * cb[q]          per 32-element sub-block  [m, n, k/32]
+          (the sub-block scale is d * (ls - 32))
 """
 from __future__ import annotations
 
@@ -42,9 +46,9 @@ def _codes(fmt, f, codebook):
         return f["q"] - 8
     if fmt == "q8_0":
         return f["q"]
-    if fmt == "iq4_nl":
+    if fmt in ("iq4_nl", "iq4_xs"):
         return np.asarray(codebook, np.int64)[f["q"]]
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         return f["q"]
     if fmt == "q6_k":
         return f["q"] - 32
@@ -102,7 +106,13 @@ def gemv_intdot(fmt, raw, n, k, xq, dx, sx, codebook=None):
         if fmt in ("q4_0", "q8_0", "iq4_nl"):
             # y = sum_b dx_b * d_b * D_b
             y[:, r0:r1] = np.einsum("tb,rb,trb->tr", dx, f["d"], D)
-        elif fmt == "q4_k":
+        elif fmt == "iq4_xs":
+            # y = sum_j dx_j * d * (ls_j - 32) * D_j
+            nb = k // 256
+            d = np.repeat(f["d"], 8, axis=1)
+            ls = f["ls"].reshape(nr, nb * 8).astype(np.float64)
+            y[:, r0:r1] = np.einsum("tj,rj,trj->tr", dx, d * (ls - 32), D)
+        elif fmt in ("q4_k", "q5_k"):
             nb = k // 256
             d = np.repeat(f["d"], 8, axis=1)                    # per sub-block
             dmin = np.repeat(f["dmin"], 8, axis=1)

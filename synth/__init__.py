@@ -15,6 +15,10 @@ Byte layouts written here (all little-endian, fp16 = IEEE binary16):
                                | 128 B of packed 4-bit codes
   Q6_K   256 elements, 210 B: d fp16 | 16 int8 sub-block scales in -64..63
                                | 128 B low code bits | 64 B high code bits
+  Q5_K   256 elements, 176 B: d fp16 | dmin fp16 | 12 B of sixteen 6-bit fields
+                               | 32 B fifth code bits | 128 B packed 4-bit codes
+  IQ4_XS 256 elements, 136 B: d fp16 | 2 B + 4 B of eight 6-bit sub-scales
+                               | 128 B of packed 4-bit codebook indices
 
 Because every code field is a whole number of uniformly random bits, drawing
 uniform random bytes for the packed regions gives codes that are uniform over
@@ -26,7 +30,8 @@ Distributions follow the workload descriptions of the decode GEMV study that
 this library implements: scales d (and Q4_K's dmin) uniform in [1e-3, 1e-2]
 stored as fp16 (round to nearest even), activations N(0, 1) in fp32, Q4_K
 scale and min fields uniform in 0..63, Q8_0 codes uniform in -127..127, Q6_K
-scales uniform in -64..63 and codes uniform in 0..63.
+scales uniform in -64..63 and codes uniform in 0..63. Q5_K follows Q4_K
+(codes uniform in 0..31); IQ4_XS sub-scales are uniform 6-bit fields.
 """
 from __future__ import annotations
 
@@ -37,13 +42,15 @@ __all__ = [
     "activations", "weights", "codebook", "router_weights", "moe_experts",
 ]
 
-FORMATS = ("q4_0", "q8_0", "q4_k", "q6_k", "iq4_nl")
-BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "iq4_nl": 32, "q4_k": 256, "q6_k": 256}
-BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210}
+FORMATS = ("q4_0", "q8_0", "q4_k", "q6_k", "iq4_nl", "q5_k", "iq4_xs")
+BLOCK_ELEMS = {"q4_0": 32, "q8_0": 32, "iq4_nl": 32, "q4_k": 256, "q6_k": 256, "q5_k": 256,
+               "iq4_xs": 256}
+BLOCK_BYTES = {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210, "q5_k": 176,
+               "iq4_xs": 136}
 
 # Byte offset of fields with a restricted range inside one block.
 _D_OFF = 0          # fp16 d, every format
-_DMIN_OFF_Q4K = 2   # fp16 dmin, Q4_K
+_DMIN_OFF_Q4K = 2   # fp16 dmin, Q4_K and Q5_K
 _Q8_CODES = (2, 34)
 _Q6K_SC = (2, 18)
 
@@ -98,7 +105,7 @@ def weights(fmt: str, n: int, k: int, seed: int, *, fixed_d: float | None = None
             blk[..., lo:hi] = sc.view(np.uint8)
     d = _fp16_uniform(rng, (n, nb)) if fixed_d is None else np.full((n, nb), fixed_d, np.float16)
     blk[..., _D_OFF:_D_OFF + 2] = d.astype("<f2").view(np.uint8).reshape(n, nb, 2)
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         dm = _fp16_uniform(rng, (n, nb)) if fixed_dmin is None else np.full((n, nb), fixed_dmin, np.float16)
         blk[..., _DMIN_OFF_Q4K:_DMIN_OFF_Q4K + 2] = dm.astype("<f2").view(np.uint8).reshape(n, nb, 2)
     out = np.zeros(padded_bytes(fmt, n, k), np.uint8)

@@ -21,13 +21,18 @@ def _f16_bytes(v):
 
 
 def test_block_sizes_and_q4_0_bits_per_weight():
-    assert formats.BLOCK_BYTES == {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210}
+    assert formats.BLOCK_BYTES == {"q4_0": 18, "q8_0": 34, "iq4_nl": 18, "q4_k": 144, "q6_k": 210,
+                                   "q5_k": 176, "iq4_xs": 136}
+    # bits per weight: Q5_K is Q4_K plus one bit per weight; IQ4_XS is 4.25
+    assert formats.BLOCK_BYTES["q5_k"] * 8 == formats.BLOCK_BYTES["q4_k"] * 8 + 256
+    assert formats.BLOCK_BYTES["iq4_xs"] * 8 / 256 == 4.25
     facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
     bpw = formats.BLOCK_BYTES["q4_0"] * 8 / formats.BLOCK_ELEMS["q4_0"]
     assert bpw == pytest.approx(facts["q4_0_bits_per_weight"]["value"])
     # row bytes at the workload shapes are multiples of 16
     for fmt, k, rb in [("q4_0", 2048, 1152), ("q4_0", 512, 288), ("q8_0", 4096, 4352),
-                       ("q4_k", 4096, 2304), ("iq4_nl", 4096, 2304), ("q6_k", 12288, 10080)]:
+                       ("q4_k", 4096, 2304), ("iq4_nl", 4096, 2304), ("q6_k", 12288, 10080),
+                       ("q5_k", 4096, 2816), ("iq4_xs", 4096, 2176)]:
         assert formats.row_bytes(fmt, k) == rb and rb % 16 == 0
 
 
@@ -114,12 +119,113 @@ def test_q6_k_planted_block():
     assert np.array_equal(v, exp)
 
 
+def test_q5_k_planted_block():
+    blk = [0] * 176
+    blk[0:2] = _f16_bytes(1.0)
+    blk[2:4] = _f16_bytes(0.25)
+    blk[4] = 0x02           # sc0 = 2
+    blk[10] = 0x04          # m0 = 4 (field 8 at bit 48 = byte 10 bit 0)
+    # qh: sub-block j's fifth bits in bytes 16 + 4j .. 16 + 4j + 3; element i
+    # of the sub-block at byte i % 4, bit i // 4
+    blk[16 + 0] = 0x01      # element 0 (byte 0, bit 0)
+    blk[16 + 3] = 0x80      # element 31 (byte 3, bit 7)
+    blk[16 + 1] = 0x10      # element 17 (byte 1, bit 4)
+    blk[48 + 0] = 0x35      # element 0 low 5; element 16 low 3
+    blk[48 + 1] = 0x60      # element 1 low 0; element 17 low 6
+    blk[48 + 15] = 0xF0     # element 15 low 0; element 31 low 15
+    blk[16 + 4 * 7 + 2] = 0x20  # sub-block 7 element 22 (byte 2, bit 5) -> element 246
+    v = formats.values("q5_k", np.array(blk, np.uint8), 1, 256)[0]
+    exp = np.zeros(256)
+    exp[0:32] = -0.25 * 4                 # q = 0: -dmin * m0
+    exp[0] = 2 * (5 + 16) - 1.0
+    exp[16] = 2 * 3 - 1.0
+    exp[17] = 2 * (6 + 16) - 1.0
+    exp[31] = 2 * (15 + 16) - 1.0
+    exp[246] = 0.0                        # sub-block 7: sc = 0, m = 0
+    assert np.array_equal(v, exp)
+    f = formats.decode("q5_k", np.array(blk, np.uint8), 1, 256)
+    assert f["q"][0, 0, 246] == 16 and f["q"][0, 0, 1] == 0
+
+
+def test_iq4_xs_planted_block():
+    cb = np.array([-127, -100, -80, -60, -40, -20, -10, -1, 0, 5, 15, 30, 50, 70, 90, 113], np.int8)
+    blk = [0] * 136
+    blk[0:2] = _f16_bytes(0.5)
+    # ls_0 = 33 (low 1, high 2), ls_1 = 0, ls_7 = 63 (low 15, high 3)
+    blk[4] = 0x01                               # scales_l[0]: ls_0 low 1, ls_1 low 0
+    blk[7] = 0xF0                               # scales_l[3]: ls_6 low 0, ls_7 low 15
+    sh = (2 << 0) | (3 << 14)
+    blk[2], blk[3] = sh & 0xFF, sh >> 8
+    blk[8 + 0] = 0xF9                           # element 0 -> idx 9 (5); element 16 -> idx 15 (113)
+    blk[8 + 16 * 7 + 3] = 0x07                  # sub-block 7, element 3 -> idx 7 (-1); element 19 -> idx 0
+    f = formats.decode("iq4_xs", np.array(blk, np.uint8), 1, 256, codebook=cb)
+    assert list(f["ls"][0, 0]) == [33, 0, 0, 0, 0, 0, 0, 63]
+    v = formats.values("iq4_xs", np.array(blk, np.uint8), 1, 256, codebook=cb)[0]
+    exp = np.zeros(256)
+    exp[0:32] = 0.5 * 1 * -127               # ls 33 -> scale 1, idx 0
+    exp[0] = 0.5 * 5
+    exp[16] = 0.5 * 113
+    exp[32:64] = 0.5 * -32 * -127            # ls_1 = 0 -> scale -32
+    for j in range(2, 7):
+        exp[32 * j:32 * j + 32] = 0.5 * -32 * -127   # ls 0 elsewhere
+    exp[224:256] = 0.5 * 31 * -127            # ls_7 = 63 -> 31
+    exp[224 + 3] = 0.5 * 31 * -1
+    assert np.array_equal(v, exp)
+
+
+def test_q5_k_with_zero_fifth_bits_is_q4_k():
+    # the same fields through the two decoders (different code offsets)
+    n, k = 4, 512
+    rng = np.random.default_rng(17)
+    nb = k // 256
+    f = {"d": rng.uniform(1e-3, 1e-2, (n, nb)).astype(np.float16).astype(np.float64),
+         "dmin": rng.uniform(1e-3, 1e-2, (n, nb)).astype(np.float16).astype(np.float64),
+         "sc": rng.integers(0, 64, (n, nb, 8)), "m": rng.integers(0, 64, (n, nb, 8)),
+         "q": rng.integers(0, 16, (n, nb, 256))}
+    v4 = formats.values("q4_k", formats.encode("q4_k", f), n, k)
+    v5 = formats.values("q5_k", formats.encode("q5_k", f), n, k)
+    assert np.array_equal(v4, v5)
+    # every fifth bit set adds 16 * d * sc_j to every element
+    raw5 = formats.encode("q5_k", dict(f, q=f["q"] + 16))
+    v5b = formats.values("q5_k", raw5, n, k).reshape(n, nb, 8, 32)
+    add = (16 * f["d"][..., None] * f["sc"])[..., None]
+    assert np.allclose(v5b - v4.reshape(n, nb, 8, 32), add, rtol=0, atol=1e-12)
+
+
+def test_iq4_xs_with_unit_sub_scales_is_iq4_nl():
+    # ls = 33 on every sub-block: an IQ4_XS super-block equals eight IQ4_NL
+    # blocks with the super-block's d
+    n, k = 3, 512
+    rng = np.random.default_rng(19)
+    nb = k // 256
+    cb = np.sort(rng.choice(np.arange(-127, 128), 16, replace=False)).astype(np.int8)
+    d = rng.uniform(1e-3, 1e-2, (n, nb)).astype(np.float16).astype(np.float64)
+    q = rng.integers(0, 16, (n, nb, 256))
+    vx = formats.values("iq4_xs", formats.encode("iq4_xs", {"d": d, "ls": np.full((n, nb, 8), 33), "q": q}),
+                        n, k, codebook=cb)
+    vn = formats.values("iq4_nl", formats.encode("iq4_nl", {"d": np.repeat(d, 8, axis=1),
+                                                             "q": q.reshape(n, nb * 8, 32)}), n, k, codebook=cb)
+    assert np.array_equal(vx, vn)
+
+
+def test_exhaustive_q5_k_codes_and_iq4_xs_sub_scales():
+    q = (np.arange(256) % 32).reshape(1, 1, 256)
+    f = {"d": np.ones((1, 1)), "dmin": np.zeros((1, 1)), "sc": np.ones((1, 1, 8), np.int64),
+         "m": np.zeros((1, 1, 8), np.int64), "q": q}
+    assert np.array_equal(formats.values("q5_k", formats.encode("q5_k", f), 1, 256)[0], q[0, 0].astype(float))
+    ls = np.arange(64).reshape(1, 8, 8)
+    cb = np.arange(-8, 8).astype(np.int8)
+    raw = formats.encode("iq4_xs", {"d": np.ones((1, 8)), "ls": ls, "q": np.full((1, 8, 256), 9)})
+    v = formats.values("iq4_xs", raw, 1, 2048, codebook=cb).reshape(8, 8, 32)
+    assert np.array_equal(v[..., 0], (ls[0] - 32).astype(np.float64))
+
+
 def _sane_scales(raw, fmt, n, k):
     """Overwrite fp16 scale bytes with finite values (random bytes can be NaN)."""
     bb = formats.BLOCK_BYTES[fmt]
     b = raw.reshape(n, -1, bb)
     rng = np.random.default_rng(5)
-    offs = [0, 2] if fmt == "q4_k" else [0]
+    offs = [0, 2] if fmt in ("q4_k", "q5_k") else [0]
     for o in offs:
         d = rng.uniform(-4, 4, size=b.shape[:2]).astype(np.float16)
         b[..., o:o + 2] = d.astype("<f2").view(np.uint8).reshape(*b.shape[:2], 2)
@@ -146,10 +252,13 @@ def test_fields_bytes_fields_round_trip(fmt):
         f["q"] = rng.integers(0, 16, (n, nb, 32))
     elif fmt == "q8_0":
         f["q"] = rng.integers(-128, 128, (n, nb, 32))
-    elif fmt == "q4_k":
+    elif fmt in ("q4_k", "q5_k"):
         f["dmin"] = rng.uniform(1e-3, 1e-2, (n, nb)).astype(np.float16).astype(np.float64)
         f["sc"] = rng.integers(0, 64, (n, nb, 8))
         f["m"] = rng.integers(0, 64, (n, nb, 8))
+        f["q"] = rng.integers(0, 16 if fmt == "q4_k" else 32, (n, nb, 256))
+    elif fmt == "iq4_xs":
+        f["ls"] = rng.integers(0, 64, (n, nb, 8))
         f["q"] = rng.integers(0, 16, (n, nb, 256))
     else:
         f["sc"] = rng.integers(-128, 128, (n, nb, 16))

@@ -44,10 +44,14 @@ def test_unit_scales_reduce_to_integer_matmul(fmt):
     elif fmt == "q8_0":
         f["q"] = rng.integers(-127, 128, (n, nb, 32))
         ints = f["q"]
-    elif fmt == "q4_k":
+    elif fmt in ("q4_k", "q5_k"):
+        top = 16 if fmt == "q4_k" else 32
         f.update(dmin=np.zeros((n, nb)), sc=np.ones((n, nb, 8), np.int64),
-                 m=np.zeros((n, nb, 8), np.int64), q=rng.integers(0, 16, (n, nb, 256)))
+                 m=np.zeros((n, nb, 8), np.int64), q=rng.integers(0, top, (n, nb, 256)))
         ints = f["q"]
+    elif fmt == "iq4_xs":
+        f.update(ls=np.full((n, nb, 8), 33, np.int64), q=rng.integers(0, 16, (n, nb, 256)))
+        ints = cb[f["q"]]
     else:
         f.update(sc=np.ones((n, nb, 16), np.int64), q=rng.integers(0, 64, (n, nb, 256)))
         ints = f["q"] - 32
@@ -83,7 +87,7 @@ def test_block_dots_equal_naive_python_sums(fmt):
                     c = int(q[r, i])
                     if fmt == "q4_0":
                         c -= 8
-                    elif fmt == "iq4_nl":
+                    elif fmt in ("iq4_nl", "iq4_xs"):
                         c = int(cb[c])
                     elif fmt == "q6_k":
                         c -= 32
@@ -135,3 +139,28 @@ def test_rows_subset_matches_full():
     rows = np.array([0, 7, 150, 299])
     sub = gemv.gemv_rows("q6_k", raw, n, k, rows, xq, dx)
     assert np.array_equal(sub, full[:, rows])
+
+
+def test_iq4_xs_sub_scales_scale_each_sub_block():
+    # Changing one sub-scale changes only that sub-block's share of y, by the
+    # ratio of (ls - 32): y is linear in each sub-block's scale.
+    n, k = 3, 512
+    rng = np.random.default_rng(31)
+    nb = k // 256
+    cb = _cb()
+    q = rng.integers(0, 16, (n, nb, 256))
+    d = np.full((n, nb), 0.25)
+    ls = rng.integers(0, 64, (n, nb, 8))
+    ls[:, 1, 5] = 40
+    base = formats.encode("iq4_xs", {"d": d, "ls": ls, "q": q})
+    ls2 = ls.copy()
+    ls2[:, 1, 5] = 48
+    other = formats.encode("iq4_xs", {"d": d, "ls": ls2, "q": q})
+    x = synth.activations(4, 1, k)
+    xq, dx, _ = quantize_q8(x)
+    y1 = gemv.gemv_dequant("iq4_xs", base, n, k, xq, dx, cb)
+    y2 = gemv.gemv_dequant("iq4_xs", other, n, k, xq, dx, cb)
+    # the affected sub-block covers elements 256 + 160 .. 256 + 191
+    sl = slice(256 + 160, 256 + 192)
+    part = (dx[0, sl.start // 32] * xq[0, sl].astype(np.float64)) @ (0.25 * cb[q[:, 1, 160:192]].T)
+    assert np.allclose(y2 - y1, (48 - 32 - (40 - 32)) * part, rtol=1e-12, atol=1e-12)

@@ -26,14 +26,18 @@ def test_weight_distributions(fmt):
     lo, hi = np.float16(1e-3), np.float16(1e-2)
     assert f["d"].min() >= float(lo) and f["d"].max() <= float(hi)
     q = f["q"]
-    if fmt in ("q4_0", "iq4_nl", "q4_k"):
+    if fmt in ("q4_0", "iq4_nl", "q4_k", "iq4_xs"):
         assert q.min() == 0 and q.max() == 15
+    elif fmt == "q5_k":
+        assert q.min() == 0 and q.max() == 31
     elif fmt == "q8_0":
         assert q.min() == -127 and q.max() == 127
     else:
         assert q.min() == 0 and q.max() == 63
         assert f["sc"].min() == -64 and f["sc"].max() == 63
-    if fmt == "q4_k":
+    if fmt == "iq4_xs":
+        assert f["ls"].min() == 0 and f["ls"].max() == 63
+    if fmt in ("q4_k", "q5_k"):
         assert f["dmin"].min() >= float(lo) and f["dmin"].max() <= float(hi)
         assert f["sc"].min() == 0 and f["sc"].max() == 63
         assert f["m"].min() == 0 and f["m"].max() == 63
