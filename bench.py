@@ -11,9 +11,9 @@ enough copies (> 2 GiB) that every step reads them from HBM, not from the
 
 Also reported (same run, after the timed region): microseconds per fused
 FFN sublayer (hidden 4096, intermediate 12288, Q4_K gate|up + Q6_K down),
-the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV and the MoE
-layer (256 experts, top-8 + shared, hidden 2048, intermediate 512) at M=1
-and M=16.
+the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV, the Q5_K and
+IQ4_XS GEMVs (4096 -> 12288) and the MoE layer (256 experts, top-8 + shared,
+hidden 2048, intermediate 512) at M=1 and M=16.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -411,6 +411,22 @@ def extras(qg, synth, torch):
     res["q4_0_2048_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
     log(f"q4_0 2048x2048: {us:.2f} us, {res['q4_0_2048_gbps']} GB/s")
     del Ws
+    # Q5_K and IQ4_XS (the formats of the pages' single-matrix bandwidth
+    # figures) at K = 4096, N = 12288, full qgemv_run calls
+    for fmt in ("q5_k", "iq4_xs"):
+        n, k = 12288, 4096
+        g = qg.GEMV(fmt, n, k, codebook=synth.codebook(1) if fmt == "iq4_xs" else None)
+        b = n * synth.row_bytes(fmt, k)
+        R = copies_for(b, cap=64)
+        Ws = rotated(synth.weights(fmt, n, k, seed=330), R)
+        x = dev(synth.activations(331, 1, k))
+        y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        gg = graph_of(lambda i: g.run(Ws[i % R], x, y=y), R)
+        us = time_graph(gg, R, reps=4)
+        res[f"{fmt}_{k}x{n}_us"] = round(us, 3)
+        res[f"{fmt}_{k}x{n}_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+        log(f"{fmt} {k}x{n}: {us:.2f} us, {res[f'{fmt}_{k}x{n}_gbps']} GB/s")
+        del Ws
     # M=32 batched GEMMs on int8 MFMA (Q4_K 4096 -> 12288, Q6_K 12288 -> 4096)
     for fmt, n, k in (("q4_k", 12288, 4096), ("q6_k", 4096, 12288)):
         g = qg.GEMV(fmt, n, k, max_m=32)

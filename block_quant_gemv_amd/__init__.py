@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libqgemv.so")
 LAYOUT_VERSION = 1
 
-FORMATS = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "iq4_nl": 5}
+FORMATS = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "iq4_nl": 5, "q5_k": 6, "iq4_xs": 7}
 _KIND = {"gemv": 0, "ffn": 1, "moe": 2}
 
 

@@ -43,7 +43,9 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool is_block_fmt(int f) { return f >= QFMT_Q4_0 && f <= QFMT_IQ4_NL; }
+bool is_block_fmt(int f) { return f >= QFMT_Q4_0 && f <= QFMT_IQ4_XS; }
+
+bool has_codebook(int f) { return f == QFMT_IQ4_NL || f == QFMT_IQ4_XS; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -171,14 +173,14 @@ int qgemv_create(qgemv_t* out, const qgemv_desc* d) {
     case QKIND_GEMV:
       if ((rc = check_gemv_shape(d->fmt, d->n, d->k, "gemv")) != QGEMV_OK) return rc;
       if (d->max_m < 1 || d->max_m > 32) return fail(QGEMV_ESHAPE, "gemv: max_m=%d not in 1..32", d->max_m);
-      need_cb = d->fmt == QFMT_IQ4_NL;
+      need_cb = has_codebook(d->fmt);
       break;
     case QKIND_FFN:
       if ((rc = check_gemv_shape(d->fmt_gateup, 2 * d->inter, d->hidden, "ffn gate|up")) != QGEMV_OK) return rc;
       if ((rc = check_gemv_shape(d->fmt_down, d->hidden, d->inter, "ffn down")) != QGEMV_OK) return rc;
       if (d->max_m < 1 || d->max_m > kGemvMaxTokens)
         return fail(QGEMV_ESHAPE, "ffn: max_m=%d not in 1..%d", d->max_m, kGemvMaxTokens);
-      need_cb = d->fmt_gateup == QFMT_IQ4_NL || d->fmt_down == QFMT_IQ4_NL;
+      need_cb = has_codebook(d->fmt_gateup) || has_codebook(d->fmt_down);
       break;
     case QKIND_MOE:
       if (d->n_experts < 1 || d->n_experts > 4096)
@@ -191,7 +193,7 @@ int qgemv_create(qgemv_t* out, const qgemv_desc* d) {
       if ((rc = check_gemv_shape(d->fmt_expert, d->hidden, d->inter, "moe down")) != QGEMV_OK) return rc;
       if (d->max_m < 1 || d->max_m > kGemvMaxTokens)
         return fail(QGEMV_ESHAPE, "moe: max_m=%d not in 1..%d", d->max_m, kGemvMaxTokens);
-      need_cb = d->fmt_expert == QFMT_IQ4_NL;
+      need_cb = has_codebook(d->fmt_expert);
       break;
     default:
       return fail(QGEMV_EINVAL, "qgemv_create: unknown kind %d", d->kind);
@@ -207,13 +209,13 @@ int qgemv_create(qgemv_t* out, const qgemv_desc* d) {
   if (need_cb) {
     if (!d->codebook16) {
       delete p;
-      return fail(QGEMV_EINVAL, "IQ4_NL needs a 16-entry codebook");
+      return fail(QGEMV_EINVAL, "IQ4_NL and IQ4_XS need a 16-entry codebook");
     }
     for (int i = 0; i < 16; ++i) p->cb[i] = d->codebook16[i];
     for (int i = 1; i < 16; ++i)
       if (p->cb[i] <= p->cb[i - 1]) {
         delete p;
-        return fail(QGEMV_EINVAL, "IQ4_NL codebook must be strictly ascending");
+        return fail(QGEMV_EINVAL, "the codebook must be strictly ascending");
       }
     memcpy(p->cbw, p->cb, 16);
   }

@@ -62,7 +62,8 @@ constexpr int kWavesPerWG = QG_WAVES_PER_WG;
 // wins. Q8_0 rows (4352 B at K=4096) are then split into K-segments.
 constexpr int tile_cap(int fmt) {
   return QG_TILE_CAP > 0 ? QG_TILE_CAP
-         : fmt == kQ8_0 ? 2560 : fmt == kQ4_K ? 5120 : fmt == kIQ4_NL ? 4608 : 3584;
+         : fmt == kQ8_0 ? 2560 : fmt == kQ4_K ? 5120 : fmt == kQ5_K ? 5632
+         : (fmt == kIQ4_NL || fmt == kIQ4_XS) ? 4608 : 3584;
 }
 // 16-byte chunks a step can span (alignment adds up to two), per lane.
 template <int FMT> constexpr int loads_per_lane() { return (tile_cap(FMT) + 32 + 1023) / 1024; }
@@ -220,6 +221,82 @@ struct FmtQ4_K {
   static constexpr int kDotsPerUnit = 1;
 };
 
+// Q4_K with a fifth code bit: sub-block j's fifth bits are the word
+// qh[4j..4j+3], element i (0..31) at bit 8 (i % 4) + i / 4. The four codes of
+// code dword i (elements 4i..4i+3, low nibbles) then take bit i of each
+// byte, and those of the high nibbles (elements 16 + 4i ..) bit 4 + i: one
+// shift and one mask move four fifth bits to bit 4 of their bytes.
+struct FmtQ5_K {
+  static constexpr int kUPB = 8, kBB = 176;
+  struct W { uint32_t c[8]; float dsc, dmm; };
+  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t*) {
+    W w;
+    const uint4 h = *reinterpret_cast<const uint4*>(t + off);
+    const uint32_t qh = *reinterpret_cast<const uint32_t*>(t + off + 16 + 4 * g);
+    const uint4 q = *reinterpret_cast<const uint4*>(t + off + 48 + 16 * g);
+    const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w.c[i] = (qq[i] & 0x0F0F0F0Fu) | ((qh << (4 - i)) & 0x10101010u);
+      w.c[4 + i] = ((qq[i] >> 4) & 0x0F0F0F0Fu) | ((qh >> i) & 0x10101010u);
+    }
+    const float d = half_bits(h.x & 0xffffu);
+    const float dmin = half_bits(h.x >> 16);
+    const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
+    const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
+    w.dsc = d * (float)((uint32_t)(s_lo >> (6 * g)) & 63u);
+    w.dmm = dmin * (float)((uint32_t)(s_hi >> (16 + 6 * g)) & 63u);
+    return w;
+  }
+  // sum xq * q (codes 0..31)
+  QG_DEV static int idot(const W& w, const Act& a) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4((int)w.c[i], a.x[i], s);
+    return s;
+  }
+  QG_DEV static float fma(const W& w, const Act& a, float acc) {
+    acc = fmaf(a.dx * w.dsc, (float)idot(w, a), acc);
+    return fmaf(-(a.dx * w.dmm), (float)(a.sa + a.sb), acc);
+  }
+  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
+  static constexpr int kDotsPerUnit = 1;
+};
+
+// IQ4_NL codes on a 256-element super-block with 6-bit sub-scales: header
+// d | scales_h | scales_l[4] (8 bytes), then sub-block j's 16 code bytes at
+// 8 + 16 j. Super-blocks (136 B) are 8-byte aligned in every step.
+struct FmtIQ4_XS {
+  static constexpr int kUPB = 8, kBB = 136;
+  struct W { uint32_t v[8]; float ds; };
+  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t* cb) {
+    W w;
+    const uint2 h = *reinterpret_cast<const uint2*>(t + off);
+    const uint2 qa = *reinterpret_cast<const uint2*>(t + off + 8 + 16 * g);
+    const uint2 qb = *reinterpret_cast<const uint2*>(t + off + 16 + 16 * g);
+    const uint32_t q[4] = {qa.x, qa.y, qb.x, qb.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w.v[i] = cb_lookup4(q[i] & 0x0F0F0F0Fu, cb);
+      w.v[4 + i] = cb_lookup4((q[i] >> 4) & 0x0F0F0F0Fu, cb);
+    }
+    const uint32_t ls = ((h.y >> (4 * g)) & 0xFu) | (((h.x >> (16 + 2 * g)) & 3u) << 4);
+    w.ds = half_bits(h.x & 0xffffu) * (float)((int)ls - 32);
+    return w;
+  }
+  QG_DEV static int idot(const W& w, const Act& a) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4((int)w.v[i], a.x[i], s);
+    return s;
+  }
+  QG_DEV static float fma(const W& w, const Act& a, float acc) {
+    return fmaf((float)idot(w, a), a.dx * w.ds, acc);
+  }
+  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
+  static constexpr int kDotsPerUnit = 1;
+};
+
 struct FmtQ6_K {
   static constexpr int kUPB = 8, kBB = 210;
   struct W { uint32_t c[8]; float d; int sca, scb; };
@@ -276,6 +353,8 @@ template <> struct FmtOf<kQ8_0> { using T = FmtQ8_0; };
 template <> struct FmtOf<kIQ4_NL> { using T = FmtIQ4_NL; };
 template <> struct FmtOf<kQ4_K> { using T = FmtQ4_K; };
 template <> struct FmtOf<kQ6_K> { using T = FmtQ6_K; };
+template <> struct FmtOf<kQ5_K> { using T = FmtQ5_K; };
+template <> struct FmtOf<kIQ4_XS> { using T = FmtIQ4_XS; };
 
 // ------------------------------------------------------------ the kernel --
 
@@ -637,7 +716,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
 int fmt_block_elems(int fmt) {
   switch (fmt) {
     case kQ4_0: case kQ8_0: case kIQ4_NL: return 32;
-    case kQ4_K: case kQ6_K: return 256;
+    case kQ4_K: case kQ6_K: case kQ5_K: case kIQ4_XS: return 256;
     case kF32: return 1;
     default: return 0;
   }
@@ -649,6 +728,8 @@ int fmt_block_bytes(int fmt) {
     case kQ8_0: return 34;
     case kQ4_K: return 144;
     case kQ6_K: return 210;
+    case kQ5_K: return 176;
+    case kIQ4_XS: return 136;
     case kF32: return 4;
     default: return 0;
   }
@@ -686,7 +767,7 @@ static int max_passes(int mt) { return mt <= 2 ? 8 : mt == 4 ? 4 : mt == 8 ? 2 :
 // over the chip.
 static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, int nprob, GemvGeom& g) {
   g = GemvGeom{};
-  const int upb = (fmt == kQ4_K || fmt == kQ6_K) ? 8 : 1;
+  const int upb = fmt_block_elems(fmt) / 32;
   const int bb = fmt_block_bytes(fmt);
   g.U = (int)(k / 32);
   g.rb = fmt_row_bytes(fmt, k);
@@ -813,6 +894,8 @@ static hipError_t launch_fmt(int fmt, const GemvArgs& a, int mt, int P, hipStrea
     case kQ4_K: return launch_mt<kQ4_K, DOTS, FUSEQ>(a, mt, P, s);
     case kQ6_K: return launch_mt<kQ6_K, DOTS, FUSEQ>(a, mt, P, s);
     case kIQ4_NL: return launch_mt<kIQ4_NL, DOTS, FUSEQ>(a, mt, P, s);
+    case kQ5_K: return launch_mt<kQ5_K, DOTS, FUSEQ>(a, mt, P, s);
+    case kIQ4_XS: return launch_mt<kIQ4_XS, DOTS, FUSEQ>(a, mt, P, s);
     default: return hipErrorInvalidValue;
   }
 }

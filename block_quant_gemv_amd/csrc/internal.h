@@ -7,7 +7,7 @@
 
 namespace qg {
 
-enum Fmt { kF32 = 0, kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3, kQ6_K = 4, kIQ4_NL = 5 };
+enum Fmt { kF32 = 0, kQ4_0 = 1, kQ8_0 = 2, kQ4_K = 3, kQ6_K = 4, kIQ4_NL = 5, kQ5_K = 6, kIQ4_XS = 7 };
 
 // Elements and bytes of one block of each format (0 for F32).
 int fmt_block_elems(int fmt);

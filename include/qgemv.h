@@ -87,16 +87,28 @@ enum {
  *              value = d * sc_j * (q - 32).
  *  QFMT_IQ4_NL 32 elements / 18 B: Q4_0 layout; value = d * codebook[q],
  *              codebook = 16 sorted int8 given at plan creation.
+ *  QFMT_Q5_K   256 elements / 176 B: d fp16 | dmin fp16 | scales[12] (as
+ *              Q4_K) | qh[32] | qs[128] (low 4 bits, as Q4_K). The fifth
+ *              bit of element 32j + i is bit i / 4 of qh[4j + i % 4].
+ *              q = low | fifth << 4 (0..31); value = d * sc_j * q - dmin * m_j.
+ *  QFMT_IQ4_XS 256 elements / 136 B: d fp16 | scales_h u16 | scales_l[4] |
+ *              qs[128] (4-bit indices, as Q4_K). Sub-scale ls_j (0..63) =
+ *              nibble j % 2 of scales_l[j / 2] (low nibble first) | bits
+ *              2j..2j+1 of scales_h as bits 4..5.
+ *              value = d * (ls_j - 32) * codebook[q].
  * The per-format value formulas are those of the decode-GEMV workloads the
- * library targets; the pages give no byte order, so the order above is this
- * library's own and is versioned by QGEMV_LAYOUT_VERSION. */
+ * library targets (Q5_K and IQ4_XS: the formats whose single-matrix
+ * bandwidth the pages report); the pages give no byte order, so the order
+ * above is this library's own and is versioned by QGEMV_LAYOUT_VERSION. */
 enum {
   QFMT_F32 = 0,
   QFMT_Q4_0 = 1,
   QFMT_Q8_0 = 2,
   QFMT_Q4_K = 3,
   QFMT_Q6_K = 4,
-  QFMT_IQ4_NL = 5
+  QFMT_IQ4_NL = 5,
+  QFMT_Q5_K = 6,
+  QFMT_IQ4_XS = 7
 };
 
 enum { QKIND_GEMV = 0, QKIND_FFN = 1, QKIND_MOE = 2 };
@@ -106,7 +118,7 @@ typedef struct qgemv_desc {
   int32_t kind;            /* QKIND_*                                        */
   int32_t layout_version;  /* must be QGEMV_LAYOUT_VERSION                   */
   /* QKIND_GEMV: y[m, n] = W[n, k] . x[m, k]                                 */
-  int32_t fmt;             /* QFMT_Q4_0 .. QFMT_IQ4_NL                       */
+  int32_t fmt;             /* QFMT_Q4_0 .. QFMT_IQ4_XS                       */
   int32_t max_m;           /* largest m passed to qgemv_run (1..32)          */
   int64_t n;               /* rows (outputs), >= 1                           */
   int64_t k;               /* inputs, multiple of the format's block elems   */
@@ -122,8 +134,8 @@ typedef struct qgemv_desc {
   int64_t n_experts;       /* routed experts                                 */
   int32_t top_k;           /* experts selected per token (1..16)             */
   int32_t fmt_expert;      /* QFMT_* of every expert matrix                  */
-  /* QFMT_IQ4_NL only: host pointer to 16 int8 codebook entries sorted
-   * ascending, copied at plan creation (the pointer is not kept).          */
+  /* QFMT_IQ4_NL and QFMT_IQ4_XS only: host pointer to 16 int8 codebook
+   * entries sorted ascending, copied at plan creation (not kept).          */
   const int8_t *codebook16;
 } qgemv_desc;
 

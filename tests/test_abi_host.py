@@ -72,6 +72,9 @@ def test_create_validation():
     assert _create(_desc(layout_version=2))[0] == EVERSION
     assert _create(_desc(fmt=0))[0] == EFORMAT
     assert _create(_desc(fmt=9))[0] == EFORMAT
+    assert _create(_desc(fmt=8))[0] == EFORMAT
+    assert _create(_desc(fmt=6, k=128))[0] == ESHAPE          # Q5_K needs K % 256 == 0
+    assert _create(_desc(fmt=7))[0] == EINVAL                 # IQ4_XS without codebook
     assert _create(_desc(k=48))[0] == ESHAPE
     assert _create(_desc(fmt=3, k=128))[0] == ESHAPE          # Q4_K needs K % 256 == 0
     assert _create(_desc(n=0))[0] == ESHAPE
@@ -83,7 +86,11 @@ def test_create_validation():
     assert _create(_desc(fmt=5, codebook16=ctypes.cast(bad, ctypes.POINTER(ctypes.c_int8))))[0] == EINVAL
     assert b"ascending" in lib.qgemv_last_error()
     good = (ctypes.c_int8 * 16)(*range(-8, 8))
-    rc, h = _create(_desc(fmt=5, codebook16=ctypes.cast(good, ctypes.POINTER(ctypes.c_int8))))
+    for fmt in (5, 7):
+        rc, h = _create(_desc(fmt=fmt, k=512, codebook16=ctypes.cast(good, ctypes.POINTER(ctypes.c_int8))))
+        assert rc == OK and h.value
+        lib.qgemv_destroy(h)
+    rc, h = _create(_desc(fmt=6, k=512))
     assert rc == OK and h.value
     lib.qgemv_destroy(h)
     assert lib.qgemv_create(None, None) == EINVAL

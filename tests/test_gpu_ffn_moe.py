@@ -33,13 +33,16 @@ def _ws_arrays(plan, ws, m, spec):
     return out
 
 
-@pytest.mark.parametrize("hidden,inter,m", [(4096, 12288, 1), (512, 1024, 3), (256, 512, 16)])
-def test_ffn_staged(hidden, inter, m):
-    say(f"ffn hidden={hidden} inter={inter} m={m}")
-    wgu = synth.weights("q4_k", 2 * inter, hidden, seed=11)
-    wdn = synth.weights("q6_k", hidden, inter, seed=12)
+@pytest.mark.parametrize("hidden,inter,m,fgu,fdn", [(4096, 12288, 1, "q4_k", "q6_k"),
+                                                    (512, 1024, 3, "q4_k", "q6_k"),
+                                                    (256, 512, 16, "q4_k", "q6_k"),
+                                                    (1024, 2048, 2, "q5_k", "q5_k")])
+def test_ffn_staged(hidden, inter, m, fgu, fdn):
+    say(f"ffn hidden={hidden} inter={inter} m={m} {fgu}/{fdn}")
+    wgu = synth.weights(fgu, 2 * inter, hidden, seed=11)
+    wdn = synth.weights(fdn, hidden, inter, seed=12)
     x = synth.activations(13, m, hidden)
-    f = qg.FFN(hidden, inter, "q4_k", "q6_k", max_m=m)
+    f = qg.FFN(hidden, inter, fgu, fdn, max_m=m)
     ws = f.workspace(m)
     full, y = guarded(torch, m * hidden, torch.float32)
     f.run(dev(wgu), dev(wdn), dev(x), y=y.view(m, hidden), ws=ws)
@@ -57,7 +60,7 @@ def test_ffn_staged(hidden, inter, m):
     assert np.array_equal(S["dx"].reshape(m, -1).view(np.int32), dx.view(np.int32))
     assert np.array_equal(S["sx"].reshape(m, -1), sx)
     # F2: gate|up
-    gu_ref = og.gemv_dequant("q4_k", wgu, 2 * inter, hidden, xq, dx)
+    gu_ref = og.gemv_dequant(fgu, wgu, 2 * inter, hidden, xq, dx)
     gu = S["gu"].reshape(m, 2 * inter)
     e2 = normwise(gu, gu_ref)
     assert e2 <= TOL, e2
@@ -70,10 +73,10 @@ def test_ffn_staged(hidden, inter, m):
     assert np.array_equal(S["hd"].reshape(m, -1).view(np.int32), hd.view(np.int32))
     assert np.array_equal(S["hs"].reshape(m, -1), hs)
     # F4 (graded): down on the device's re-quantized h
-    y_ref = og.gemv_dequant("q6_k", wdn, hidden, inter, hq, hd)
+    y_ref = og.gemv_dequant(fdn, wdn, hidden, inter, hq, hd)
     e4 = normwise(y, y_ref)
     # F5 (information): fully independent chain
-    full_ref = offn.ffn_ref(wgu, wdn, x, hidden, inter)
+    full_ref = offn.ffn_ref(wgu, wdn, x, hidden, inter, fgu, fdn)
     flips = int((full_ref["hq"] != hq).sum())
     say(f"  F2 {e2:.2e}  F4 {e4:.2e}  independent {normwise(y, full_ref['y']):.2e} (h code flips {flips})")
     assert e4 <= TOL

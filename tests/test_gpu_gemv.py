@@ -17,6 +17,7 @@ if not torch.cuda.is_available():
 import block_quant_gemv_amd as qg  # noqa: E402
 
 CB_SEED = 77
+CB_FORMATS = ("iq4_nl", "iq4_xs")
 
 
 def _codebook():
@@ -136,11 +137,21 @@ SMALL = [
     ("q8_0", 1000, 4096, 16),
     ("q4_0", 700, 8192, 2),
     ("q8_0", 8, 4096, 1),
+    # Q5_K and IQ4_XS: the formats the pages' single-matrix bandwidth figures
+    # are quoted on (full-size shape, ragged rows, several tokens, long rows)
+    ("q5_k", 4096, 4096, 1),
+    ("q5_k", 257, 768, 3),
+    ("q5_k", 20, 256, 16),
+    ("q5_k", 33, 16384, 2),
+    ("iq4_xs", 4096, 4096, 1),
+    ("iq4_xs", 257, 768, 2),     # 3 super-blocks per row: 8-byte aligned rows
+    ("iq4_xs", 20, 256, 8),
+    ("iq4_xs", 9, 16640, 1),     # 65 super-blocks per row, K-segmented
 ]
 
 
 def _run_case(fmt, n, k, m, seed):
-    cb = _codebook() if fmt == "iq4_nl" else None
+    cb = _codebook() if fmt in CB_FORMATS else None
     w = synth.weights(fmt, n, k, seed=seed)
     x = synth.activations(seed + 1, m, k)
     g = qg.GEMV(fmt, n, k, max_m=max(m, 1), codebook=cb)
@@ -170,10 +181,11 @@ def test_gemv_parity(fmt, n, k, m):
 
 @pytest.mark.parametrize("fmt,n,k", [("q8_0", 12288, 4096), ("q8_0", 24576, 4096),
                                      ("q4_k", 12288, 4096), ("q4_k", 24576, 4096),
-                                     ("iq4_nl", 248320, 4096)])
+                                     ("iq4_nl", 248320, 4096), ("q5_k", 12288, 4096),
+                                     ("iq4_xs", 12288, 4096)])
 def test_gemv_full_size_sampled_rows(fmt, n, k):
     say(f"gemv full size {fmt} n={n} k={k}")
-    cb = _codebook() if fmt == "iq4_nl" else None
+    cb = _codebook() if fmt in CB_FORMATS else None
     w = synth.weights(fmt, n, k, seed=101)
     x = synth.activations(102, 1, k)
     g = qg.GEMV(fmt, n, k, codebook=cb)
