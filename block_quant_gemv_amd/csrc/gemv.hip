@@ -46,7 +46,7 @@ namespace qg {
 #define QG_WLOAD_AUX 2    // cache-policy bits of the weight loads (2: non-temporal, read once)
 #endif
 #ifndef QG_Q4K_DIRECT
-#define QG_Q4K_DIRECT 1   // single-token Q4_K GEMVs use the register-direct kernel
+#define QG_Q4K_DIRECT 1   // single-token Q4_K and Q5_K GEMVs use the register-direct kernel
 #endif
 #ifndef QG_PREFETCH
 #define QG_PREFETCH 1     // weight steps in flight per wave (1 or 2)
@@ -918,7 +918,7 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
   if (p.m < 1 || p.m > kGemvMaxTokens || p.n < 1) return hipErrorInvalidValue;
   if (p.xf && dots_epilogue) return hipErrorInvalidValue;
 #if QG_Q4K_DIRECT
-  if (fmt == kQ4_K && q4k_direct_ok(p, dots_epilogue)) return launch_q4k_direct(p, dots_epilogue, s);
+  if (kdirect_ok(fmt, p, dots_epilogue)) return launch_kdirect(fmt, p, dots_epilogue, s);
 #endif
   int mt = token_tile(p.tbl ? kGroupTokens : p.m);
   GemvArgs a;

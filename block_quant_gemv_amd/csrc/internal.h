@@ -74,12 +74,13 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
 // Codes xq [m, k] (m <= 32) copied to the token-tiled layout [block][token][32].
 hipError_t launch_tile_codes(const int8_t* xq, int8_t* xqt, int m, int kblocks, hipStream_t s);
 
-// Single-token Q4_K GEMV that loads the 16-byte-aligned super-block fields
-// straight into registers (no LDS); applies when q4k_direct_ok(p): m == 1,
-// quantized activations given, no grouping, K a multiple of 2048 up to 8192.
-// dots selects the integer-store checking epilogue (p.dots, int32 [n, K/32]).
-bool q4k_direct_ok(const GemvProblem& p, bool dots);
-hipError_t launch_q4k_direct(const GemvProblem& p, bool dots, hipStream_t s);
+// Single-token Q4_K / Q5_K GEMV that loads the 16-byte-aligned super-block
+// fields straight into registers (no LDS); applies when kdirect_ok(fmt, p):
+// m == 1, quantized activations given, no grouping, K a multiple of 2048 up
+// to 8192. dots selects the integer-store checking epilogue (p.dots, int32
+// [n, K/32]).
+bool kdirect_ok(int fmt, const GemvProblem& p, bool dots);
+hipError_t launch_kdirect(int fmt, const GemvProblem& p, bool dots, hipStream_t s);
 
 // Largest token count one GEMV launch handles.
 constexpr int kGemvMaxTokens = 16;

@@ -143,6 +143,9 @@ SMALL = [
     ("q5_k", 257, 768, 3),
     ("q5_k", 20, 256, 16),
     ("q5_k", 33, 16384, 2),
+    ("q5_k", 333, 2048, 1),       # register-direct kernel: K = 2048 ... 8192,
+    ("q5_k", 8195, 4096, 1),      # four-row groups with a ragged last group
+    ("q5_k", 4097, 8192, 1),
     ("iq4_xs", 4096, 4096, 1),
     ("iq4_xs", 257, 768, 2),     # 3 super-blocks per row: 8-byte aligned rows
     ("iq4_xs", 20, 256, 8),
