@@ -34,6 +34,9 @@ def _ws_arrays(plan, ws, m, spec):
 
 
 @pytest.mark.parametrize("hidden,inter,m,fgu,fdn", [(4096, 12288, 1, "q4_k", "q6_k"),
+                                                    (4096, 256, 1, "q5_k", "q6_k"),
+                                                    (6144, 1024, 1, "q4_k", "q4_0"),
+                                                    (8192, 4096, 1, "q5_k", "q8_0"),
                                                     (512, 1024, 3, "q4_k", "q6_k"),
                                                     (256, 512, 16, "q4_k", "q6_k"),
                                                     (1024, 2048, 2, "q5_k", "q5_k")])
@@ -80,6 +83,46 @@ def test_ffn_staged(hidden, inter, m, fgu, fdn):
     flips = int((full_ref["hq"] != hq).sum())
     say(f"  F2 {e2:.2e}  F4 {e4:.2e}  independent {normwise(y, full_ref['y']):.2e} (h code flips {flips})")
     assert e4 <= TOL
+
+
+def test_ffn_repeated_calls_and_graph_replays():
+    # Starting from a workspace of 0xFF bytes (nothing may rely on a cleared
+    # workspace), repeated eager calls and graph replays (with eager calls in
+    # between) must reproduce each input's result bit for bit, and the last
+    # eager result must match the oracle on the device's codes.
+    hidden, inter = 4096, 12288
+    wgu = dev(synth.weights("q4_k", 2 * inter, hidden, seed=21))
+    wdn_np = synth.weights("q6_k", hidden, inter, seed=22)
+    wdn = dev(wdn_np)
+    f = qg.FFN(hidden, inter)
+    ws = f.workspace(1)
+    ws.fill_(255)
+    xs = [dev(synth.activations(800 + i, 1, hidden)) for i in range(3)]
+    eager = [f.run(wgu, wdn, x, ws=ws).clone() for x in xs]
+    torch.cuda.synchronize()
+    hq = host(f.ws_view(ws, 1, "hq", torch.int8, inter))[None]
+    hd = host(f.ws_view(ws, 1, "hd", torch.float32, inter // 32))[None]
+    e = normwise(host(eager[2]), og.gemv_dequant("q6_k", wdn_np, hidden, inter, hq, hd))
+    say(f"  last eager call vs oracle on the device's codes {e:.2e}")
+    assert e <= TOL
+    for i in range(3):
+        assert torch.equal(f.run(wgu, wdn, xs[i], ws=ws), eager[i]), f"eager repeat {i}"
+    x_in = xs[0].clone()
+    y_out = torch.empty((1, hidden), dtype=torch.float32, device="cuda")
+    f.run(wgu, wdn, x_in, y=y_out, ws=ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f.run(wgu, wdn, x_in, y=y_out, ws=ws)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            x_in.copy_(xs[i])
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_out, eager[i]), f"replay {rep} input {i}"
+            other = f.run(wgu, wdn, xs[(i + 1) % 3], ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager[(i + 1) % 3])
 
 
 def _moe_inputs(E, H, I, seed):
