@@ -22,6 +22,9 @@ precision:
 * `ffn`: SwiGLU, re-quantization and the fused FFN chain, stage by stage.
 * `moe`: the fp32 router GEMV, softmax / top-k / renormalisation, expert
   chains and the weighted combine with the shared expert.
+* `attention`: decode attention of one token over an fp16 KV cache
+  (grouped-query heads), the definition that the two-stage chunked
+  reduction rearranges.
 
 Sources: the method is described on three web pages -- "Why expert caching
 can't save dense models: running a 27B dense model in 16 GB VRAM" (xhh.club
@@ -32,4 +35,4 @@ three on device MoE kernels and the CPU reference matvec). Where the pages are
 silent (byte order inside blocks, tie-breaking, the zero block), each module
 states the reading it takes.
 """
-from . import formats, quant, gemv, ffn, moe  # noqa: F401
+from . import formats, quant, gemv, ffn, moe, attention  # noqa: F401

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the block-quantized GEMV, FFN and MoE workloads.
+"""Seeded synthetic inputs for the block-quantized GEMV, FFN and MoE workloads
+(and the decode-attention workload that runs beside them).
 
 This module is shared by the GPU tests, the benchmark and the CPU oracle's
 tests. It only draws random numbers and places them at the byte positions of
@@ -39,7 +40,7 @@ import numpy as np
 
 __all__ = [
     "FORMATS", "BLOCK_ELEMS", "BLOCK_BYTES", "row_bytes", "padded_bytes",
-    "activations", "weights", "codebook", "router_weights", "moe_experts",
+    "activations", "weights", "codebook", "router_weights", "moe_experts", "attention_inputs",
 ]
 
 FORMATS = ("q4_0", "q8_0", "q4_k", "q6_k", "iq4_nl", "q5_k", "iq4_xs")
@@ -143,3 +144,14 @@ def moe_experts(seed: int, n_experts: int, hidden: int, inter: int, fmt: str = "
     gu = weights(fmt, gu_one, hidden, int(s1))
     dn = weights(fmt, n_experts * hidden, inter, int(s2))
     return gu, dn
+
+
+def attention_inputs(seed: int, n_heads: int, n_kv_heads: int, head_dim: int, n_ctx: int):
+    """Decode-attention inputs: q fp32 [n_heads, head_dim] ~ N(0, 1); keys and
+    values fp16 [n_kv_heads, n_ctx, head_dim] ~ N(0, 1) rounded to fp16
+    (draw order: q, k, v)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n_heads, head_dim)).astype(np.float32)
+    k = rng.standard_normal((n_kv_heads, n_ctx, head_dim)).astype(np.float16)
+    v = rng.standard_normal((n_kv_heads, n_ctx, head_dim)).astype(np.float16)
+    return q, k, v
