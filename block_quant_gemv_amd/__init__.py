@@ -2,7 +2,7 @@
 for AMD MI355X (gfx950).
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernels behind the C ABI declared in include/qgemv.h. Tensors are torch
+kernels behind the C ABI declared in include/qgemv.h and include/qattn.h. Tensors are torch
 tensors on the GPU; streams are torch's current stream. There is no CPU
 fallback: importing this package raises if the library is missing, and every
 call raises RuntimeError on a non-zero status.
@@ -14,7 +14,7 @@ import os
 
 import torch  # loads torch's HIP runtime first; the library then binds to it
 
-__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "debug_quantize", "lib_path", "LAYOUT_VERSION"]
+__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "lib_path", "LAYOUT_VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libqgemv.so")
@@ -65,7 +65,9 @@ _lib.qgemv_status_string.restype = ctypes.c_char_p
 _lib.qgemv_last_error.restype = ctypes.c_char_p
 _lib.qgemv_debug_quantize.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_size_t, _vp]
-for _f in ("qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
+_lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
+_lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
+for _f in ("qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -304,3 +306,36 @@ def debug_quantize(x: torch.Tensor, stream=None):
     _check(_lib.qgemv_debug_quantize(_dev(x, torch.float32, "x"), xq.data_ptr(), dx.data_ptr(), sx.data_ptr(),
                                      m, k, _stream(stream)), "qgemv_debug_quantize")
     return xq, dx, sx
+
+
+class Attention:
+    """Decode attention of one token over an fp16 KV cache (qattn_decode):
+    q fp32 [n_heads, head_dim], caches fp16 [n_kv_heads, n_ctx, head_dim]."""
+
+    def __init__(self, n_heads: int, n_kv_heads: int, head_dim: int):
+        self.n_heads, self.n_kv_heads, self.head_dim = n_heads, n_kv_heads, head_dim
+
+    def workspace_size(self, n_ctx: int) -> int:
+        b = _sz()
+        _check(_lib.qattn_workspace_size(self.n_heads, self.n_kv_heads, self.head_dim, n_ctx, ctypes.byref(b)),
+               "qattn_workspace_size")
+        return b.value
+
+    def workspace(self, n_ctx: int, device="cuda") -> torch.Tensor:
+        return torch.empty(max(1, self.workspace_size(n_ctx)), dtype=torch.uint8, device=device)
+
+    def run(self, q, k_cache, v_cache, out=None, ws=None, stream=None):
+        n_ctx = k_cache.shape[1] if k_cache.dim() == 3 else 0
+        if k_cache.shape != (self.n_kv_heads, n_ctx, self.head_dim) or v_cache.shape != k_cache.shape:
+            raise ValueError("k_cache and v_cache must be [n_kv_heads, n_ctx, head_dim]")
+        if q.shape != (self.n_heads, self.head_dim):
+            raise ValueError("q must be [n_heads, head_dim]")
+        if out is None:
+            out = torch.empty((self.n_heads, self.head_dim), dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = self.workspace(n_ctx, q.device)
+        _check(_lib.qattn_decode(_dev(q, torch.float32, "q"), _dev(k_cache, torch.float16, "k_cache"),
+                                 _dev(v_cache, torch.float16, "v_cache"), _dev(out, torch.float32, "out"),
+                                 self.n_heads, self.n_kv_heads, self.head_dim, n_ctx,
+                                 _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qattn_decode")
+        return out

@@ -15,8 +15,10 @@
 
 #include <new>
 
+#include "../../include/qattn.h"
 #include "../../include/qgemv.h"
 #include "internal.h"
+#include "attn.h"
 #include "moe.h"
 #include "mfma.h"
 #include "swiglu.h"
@@ -548,6 +550,50 @@ int qgemv_debug_block_dots(qgemv_t h, const void* w, const int8_t* xq, int32_t* 
     if (rc) return rc;
   }
   return QGEMV_OK;
+}
+
+namespace {
+int attn_shape(int n_heads, int n_kv_heads, int head_dim, int64_t n_ctx, AttnShape& a, const char* fn) {
+  a.n_heads = n_heads;
+  a.n_kv = n_kv_heads;
+  a.head_dim = head_dim;
+  a.n_ctx = n_ctx;
+  if (!attn_supported(a))
+    return fail(QGEMV_ESHAPE,
+                "%s: unsupported shape heads=%d kv_heads=%d head_dim=%d n_ctx=%lld (head_dim 128/256, "
+                "heads/kv_heads in {1,2,4,8}, 1 <= n_ctx, n_ctx*head_dim*2 + 4096 < 2^31)",
+                fn, n_heads, n_kv_heads, head_dim, (long long)n_ctx);
+  return QGEMV_OK;
+}
+}  // namespace
+
+int qattn_workspace_size(int n_heads, int n_kv_heads, int head_dim, int64_t n_ctx, size_t* bytes) {
+  if (!bytes) return fail(QGEMV_EINVAL, "qattn_workspace_size: null pointer");
+  AttnShape a;
+  int rc = attn_shape(n_heads, n_kv_heads, head_dim, n_ctx, a, "qattn_workspace_size");
+  if (rc) return rc;
+  *bytes = attn_workspace_bytes(a);
+  return QGEMV_OK;
+}
+
+int qattn_decode(const float* q, const void* k_cache, const void* v_cache, float* out, int n_heads,
+                 int n_kv_heads, int head_dim, int64_t n_ctx, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !out) return fail(QGEMV_EINVAL, "qattn_decode: null pointer");
+  AttnShape a;
+  int rc = attn_shape(n_heads, n_kv_heads, head_dim, n_ctx, a, "qattn_decode");
+  if (rc) return rc;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return fail(QGEMV_EALIGN, "qattn_decode: q, caches and out need 16-byte alignment");
+  const size_t need = attn_workspace_bytes(a);
+  if (need) {
+    if (!ws) return fail(QGEMV_EINVAL, "qattn_decode: this context needs a workspace of %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QGEMV_EALIGN, "qattn_decode: ws needs 256-byte alignment");
+    if (ws_bytes < need) return fail(QGEMV_EWORKSPACE, "qattn_decode: workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  if (fault_injected()) return fail(QGEMV_EHIP, "qattn_decode: launch failure injected (QGEMV_FAULT)");
+  return check_launch(launch_attn(a, q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                                  out, ws, static_cast<hipStream_t>(stream)),
+                      "attention");
 }
 
 }  // extern "C"

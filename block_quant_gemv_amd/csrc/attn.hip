@@ -1,0 +1,329 @@
+// Decode attention of one new token over an fp16 KV cache, in two stages.
+//
+// The long-context attention of "Why expert caching can't save dense models:
+// running a 27B dense model in 16 GB VRAM" (xhh.club, in-place compute and
+// single-stream fusion section and its Q&A) splits the cached tokens into
+// chunks, computes each chunk's partial softmax result, then merges the
+// chunks; a short context takes one online-softmax pass. Here:
+//
+// Stage 1 (attn_partial_kernel): one workgroup per (chunk, key/value head)
+// computes, for the G query heads that share that key/value head
+// (grouped-query attention; the workload shape, 16 query heads over 2
+// key/value heads of dimension 256, is the gated-attention shape in
+// "Understanding Qwen3.6-35B-A3B in llama.cpp", cnblogs, section 1.1), the
+// chunk's running maximum m, sum l of exp(s - m) and unnormalised output
+// sum_t exp(s_t - m) v_t. Keys and values are read once per group of G
+// heads. A token's row of D fp16 values is spread over D/8 lanes, 16 bytes
+// each, so one 128-bit load instruction of a wave reads 1 KB of consecutive
+// tokens; the lanes of a token add their partial dot products with DPP and
+// one cross-row exchange, and each lane keeps the running state for its 8
+// dimensions. Scores are kept in base 2 (q pre-scaled by log2(e)/sqrt(D)),
+// so every exponential is one v_exp_f32.
+//
+// Stage 2 (attn_merge_kernel): per query head, M = max_c m_c,
+// L = sum_c l_c 2^(m_c - M), o = sum_c 2^(m_c - M) o_c / L.
+//
+// With a single chunk stage 1 normalises and writes o itself.
+#include "attn.h"
+#include "common.cuh"
+
+namespace qg {
+
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBatch = 4;          // token iterations whose loads are issued together
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
+
+QG_DEV float h2f(uint32_t bits) { return half_bits(bits & 0xffffu); }
+
+// Running softmax state of one lane for G heads and its 8 dimensions.
+template <int G>
+struct AState {
+  float m[G], l[G], acc[G][8];
+};
+
+// Merge state b into a (both over disjoint token sets), base-2 exponents.
+template <int G>
+QG_DEV void merge_into(AState<G>& a, const float (&mb)[G], const float (&lb)[G], const float (&ob)[G][8]) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float M = fmaxf(a.m[j], mb[j]);
+    const float ca = a.m[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.m[j] - M);
+    const float cb = mb[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb[j] - M);
+    a.m[j] = M;
+    a.l[j] = a.l[j] * ca + lb[j] * cb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a.acc[j][i] = a.acc[j][i] * ca + ob[j][i] * cb;
+  }
+}
+
+// D: head dimension (128 or 256); G: query heads per key/value head.
+// grid = (nchunks, n_kv); block = 4 waves.
+template <int D, int G>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po,
+    int64_t n_ctx, int64_t chunk, int nchunks, float qscale) {
+  constexpr int LPT = D / 8;          // lanes per token
+  constexpr int TPW = 64 / LPT;       // tokens per wave load
+  __shared__ float red[kAttnWaves][G][2 + D];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int dl = lane % LPT;          // this lane's 8 dimensions: 8 dl .. 8 dl + 7
+  const int slot = lane / LPT;        // token slot within a wave load
+
+  // Query rows of the group, this lane's dimensions, pre-scaled.
+  float qr[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float4* qp = reinterpret_cast<const float4*>(q + ((int64_t)kvh * G + j) * D + 8 * dl);
+    const float4 a = qp[0], b = qp[1];
+    qr[j][0] = a.x * qscale; qr[j][1] = a.y * qscale; qr[j][2] = a.z * qscale; qr[j][3] = a.w * qscale;
+    qr[j][4] = b.x * qscale; qr[j][5] = b.y * qscale; qr[j][6] = b.z * qscale; qr[j][7] = b.w * qscale;
+  }
+
+  AState<G> st;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    st.m[j] = -INFINITY;
+    st.l[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[j][i] = 0.0f;
+  }
+
+  // This head's cache through buffer resources spanning exactly its n_ctx
+  // rows: reads past the last token return zeros without a memory access.
+  const int64_t head_off = (int64_t)kvh * n_ctx * D;
+  const int nbytes = (int)(n_ctx * D * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, nbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, nbytes, kBufWord3);
+
+  const int64_t t0 = (int64_t)c * chunk;
+  const int64_t t1 = (t0 + chunk) < n_ctx ? (t0 + chunk) : n_ctx;
+  constexpr int kStep = kAttnWaves * TPW;  // tokens per iteration of the whole workgroup
+  for (int64_t tb = t0 + (int64_t)wid * TPW; tb < t1; tb += (int64_t)kStep * kAttnBatch) {
+    u32x4 kb[kAttnBatch], vb[kAttnBatch];
+#pragma unroll
+    for (int u = 0; u < kAttnBatch; ++u) {
+      const int64_t t = tb + (int64_t)u * kStep + slot;
+      const int off = (int)((t < t1 ? t : n_ctx) * (D * 2)) + 16 * dl;  // past the chunk: out of range, zeros
+      kb[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 2);
+      vb[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 2);
+    }
+#pragma unroll
+    for (int u = 0; u < kAttnBatch; ++u) {
+      const int64_t t = tb + (int64_t)u * kStep + slot;
+      const bool valid = t < t1;
+      float kf[8], vf[8];
+      const uint32_t kw[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
+      const uint32_t vw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kf[2 * i] = h2f(kw[i]);
+        kf[2 * i + 1] = h2f(kw[i] >> 16);
+        vf[2 * i] = h2f(vw[i]);
+        vf[2 * i + 1] = h2f(vw[i] >> 16);
+      }
+      float e[G], cr[G];
+      bool grew = false;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(qr[j][i], kf[i], s);
+        s = group_sum16(s, 16);
+        if constexpr (LPT == 32) s += __shfl_xor(s, 16, 64);
+        const float mn = valid ? fmaxf(st.m[j], s) : st.m[j];
+        cr[j] = (mn == st.m[j]) ? 1.0f : __builtin_amdgcn_exp2f(st.m[j] - mn);  // m = -inf: exp2(-inf) = 0
+        grew |= mn != st.m[j];
+        e[j] = valid ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
+        st.m[j] = mn;
+        st.l[j] = fmaf(st.l[j], cr[j], e[j]);
+      }
+      if (__builtin_amdgcn_ballot_w64(grew)) {  // wave-uniform: rescale only when some maximum grew
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) st.acc[j][i] *= cr[j];
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[j][i] = fmaf(e[j], vf[i], st.acc[j][i]);
+    }
+  }
+
+  // Merge the token slots of the wave (lanes with the same dimensions).
+#pragma unroll
+  for (int x = LPT; x < 64; x <<= 1) {
+    float mb[G], lb[G], ob[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      mb[j] = __shfl_xor(st.m[j], x, 64);
+      lb[j] = __shfl_xor(st.l[j], x, 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[j][i] = __shfl_xor(st.acc[j][i], x, 64);
+    }
+    merge_into<G>(st, mb, lb, ob);
+  }
+  // Merge the waves through LDS (wave order fixed), then write.
+  if (lane < LPT) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (lane == 0) {
+        red[wid][j][0] = st.m[j];
+        red[wid][j][1] = st.l[j];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wid][j][2 + 8 * dl + i] = st.acc[j][i];
+    }
+  }
+  __syncthreads();
+  if (wid != 0 || lane >= LPT) return;
+#pragma unroll
+  for (int w = 1; w < kAttnWaves; ++w) {
+    float mb[G], lb[G], ob[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      mb[j] = red[w][j][0];
+      lb[j] = red[w][j][1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[j][i] = red[w][j][2 + 8 * dl + i];
+    }
+    merge_into<G>(st, mb, lb, ob);
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int64_t h = (int64_t)kvh * G + j;
+    if (nchunks == 1) {
+      const float inv = 1.0f / st.l[j];
+      float4* op = reinterpret_cast<float4*>(out + h * D + 8 * dl);
+      op[0] = make_float4(st.acc[j][0] * inv, st.acc[j][1] * inv, st.acc[j][2] * inv, st.acc[j][3] * inv);
+      op[1] = make_float4(st.acc[j][4] * inv, st.acc[j][5] * inv, st.acc[j][6] * inv, st.acc[j][7] * inv);
+    } else {
+      if (dl == 0) {
+        pm[h * nchunks + c] = st.m[j];
+        pl[h * nchunks + c] = st.l[j];
+      }
+      float4* op = reinterpret_cast<float4*>(po + (h * nchunks + c) * D + 8 * dl);
+      op[0] = make_float4(st.acc[j][0], st.acc[j][1], st.acc[j][2], st.acc[j][3]);
+      op[1] = make_float4(st.acc[j][4], st.acc[j][5], st.acc[j][6], st.acc[j][7]);
+    }
+  }
+}
+
+// grid = n_heads; block = D threads, one output dimension each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
+                                                         const float* __restrict__ po, float* __restrict__ out,
+                                                         int nchunks) {
+  const int64_t h = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* m = pm + h * nchunks;
+  const float* l = pl + h * nchunks;
+  float M = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, m[c]);
+  float L = 0.0f, o = 0.0f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float w = m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[c] - M);
+    L = fmaf(l[c], w, L);
+    o = fmaf(po[(h * nchunks + c) * D + d], w, o);
+  }
+  out[h * D + d] = o / L;
+}
+
+template <int D, int G>
+hipError_t launch_dg(const AttnShape& a, const AttnPlan& pl, const float* q, const uint16_t* k, const uint16_t* v,
+                     float* out, void* ws, hipStream_t s) {
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
+  float* pm = nullptr;
+  float* plv = nullptr;
+  float* po = nullptr;
+  if (pl.nchunks > 1) {  // workspace: o partials [n_heads, nchunks, D], then m and l [n_heads, nchunks]
+    po = static_cast<float*>(ws);
+    pm = po + (int64_t)a.n_heads * pl.nchunks * D;
+    plv = pm + (int64_t)a.n_heads * pl.nchunks;
+  }
+  hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3((unsigned)pl.nchunks, (unsigned)a.n_kv),
+                     dim3(kAttnWaves * 64), 0, s, q, k, v, out, pm, plv, po, a.n_ctx, pl.chunk,
+                     (int)pl.nchunks, qscale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nchunks == 1) return e;
+  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)a.n_heads), dim3(D), 0, s, pm, plv, po, out,
+                     (int)pl.nchunks);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnShape& a, const AttnPlan& pl, const float* q, const uint16_t* k, const uint16_t* v,
+                    float* out, void* ws, hipStream_t s) {
+  switch (a.n_heads / a.n_kv) {
+    case 1: return launch_dg<D, 1>(a, pl, q, k, v, out, ws, s);
+    case 2: return launch_dg<D, 2>(a, pl, q, k, v, out, ws, s);
+    case 4: return launch_dg<D, 4>(a, pl, q, k, v, out, ws, s);
+    case 8: return launch_dg<D, 8>(a, pl, q, k, v, out, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int device_cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+}  // namespace
+
+bool attn_supported(const AttnShape& a) {
+  if (a.head_dim != 128 && a.head_dim != 256) return false;
+  if (a.n_kv < 1 || a.n_heads < a.n_kv || a.n_heads % a.n_kv) return false;
+  const int g = a.n_heads / a.n_kv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return false;
+  if (a.n_kv > 65535) return false;
+  // Byte offsets inside one head's cache are 32-bit.
+  return a.n_ctx >= 1 && a.n_ctx * a.head_dim * 2 + 4096 < ((int64_t)1 << 31);
+}
+
+AttnPlan attn_plan(const AttnShape& a) {
+  // Tokens one workgroup iteration covers; a chunk is a whole number of them.
+  const int64_t step = (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
+  const int64_t min_chunk = step * kAttnBatch;
+  // Enough chunks for two workgroups per CU, none shorter than one batched
+  // iteration of the workgroup.
+  const int64_t want = ((int64_t)device_cu_count() * 2 + a.n_kv - 1) / a.n_kv;
+  int64_t nch = (a.n_ctx + min_chunk - 1) / min_chunk;
+  if (nch > want) nch = want;
+  if (nch < 1) nch = 1;
+  int64_t chunk = (a.n_ctx + nch - 1) / nch;
+  chunk = (chunk + step - 1) / step * step;
+  AttnPlan p;
+  p.chunk = chunk;
+  p.nchunks = (a.n_ctx + chunk - 1) / chunk;
+  return p;
+}
+
+size_t attn_workspace_bytes(const AttnShape& a) {
+  const AttnPlan p = attn_plan(a);
+  if (p.nchunks <= 1) return 0;
+  return (size_t)a.n_heads * (size_t)p.nchunks * (2 + (size_t)a.head_dim) * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnShape& a, const float* q, const uint16_t* k, const uint16_t* v, float* out,
+                       void* ws, hipStream_t s) {
+  if (!attn_supported(a)) return hipErrorInvalidValue;
+  const AttnPlan p = attn_plan(a);
+  return a.head_dim == 128 ? launch_d<128>(a, p, q, k, v, out, ws, s) : launch_d<256>(a, p, q, k, v, out, ws, s);
+}
+
+}  // namespace qg

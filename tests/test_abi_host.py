@@ -1,5 +1,5 @@
 """Host-only checks of the C ABI (no GPU needed): the library loads, exports
-every function include/qgemv.h declares, the descriptor layout matches the
+every function include/qgemv.h and include/qattn.h declare, the descriptor layout matches the
 binding, and every validation error is reported before anything touches the
 device."""
 import ctypes
@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qgemv.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "qattn.h")]
 
 qg = pytest.importorskip("block_quant_gemv_amd", reason="libqgemv.so not built")
 lib = qg._lib
@@ -20,14 +21,17 @@ OK, EINVAL, EFORMAT, ESHAPE, EALIGN, EWORKSPACE, EVERSION, EHIP = 0, -1, -2, -3,
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert len(names) >= 12
+    assert len(names) >= 14 and "qattn_decode" in names and "qattn_workspace_size" in names
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", qg.lib_path()], capture_output=True, text=True).stdout
@@ -155,3 +159,26 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(g.weight_bytes(), dtype=torch.uint8)
     with pytest.raises(ValueError):
         g.run(w, torch.zeros(1, 256))
+
+
+def test_attention_validation_before_launch():
+    sz = ctypes.c_size_t()
+    # supported shapes: head_dim 128/256, heads/kv_heads in {1, 2, 4, 8}
+    assert lib.qattn_workspace_size(16, 2, 256, 32768, ctypes.byref(sz)) == OK and sz.value > 0
+    assert lib.qattn_workspace_size(16, 2, 256, 8, ctypes.byref(sz)) == OK and sz.value == 0  # one chunk
+    assert lib.qattn_workspace_size(16, 2, 64, 100, ctypes.byref(sz)) == ESHAPE
+    assert lib.qattn_workspace_size(12, 8, 128, 100, ctypes.byref(sz)) == ESHAPE
+    assert lib.qattn_workspace_size(48, 3, 128, 100, ctypes.byref(sz)) == ESHAPE  # group of 16
+    assert lib.qattn_workspace_size(16, 2, 256, 0, ctypes.byref(sz)) == ESHAPE
+    assert lib.qattn_workspace_size(16, 2, 256, 1 << 22, ctypes.byref(sz)) == ESHAPE  # 32-bit offsets
+    assert lib.qattn_workspace_size(16, 2, 256, 100, None) == EINVAL
+    a = 1 << 20  # fake, never dereferenced: every call below fails validation
+    assert lib.qattn_decode(None, a, a, a, 16, 2, 256, 100, a, 1 << 30, None) == EINVAL
+    assert lib.qattn_decode(a, a, a, a, 16, 2, 200, 100, a, 1 << 30, None) == ESHAPE
+    assert lib.qattn_decode(a + 4, a, a, a, 16, 2, 256, 100, a, 1 << 30, None) == EALIGN
+    assert lib.qattn_decode(a, a, a + 8, a, 16, 2, 256, 100, a, 1 << 30, None) == EALIGN
+    assert lib.qattn_workspace_size(16, 2, 256, 4096, ctypes.byref(sz)) == OK
+    assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, a, sz.value - 1, None) == EWORKSPACE
+    assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, None, sz.value, None) == EINVAL
+    assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, a + 16, sz.value, None) == EALIGN
+    assert b"workspace" in lib.qgemv_last_error() or b"ws" in lib.qgemv_last_error()
