@@ -12,8 +12,10 @@ enough copies (> 2 GiB) that every step reads them from HBM, not from the
 Also reported (same run, after the timed region): microseconds per fused
 FFN sublayer (hidden 4096, intermediate 12288, Q4_K gate|up + Q6_K down),
 the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV, the Q5_K and
-IQ4_XS GEMVs (4096 -> 12288) and the MoE layer (256 experts, top-8 + shared,
-hidden 2048, intermediate 512) at M=1 and M=16.
+IQ4_XS GEMVs (4096 -> 12288), the MoE layer (256 experts, top-8 + shared,
+hidden 2048, intermediate 512) at M=1 and M=16, and the two-stage decode
+attention (16 query heads, 2 key/value heads, dimension 256) at 4K and 32K
+cached tokens.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -462,6 +464,25 @@ def extras(qg, synth, torch):
         us = time_graph(gm, R, reps=16)
         res[f"moe_m{m}_us"] = round(us, 3)
         log(f"moe m={m}: {us:.2f} us")
+    del GU, DN
+    # Two-stage decode attention, 16 query heads over 2 key/value heads of
+    # dimension 256, fp16 KV cache, at 4K and 32K cached tokens
+    hq, hkv, d = 16, 2, 256
+    at = qg.Attention(hq, hkv, d)
+    for t in (4096, 32768):
+        q, k, v = synth.attention_inputs(350, hq, hkv, d, t)
+        b = 2 * k.nbytes
+        R = copies_for(b, cap=64)
+        Ks, Vs = rotated(k, R), rotated(v, R)
+        qd = dev(q)
+        o = torch.empty((hq, d), dtype=torch.float32, device="cuda")
+        ws = at.workspace(t)
+        ga = graph_of(lambda i: at.run(qd, Ks[i % R], Vs[i % R], out=o, ws=ws), R)
+        us = time_graph(ga, R, reps=max(2, 64 // R))
+        res[f"attn_{t}_us"] = round(us, 3)
+        res[f"attn_{t}_kv_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+        log(f"attention {hq}/{hkv}x{d} ctx {t}: {us:.2f} us, {res[f'attn_{t}_kv_gbps']} GB/s of KV cache")
+        del Ks, Vs
     return res
 
 

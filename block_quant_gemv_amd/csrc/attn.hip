@@ -15,13 +15,16 @@
 // sum_t exp(s_t - m) v_t. Keys and values are read once per group of G
 // heads. A token's row of D fp16 values is spread over D/8 lanes, 16 bytes
 // each, so one 128-bit load instruction of a wave reads 1 KB of consecutive
-// tokens; the lanes of a token add their partial dot products with DPP and
-// one cross-row exchange, and each lane keeps the running state for its 8
+// tokens; the lanes of a token add their partial dot products with DPP adds
+// and one cross-row swap, and each lane keeps the running state for its 8
 // dimensions. Scores are kept in base 2 (q pre-scaled by log2(e)/sqrt(D)),
-// so every exponential is one v_exp_f32.
+// so every exponential is one v_exp_f32, and the running maximum is a lazy
+// reference (moved only when a score exceeds it by 2^8), so most tokens cost
+// one exponential per head and no rescaling.
 //
 // Stage 2 (attn_merge_kernel): per query head, M = max_c m_c,
-// L = sum_c l_c 2^(m_c - M), o = sum_c 2^(m_c - M) o_c / L.
+// L = sum_c l_c 2^(m_c - M), o = sum_c 2^(m_c - M) o_c / L, with the
+// dimensions split over workgroups and the chunks over four waves.
 //
 // With a single chunk stage 1 normalises and writes o itself.
 #include "attn.h"
@@ -32,10 +35,34 @@ namespace qg {
 namespace {
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnBatch = 4;          // token iterations whose loads are issued together
+constexpr int kAttnBatch = 2;          // token iterations whose loads are issued together (double-buffered)
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
 
 QG_DEV float h2f(uint32_t bits) { return half_bits(bits & 0xffffu); }
+
+// How far (base 2) a score may exceed a head's reference maximum before the
+// running sums are rescaled to a new maximum.
+constexpr float kTau = 8.0f;
+
+template <int CTRL>
+QG_DEV float dppf(float v) {  // bound_ctrl set: every lane's partner exists, lets the add take the DPP operand
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+// Sum over each row of 16 lanes, in every lane of the row: quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+QG_DEV float row_sum16(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+// Rows 2i and 2i+1 hold row sums; every lane of both gets their total
+// (v_permlane16_swap exchanges the odd rows of one copy with the even rows of
+// the other, so the two results hold row 2i and row 2i+1 in every lane).
+QG_DEV float pair_rows_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Running softmax state of one lane for G heads and its 8 dimensions.
 template <int G>
@@ -61,7 +88,7 @@ QG_DEV void merge_into(AState<G>& a, const float (&mb)[G], const float (&lb)[G],
 // D: head dimension (128 or 256); G: query heads per key/value head.
 // grid = (nchunks, n_kv); block = 4 waves.
 template <int D, int G>
-__global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_kernel(
     const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po,
     int64_t n_ctx, int64_t chunk, int nchunks, float qscale) {
@@ -107,8 +134,58 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
   const int64_t t0 = (int64_t)c * chunk;
   const int64_t t1 = (t0 + chunk) < n_ctx ? (t0 + chunk) : n_ctx;
   constexpr int kStep = kAttnWaves * TPW;  // tokens per iteration of the whole workgroup
-  for (int64_t tb = t0 + (int64_t)wid * TPW; tb < t1; tb += (int64_t)kStep * kAttnBatch) {
-    u32x4 kb[kAttnBatch], vb[kAttnBatch];
+
+  // One token per lane group: scores of the G heads (sum over the LPT lanes
+  // of the token), then the lazily rescaled online softmax: the reference
+  // maximum m of a head only moves when a score exceeds it by more than
+  // kTau (base 2), so the common step is e = 2^(s - m), l += e,
+  // acc += e * v, and the rescale is a rare wave-uniform branch.
+  auto token = [&](const u32x4& kb, const u32x4& vb, bool valid) __attribute__((always_inline)) {
+    const uint32_t kw[4] = {kb.x, kb.y, kb.z, kb.w};
+    const uint32_t vw[4] = {vb.x, vb.y, vb.z, vb.w};
+    float kf[8], vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kf[2 * i] = h2f(kw[i]);
+      kf[2 * i + 1] = h2f(kw[i] >> 16);
+      vf[2 * i] = h2f(vw[i]);
+      vf[2 * i + 1] = h2f(vw[i] >> 16);
+    }
+    float sc[G];
+    bool big = false;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float x = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x = fmaf(qr[j][i], kf[i], x);
+      x = row_sum16(x);
+      if constexpr (LPT == 32) x = pair_rows_sum(x);
+      sc[j] = valid ? x : -INFINITY;
+      big |= sc[j] > st.m[j] + kTau;  // m = -inf: any valid score
+    }
+    if (__builtin_amdgcn_ballot_w64(big)) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float mn = fmaxf(st.m[j], sc[j]);
+        const float cr = mn == st.m[j] ? 1.0f : __builtin_amdgcn_exp2f(st.m[j] - mn);  // exp2(-inf) = 0
+        st.m[j] = mn;
+        st.l[j] *= cr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[j][i] *= cr;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float e = valid ? __builtin_amdgcn_exp2f(sc[j] - st.m[j]) : 0.0f;
+      st.l[j] += e;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st.acc[j][i] = fmaf(e, vf[i], st.acc[j][i]);
+    }
+  };
+
+  // Batches of kAttnBatch token loads per lane, double-buffered: the next
+  // batch is requested before the current one is processed.
+  auto fetch = [&](u32x4 (&kb)[kAttnBatch], u32x4 (&vb)[kAttnBatch], int64_t tb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kAttnBatch; ++u) {
       const int64_t t = tb + (int64_t)u * kStep + slot;
@@ -116,78 +193,40 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
       kb[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 2);
       vb[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 2);
     }
+  };
+  auto consume = [&](const u32x4 (&kb)[kAttnBatch], const u32x4 (&vb)[kAttnBatch], int64_t tb)
+                     __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kAttnBatch; ++u) {
-      const int64_t t = tb + (int64_t)u * kStep + slot;
-      const bool valid = t < t1;
-      float kf[8], vf[8];
-      const uint32_t kw[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
-      const uint32_t vw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kf[2 * i] = h2f(kw[i]);
-        kf[2 * i + 1] = h2f(kw[i] >> 16);
-        vf[2 * i] = h2f(vw[i]);
-        vf[2 * i + 1] = h2f(vw[i] >> 16);
-      }
-      float e[G], cr[G];
-      bool grew = false;
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s = fmaf(qr[j][i], kf[i], s);
-        s = group_sum16(s, 16);
-        if constexpr (LPT == 32) s += __shfl_xor(s, 16, 64);
-        const float mn = valid ? fmaxf(st.m[j], s) : st.m[j];
-        cr[j] = (mn == st.m[j]) ? 1.0f : __builtin_amdgcn_exp2f(st.m[j] - mn);  // m = -inf: exp2(-inf) = 0
-        grew |= mn != st.m[j];
-        e[j] = valid ? __builtin_amdgcn_exp2f(s - mn) : 0.0f;
-        st.m[j] = mn;
-        st.l[j] = fmaf(st.l[j], cr[j], e[j]);
-      }
-      if (__builtin_amdgcn_ballot_w64(grew)) {  // wave-uniform: rescale only when some maximum grew
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) st.acc[j][i] *= cr[j];
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st.acc[j][i] = fmaf(e[j], vf[i], st.acc[j][i]);
-    }
+    for (int u = 0; u < kAttnBatch; ++u) token(kb[u], vb[u], tb + (int64_t)u * kStep + slot < t1);
+  };
+  constexpr int64_t kBatchTokens = (int64_t)kStep * kAttnBatch;
+  u32x4 kA[kAttnBatch], vA[kAttnBatch], kB[kAttnBatch], vB[kAttnBatch];
+  int64_t tb = t0 + (int64_t)wid * TPW;
+  if (tb < t1) fetch(kA, vA, tb);
+  while (tb < t1) {
+    if (tb + kBatchTokens < t1) fetch(kB, vB, tb + kBatchTokens);
+    consume(kA, vA, tb);
+    tb += kBatchTokens;
+    if (tb >= t1) break;
+    if (tb + kBatchTokens < t1) fetch(kA, vA, tb + kBatchTokens);
+    consume(kB, vB, tb);
+    tb += kBatchTokens;
   }
 
-  // Merge the token slots of the wave (lanes with the same dimensions).
-#pragma unroll
-  for (int x = LPT; x < 64; x <<= 1) {
-    float mb[G], lb[G], ob[G][8];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      mb[j] = __shfl_xor(st.m[j], x, 64);
-      lb[j] = __shfl_xor(st.l[j], x, 64);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ob[j][i] = __shfl_xor(st.acc[j][i], x, 64);
-    }
-    merge_into<G>(st, mb, lb, ob);
-  }
-  // Merge the waves through LDS (wave order fixed), then write.
-  if (lane < LPT) {
+  // Merge through LDS in a fixed order: first the token slots of each wave
+  // into slot 0 (one slot per round), then waves 1..3 into wave 0.
+  auto put = [&](int w) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      if (lane == 0) {
-        red[wid][j][0] = st.m[j];
-        red[wid][j][1] = st.l[j];
+      if (dl == 0) {
+        red[w][j][0] = st.m[j];
+        red[w][j][1] = st.l[j];
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[wid][j][2 + 8 * dl + i] = st.acc[j][i];
+      for (int i = 0; i < 8; ++i) red[w][j][2 + 8 * dl + i] = st.acc[j][i];
     }
-  }
-  __syncthreads();
-  if (wid != 0 || lane >= LPT) return;
-#pragma unroll
-  for (int w = 1; w < kAttnWaves; ++w) {
+  };
+  auto take = [&](int w) __attribute__((always_inline)) {
     float mb[G], lb[G], ob[G][8];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -197,7 +236,19 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
       for (int i = 0; i < 8; ++i) ob[j][i] = red[w][j][2 + 8 * dl + i];
     }
     merge_into<G>(st, mb, lb, ob);
+  };
+#pragma unroll 1
+  for (int sl = 1; sl < TPW; ++sl) {
+    if (slot == sl) put(wid);
+    __syncthreads();
+    if (slot == 0) take(wid);
+    __syncthreads();
   }
+  if (slot == 0) put(wid);
+  __syncthreads();
+  if (wid != 0 || slot != 0) return;
+#pragma unroll 1
+  for (int w = 1; w < kAttnWaves; ++w) take(w);
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const int64_t h = (int64_t)kvh * G + j;
@@ -218,24 +269,80 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_partial_kernel(
   }
 }
 
-// grid = n_heads; block = D threads, one output dimension each.
+// grid = (n_heads, D / 64); block = 4 waves. The chunk maxima and sums are
+// read with vector loads by all threads: M = max_c m_c and the chunk weights
+// w_c = 2^(m_c - M) go to LDS, L = sum_c w_c l_c. Then wave g adds
+// w_c o_c[d] over chunks c = g, g + 4, ... for the 64 dimensions of this
+// block (one per lane, up to 16 loads in flight), and wave 0 adds the four
+// sums in wave order.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeUnroll = 16;
+constexpr int kMaxChunks = 1024;
+
+QG_DEV float block_reduce(float v, float* sh, bool is_max) {
+  // every thread gets the result; sh holds kMergeWaves floats
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kMergeWaves; ++i) r = is_max ? fmaxf(r, sh[i]) : r + sh[i];
+  return r;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
-                                                         const float* __restrict__ po, float* __restrict__ out,
-                                                         int nchunks) {
+__global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(const float* __restrict__ pm,
+                                                                    const float* __restrict__ pl,
+                                                                    const float* __restrict__ po,
+                                                                    float* __restrict__ out, int nchunks) {
+  __shared__ float wts[kMaxChunks];
+  __shared__ float red[kMergeWaves][64];
+  __shared__ float sh[kMergeWaves];
   const int64_t h = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const float* m = pm + h * nchunks;
   const float* l = pl + h * nchunks;
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, m[c]);
-  float L = 0.0f, o = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float w = m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[c] - M);
-    L = fmaf(l[c], w, L);
-    o = fmaf(po[(h * nchunks + c) * D + d], w, o);
+  for (int c = tid; c < nchunks; c += kMergeWaves * 64) M = fmaxf(M, m[c]);
+  M = block_reduce(M, sh, true);
+  float Lp = 0.0f;
+  for (int c = tid; c < nchunks; c += kMergeWaves * 64) {
+    const float wt = m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[c] - M);
+    wts[c] = wt;
+    Lp = fmaf(l[c], wt, Lp);
   }
-  out[h * D + d] = o / L;
+  const float L = block_reduce(Lp, sh, false);  // its barriers also publish wts
+  const int d = blockIdx.y * 64 + lane;
+  const float* o = po + h * nchunks * D + d;
+  float acc = 0.0f;
+  for (int c0 = w; c0 < nchunks; c0 += kMergeWaves * kMergeUnroll) {
+    float x[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int c = c0 + u * kMergeWaves;
+      x[u] = c < nchunks ? o[(int64_t)c * D] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int c = c0 + u * kMergeWaves;
+      if (c < nchunks) acc = fmaf(x[u], wts[c], acc);
+    }
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+  float oo = red[0][lane];
+#pragma unroll
+  for (int v = 1; v < kMergeWaves; ++v) oo += red[v][lane];
+  out[h * D + d] = oo / L;
 }
 
 template <int D, int G>
@@ -255,8 +362,8 @@ hipError_t launch_dg(const AttnShape& a, const AttnPlan& pl, const float* q, con
                      (int)pl.nchunks, qscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nchunks == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)a.n_heads), dim3(D), 0, s, pm, plv, po, out,
-                     (int)pl.nchunks);
+  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)a.n_heads, D / 64), dim3(kMergeWaves * 64), 0, s, pm,
+                     plv, po, out, (int)pl.nchunks);
   return hipGetLastError();
 }
 
@@ -298,10 +405,11 @@ bool attn_supported(const AttnShape& a) {
 AttnPlan attn_plan(const AttnShape& a) {
   // Tokens one workgroup iteration covers; a chunk is a whole number of them.
   const int64_t step = (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
-  const int64_t min_chunk = step * kAttnBatch;
-  // Enough chunks for two workgroups per CU, none shorter than one batched
-  // iteration of the workgroup.
-  const int64_t want = ((int64_t)device_cu_count() * 2 + a.n_kv - 1) / a.n_kv;
+  const int64_t min_chunk = step * kAttnBatch * 2;
+  // Enough chunks for two workgroups per CU (at most kMaxChunks), none
+  // shorter than two batched iterations of the workgroup.
+  int64_t want = ((int64_t)device_cu_count() * 2 + a.n_kv - 1) / a.n_kv;
+  if (want > kMaxChunks) want = kMaxChunks;
   int64_t nch = (a.n_ctx + min_chunk - 1) / min_chunk;
   if (nch > want) nch = want;
   if (nch < 1) nch = 1;
