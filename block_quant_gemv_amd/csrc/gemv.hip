@@ -148,12 +148,19 @@ struct FmtQ8_0 {
 // 4 codebook indices (one per byte, 0..15) -> 4 int8 codebook values.
 // Entries 0..7 come from {cb1:cb0}, 8..15 from {cb3:cb2}; bit 3 of each
 // index then picks between the two candidates with a third byte permute.
-QG_DEV uint32_t cb_lookup4(uint32_t idx, const uint32_t* cb) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t lo = perm(cb[1], cb[0], sel);
-  const uint32_t hi = perm(cb[3], cb[2], sel);
-  const uint32_t pick = ((idx >> 1) & 0x04040404u) | 0x03020100u;
-  return perm(hi, lo, pick);
+// cb[4] holds the identity selector 0x03020100 in a register, so the pick
+// is one and-or (a register operand instead of a second literal).
+// b3 holds bit 3 of each index at bit 2 of its byte (any other bits of b3
+// are ignored).
+QG_DEV uint32_t cb_lookup4(uint32_t sel7, uint32_t b3, const uint32_t* cb) {
+  const uint32_t lo = perm(cb[1], cb[0], sel7);
+  const uint32_t hi = perm(cb[3], cb[2], sel7);
+  return perm(hi, lo, (b3 & 0x04040404u) | cb[4]);
+}
+// The 8 indices of one dword of packed nibbles (low nibbles, then high).
+QG_DEV void cb_lookup8(uint32_t q, const uint32_t* cb, uint32_t& vlo, uint32_t& vhi) {
+  vlo = cb_lookup4(q & 0x07070707u, q >> 1, cb);
+  vhi = cb_lookup4((q >> 4) & 0x07070707u, q >> 5, cb);
 }
 
 struct FmtIQ4_NL {
@@ -165,10 +172,7 @@ struct FmtIQ4_NL {
     w.d = half_bits(lds_u16(t, off));
     lds_read_unaligned<4>(t, off + 2, q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w.v[i] = cb_lookup4(q[i] & 0x0F0F0F0Fu, cb);
-      w.v[4 + i] = cb_lookup4((q[i] >> 4) & 0x0F0F0F0Fu, cb);
-    }
+    for (int i = 0; i < 4; ++i) cb_lookup8(q[i], cb, w.v[i], w.v[4 + i]);
     return w;
   }
   QG_DEV static int idot(const W& w, const Act& a) {
@@ -276,10 +280,7 @@ struct FmtIQ4_XS {
     const uint2 qb = *reinterpret_cast<const uint2*>(t + off + 16 + 16 * g);
     const uint32_t q[4] = {qa.x, qa.y, qb.x, qb.y};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w.v[i] = cb_lookup4(q[i] & 0x0F0F0F0Fu, cb);
-      w.v[4 + i] = cb_lookup4((q[i] >> 4) & 0x0F0F0F0Fu, cb);
-    }
+    for (int i = 0; i < 4; ++i) cb_lookup8(q[i], cb, w.v[i], w.v[4 + i]);
     const uint32_t ls = ((h.y >> (4 * g)) & 0xFu) | (((h.x >> (16 + 2 * g)) & 3u) << 4);
     w.ds = half_bits(h.x & 0xffffu) * (float)((int)ls - 32);
     return w;
@@ -594,6 +595,13 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
                                      FUSEQ && p.xq_out && blockIdx.x == 0 && (!p.tbl || shared), pre);
   __syncthreads();
 
+  // Codebook words plus the identity byte selector, pinned in registers
+  // (opaque values): the byte permutes and the pick's and-or then take them
+  // as register operands without re-copying them from scalar registers.
+  uint32_t cbr[5] = {p.cb[0], p.cb[1], p.cb[2], p.cb[3], 0x03020100u};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+
   float acc[P][MT];
 #pragma unroll
   for (int a = 0; a < P; ++a)
@@ -637,7 +645,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
         for (int pp = 0; pp < P; ++pp) {
           int rl = pp * RPP + rho;
           rl = rl < nrows ? rl : nrows - 1;
-          wv[pp] = F::load(tile, base + (uint32_t)(rl * g.rb) + uoff, sub, p.cb);
+          wv[pp] = F::load(tile, base + (uint32_t)(rl * g.rb) + uoff, sub, cbr);
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
