@@ -128,3 +128,62 @@ def test_reconstruction_error_bound():
     err = np.abs(x.astype(np.float64) - dequantize_q8(q, d))
     bound = np.repeat(d.astype(np.float64), 32, axis=1) * (0.5 + 1e-6)
     assert np.all(err <= bound)
+
+
+# ---- 16-bit variant (scale = absmax / 32767, int16 codes) ----
+
+from oracle.quant import quantize_s16  # noqa: E402
+
+
+def test_s16_ties_round_half_away_from_zero():
+    # absmax 32767 makes d = 1 exactly, so v = x.
+    x = _block([32767.0, 2.5, -2.5, 0.5, -0.5, 1.5, 32766.5, -32766.5, np.float32(0.49999997), 3.5])
+    q, d, s = quantize_s16(x)
+    assert q.dtype == np.int16 and d[0, 0] == np.float32(1.0)
+    assert list(q[0, :10]) == [32767, 3, -3, 1, -1, 2, 32767, -32767, 0, 4]
+    assert s[0, 0] == int(q[0].astype(np.int64).sum())
+
+
+@pytest.mark.parametrize("e", [-20, 0, 7])
+def test_s16_power_of_two_round_trip(e):
+    rng = np.random.default_rng(e + 300)
+    qi = rng.integers(-32767, 32768, size=(2, 64))
+    qi[:, ::32] = 32767
+    x = (qi * 2.0 ** e).astype(np.float32)
+    q, d, s = quantize_s16(x)
+    assert np.all(d == np.float32(2.0 ** e))
+    assert np.array_equal(q.astype(np.int64), qi)
+    assert np.array_equal(s.astype(np.int64), qi.reshape(2, 2, 32).sum(-1))
+
+
+def test_s16_zero_block_and_exact_rationals():
+    q, d, s = quantize_s16(np.zeros((1, 32), np.float32))
+    assert np.all(q == 0) and d[0, 0] == 0 and s[0, 0] == 0
+    # The exact-rational restatement above (binary32 rounding of the scale
+    # and of every quotient), with 32767 in place of 127.
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        x = (rng.standard_normal(32) * 10.0 ** rng.integers(-3, 4)).astype(np.float32)
+        q, d, s = quantize_s16(x[None])
+        a = max(abs(Fraction(float(v))) for v in x)
+        dd = _fp32_round(a / 32767)
+        assert Fraction(float(d[0, 0])) == dd
+        for i, v in enumerate(x):
+            t = _fp32_round(Fraction(float(v)) / dd) if v != 0 else Fraction(0)
+            want = int(math.copysign(math.floor(abs(t) + Fraction(1, 2)), t))
+            want = max(-32767, min(32767, want))
+            assert int(q[0, i]) == want
+
+
+def test_s16_step_is_256_times_finer_and_error_bound():
+    # The page's ledger reports a 256x smaller quantization step: the scale
+    # ratio is 127 / 32767 (about 1/258), and |x - d q| <= d / 2 holds.
+    x = np.random.default_rng(8).standard_normal((4, 256)).astype(np.float32)
+    q8, d8, _ = quantize_q8(x)
+    q16, d16, _ = quantize_s16(x)
+    ratio = d8.astype(np.float64) / d16.astype(np.float64)
+    assert np.allclose(ratio, 32767 / 127, rtol=1e-6)
+    err = np.abs(x.astype(np.float64) - dequantize_q8(q16, d16))
+    assert np.all(err <= np.repeat(d16.astype(np.float64), 32, axis=1) / 2 * (1 + 1e-6))
+    err8 = np.abs(x.astype(np.float64) - dequantize_q8(q8, d8))
+    assert err.max() * 200 < err8.max()
