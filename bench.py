@@ -12,7 +12,8 @@ enough copies (> 2 GiB) that every step reads them from HBM, not from the
 Also reported (same run, after the timed region): microseconds per fused
 FFN sublayer (hidden 4096, intermediate 12288, Q4_K gate|up + Q6_K down),
 the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV, the Q5_K and
-IQ4_XS GEMVs (4096 -> 12288), the MoE layer (256 experts, top-8 + shared,
+IQ4_XS GEMVs (4096 -> 12288), the Q4_K GEMV with 16-bit activations
+(4096 -> 12288), the MoE layer (256 experts, top-8 + shared,
 hidden 2048, intermediate 512) at M=1 and M=16, and the two-stage decode
 attention (16 query heads, 2 key/value heads, dimension 256) at 4K and 32K
 cached tokens.
@@ -429,6 +430,21 @@ def extras(qg, synth, torch):
         res[f"{fmt}_{k}x{n}_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
         log(f"{fmt} {k}x{n}: {us:.2f} us, {res[f'{fmt}_{k}x{n}_gbps']} GB/s")
         del Ws
+    # 16-bit activations (Q4_K, K = 4096, N = 12288), full qgemv_run_s16 calls
+    n, k = 12288, 4096
+    g = qg.GEMV("q4_k", n, k)
+    b = n * synth.row_bytes("q4_k", k)
+    R = copies_for(b, cap=64)
+    Ws = rotated(synth.weights("q4_k", n, k, seed=335), R)
+    x = dev(synth.activations(336, 1, k))
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    ws16 = g.workspace_s16()
+    gg = graph_of(lambda i: g.run_s16(Ws[i % R], x, y=y, ws=ws16), R)
+    us = time_graph(gg, R, reps=4)
+    res[f"s16_q4_k_{k}x{n}_us"] = round(us, 3)
+    res[f"s16_q4_k_{k}x{n}_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+    log(f"s16 q4_k {k}x{n}: {us:.2f} us, {res[f's16_q4_k_{k}x{n}_gbps']} GB/s")
+    del Ws
     # M=32 batched GEMMs on int8 MFMA (Q4_K 4096 -> 12288, Q6_K 12288 -> 4096)
     for fmt, n, k in (("q4_k", 12288, 4096), ("q6_k", 4096, 12288)):
         g = qg.GEMV(fmt, n, k, max_m=32)

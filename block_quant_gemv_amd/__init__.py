@@ -14,7 +14,7 @@ import os
 
 import torch  # loads torch's HIP runtime first; the library then binds to it
 
-__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "lib_path", "LAYOUT_VERSION"]
+__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "debug_quantize_s16", "lib_path", "LAYOUT_VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libqgemv.so")
@@ -65,9 +65,14 @@ _lib.qgemv_status_string.restype = ctypes.c_char_p
 _lib.qgemv_last_error.restype = ctypes.c_char_p
 _lib.qgemv_debug_quantize.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, ctypes.c_size_t, _vp]
+_lib.qgemv_workspace_size_s16.argtypes = [_vp, ctypes.POINTER(_sz)]
+_lib.qgemv_run_s16.argtypes = [_vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.qgemv_debug_quantize_s16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
+_lib.qgemv_debug_block_dots_s16.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
 _lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
-for _f in ("qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
+for _f in ("qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
+           "qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -219,6 +224,37 @@ class GEMV(_Plan):
                "qgemv_run_quantized")
         return y
 
+    def workspace_size_s16(self) -> int:
+        b = _sz()
+        _check(_lib.qgemv_workspace_size_s16(self._h, ctypes.byref(b)), "qgemv_workspace_size_s16")
+        return b.value
+
+    def workspace_s16(self, device="cuda") -> torch.Tensor:
+        return torch.empty(self.workspace_size_s16(), dtype=torch.uint8, device=device)
+
+    def run_s16(self, w, x, y=None, ws=None, stream=None):
+        """One token with 16-bit activation codes (qgemv_run_s16)."""
+        if x.numel() != self.k:
+            raise ValueError(f"x must hold one token of {self.k} values")
+        if y is None:
+            y = torch.empty((1, self.n), dtype=torch.float32, device=x.device)
+        if y.numel() != self.n:
+            raise ValueError("y has the wrong size")
+        if ws is None:
+            ws = self.workspace_s16(x.device)
+        _check(_lib.qgemv_run_s16(self._h, self._check_w(w, 0, "w"), _dev(x, torch.float32, "x"),
+                                  _dev(y, torch.float32, "y"), _dev(ws, torch.uint8, "ws"), ws.numel(),
+                                  _stream(stream)), "qgemv_run_s16")
+        return y
+
+    def block_dots_s16(self, w, xq, stream=None):
+        """Exact per-sub-block int32 dots with 16-bit codes xq int16 [k] (checking export)."""
+        dots = torch.empty((self.n, self.k // 32), dtype=torch.int32, device=xq.device)
+        _check(_lib.qgemv_debug_block_dots_s16(self._h, self._check_w(w, 0, "w"), _dev(xq, torch.int16, "xq"),
+                                               _dev(dots, torch.int32, "dots"), _stream(stream)),
+               "qgemv_debug_block_dots_s16")
+        return dots
+
     def block_dots(self, w, xq, stream=None):
         """Exact per-block int32 dot products (checking export)."""
         m = xq.shape[0]
@@ -305,6 +341,17 @@ def debug_quantize(x: torch.Tensor, stream=None):
     sx = torch.empty((m, k // 32), dtype=torch.int32, device=x.device)
     _check(_lib.qgemv_debug_quantize(_dev(x, torch.float32, "x"), xq.data_ptr(), dx.data_ptr(), sx.data_ptr(),
                                      m, k, _stream(stream)), "qgemv_debug_quantize")
+    return xq, dx, sx
+
+
+def debug_quantize_s16(x: torch.Tensor, stream=None):
+    """Device 16-bit activation quantizer alone: returns (xq int16, dx fp32, sx int32)."""
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int16, device=x.device)
+    dx = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    sx = torch.empty((m, k // 32), dtype=torch.int32, device=x.device)
+    _check(_lib.qgemv_debug_quantize_s16(_dev(x, torch.float32, "x"), xq.data_ptr(), dx.data_ptr(), sx.data_ptr(),
+                                         m, k, _stream(stream)), "qgemv_debug_quantize_s16")
     return xq, dx, sx
 
 

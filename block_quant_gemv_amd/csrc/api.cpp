@@ -20,6 +20,7 @@
 #include "internal.h"
 #include "attn.h"
 #include "moe.h"
+#include "s16.h"
 #include "mfma.h"
 #include "swiglu.h"
 
@@ -594,6 +595,67 @@ int qattn_decode(const float* q, const void* k_cache, const void* v_cache, float
   return check_launch(launch_attn(a, q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
                                   out, ws, static_cast<hipStream_t>(stream)),
                       "attention");
+}
+
+namespace {
+int s16_plan(qgemv_t h, const char* fn) {
+  if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);
+  if (h->d.fmt != QFMT_Q4_K) return fail(QGEMV_EFORMAT, "%s: 16-bit activations need a Q4_K plan", fn);
+  if (!s16_gemv_ok(kQ4_K, h->d.n, h->d.k))
+    return fail(QGEMV_ESHAPE, "%s: k=%lld must be a multiple of 2048 up to 8192", fn, (long long)h->d.k);
+  return QGEMV_OK;
+}
+size_t s16_ws_bytes(int64_t k) { return round_up((size_t)k * 2, 256) + 2 * round_up((size_t)(k / 32) * 4, 256); }
+}  // namespace
+
+int qgemv_workspace_size_s16(qgemv_t h, size_t* bytes) {
+  int rc = s16_plan(h, "qgemv_workspace_size_s16");
+  if (rc) return rc;
+  if (!bytes) return fail(QGEMV_EINVAL, "qgemv_workspace_size_s16: null pointer");
+  *bytes = s16_ws_bytes(h->d.k);
+  return QGEMV_OK;
+}
+
+int qgemv_run_s16(qgemv_t h, const void* w, const float* x, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = s16_plan(h, "qgemv_run_s16");
+  if (rc) return rc;
+  if (!w || !x || !y || !ws) return fail(QGEMV_EINVAL, "qgemv_run_s16: null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(ws, 256))
+    return fail(QGEMV_EALIGN, "qgemv_run_s16: w and x need 16-byte, y 4-byte, ws 256-byte alignment");
+  const int64_t k = h->d.k;
+  if (ws_bytes < s16_ws_bytes(k))
+    return fail(QGEMV_EWORKSPACE, "qgemv_run_s16: workspace %zu < %zu bytes", ws_bytes, s16_ws_bytes(k));
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run_s16: launch failure injected (QGEMV_FAULT)");
+  char* base = static_cast<char*>(ws);
+  int16_t* xq = reinterpret_cast<int16_t*>(base);
+  float* dx = reinterpret_cast<float*>(base + round_up((size_t)k * 2, 256));
+  int32_t* sx = reinterpret_cast<int32_t*>(base + round_up((size_t)k * 2, 256) + round_up((size_t)(k / 32) * 4, 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = check_launch(launch_quant_s16(x, xq, dx, sx, k / 32, s), "quantize s16"))) return rc;
+  return check_launch(launch_q4k_s16(static_cast<const uint8_t*>(w), xq, dx, sx, y, nullptr, h->d.n, k, s),
+                      "gemv s16");
+}
+
+int qgemv_debug_quantize_s16(const float* x, int16_t* xq, float* dx, int32_t* sx, int m, int64_t k, void* stream) {
+  if (!x || !xq || !dx || !sx) return fail(QGEMV_EINVAL, "qgemv_debug_quantize_s16: null pointer");
+  if (!aligned(x, 16) || !aligned(xq, 8) || !aligned(dx, 4) || !aligned(sx, 4))
+    return fail(QGEMV_EALIGN, "qgemv_debug_quantize_s16: x needs 16-byte, xq 8-byte, others 4-byte alignment");
+  if (m < 1 || k < 32 || k % 32) return fail(QGEMV_ESHAPE, "qgemv_debug_quantize_s16: bad m/k");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_quantize_s16: launch failure injected");
+  return check_launch(launch_quant_s16(x, xq, dx, sx, (int64_t)m * (k / 32), static_cast<hipStream_t>(stream)),
+                      "quantize s16");
+}
+
+int qgemv_debug_block_dots_s16(qgemv_t h, const void* w, const int16_t* xq, int32_t* dots, void* stream) {
+  int rc = s16_plan(h, "qgemv_debug_block_dots_s16");
+  if (rc) return rc;
+  if (!w || !xq || !dots) return fail(QGEMV_EINVAL, "qgemv_debug_block_dots_s16: null pointer");
+  if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(dots, 4))
+    return fail(QGEMV_EALIGN, "qgemv_debug_block_dots_s16: w and xq need 16-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots_s16: launch failure injected");
+  return check_launch(launch_q4k_s16(static_cast<const uint8_t*>(w), xq, nullptr, nullptr, nullptr, dots, h->d.n,
+                                     h->d.k, static_cast<hipStream_t>(stream)),
+                      "block dots s16");
 }
 
 }  // extern "C"

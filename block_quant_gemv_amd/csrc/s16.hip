@@ -1,0 +1,233 @@
+// 16-bit activation variant of the decode GEMV.
+//
+// Int8 activation error compounds over a deep MoE stack; the fix recorded in
+// "01 · Phase overview: from 2B to 8B to MoE" (icman.com.cn, issue ledger
+// item ⑫) was 16-bit activations, a quantization step 256 times finer. Here
+// the activation blocks keep their shape (32 elements, one fp32 scale) with
+// scale = absmax / 32767 (IEEE fp32 division) and int16 codes rounded half
+// away from zero from the IEEE quotient x / scale.
+//
+// The GEMV is the register-direct single-token Q4_K kernel's layout (lane l
+// owns sub-blocks l, l + 64, ... of every row; the super-block header and the
+// sub-block's 16 code bytes are aligned 128-bit loads) with the int8 dot
+// products replaced by v_dot2_i32_i16: each dword of packed 4-bit codes is
+// split into four int16 pairs by masks (elements 4i, 4i+2 | 4i+1, 4i+3 |
+// 16+4i, 16+4i+2 | 16+4i+1, 16+4i+3) and the activation codes are permuted
+// into the same pairs once, when the lane loads them. The sub-block dot
+// D = sum x16 * q (|D| <= 32 * 32767 * 15 < 2^24, exact in int32 and in
+// fp32) then takes the scale and min correction as in the int8 path:
+// y += dx * (d * sc) * D - dx * (dmin * m) * sum(x16).
+#include "common.cuh"
+#include "internal.h"
+#include "s16.h"
+
+namespace qg {
+
+namespace {
+
+constexpr int kWaves16 = 4;
+constexpr int kBuf3 = 0x00020000;  // raw buffer resource, gfx9 family
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+QG_DEV int dot2(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), c, false);
+}
+
+QG_DEV int code16(float x, float d) {
+  const float q = fminf(fmaxf(roundf(x / d), -32767.0f), 32767.0f);
+  return (int)q;
+}
+
+// Eight lanes per block, four elements each (one 128-bit load).
+__global__ __launch_bounds__(256) void quant_s16_kernel(const float* __restrict__ x, int16_t* __restrict__ xq,
+                                                        float* __restrict__ dx, int32_t* __restrict__ sx,
+                                                        int64_t nblocks) {
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gt >> 3;
+  const int part = (int)(gt & 7);
+  if (blk >= nblocks) return;  // whole groups of eight lanes leave together
+  const float4 v = reinterpret_cast<const float4*>(x)[blk * 8 + part];
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = max8(a);
+  const float d = (a > 0.0f) ? a / 32767.0f : 0.0f;
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+  if (d != 0.0f) {
+    q0 = code16(v.x, d);
+    q1 = code16(v.y, d);
+    q2 = code16(v.z, d);
+    q3 = code16(v.w, d);
+  }
+  uint2 packed;
+  packed.x = ((uint32_t)q0 & 0xffffu) | ((uint32_t)q1 << 16);
+  packed.y = ((uint32_t)q2 & 0xffffu) | ((uint32_t)q3 << 16);
+  reinterpret_cast<uint2*>(xq)[blk * 8 + part] = packed;
+  int s = q0 + q1 + q2 + q3;
+  s = sum4(s);
+  s += other_quad(s);
+  if (part == 0) {
+    dx[blk] = d;
+    sx[blk] = s;
+  }
+}
+
+QG_DEV uint32_t field6(uint32_t hi, uint32_t lo, uint32_t sh) { return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u; }
+
+// JU sub-blocks per lane per row (K = 2048 JU); R rows per wave iteration.
+template <int JU, int R, bool DOTS>
+__global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* __restrict__ W,
+                                                                 const int16_t* __restrict__ xq,
+                                                                 const float* __restrict__ dx,
+                                                                 const int32_t* __restrict__ sx,
+                                                                 float* __restrict__ y, int32_t* __restrict__ dots,
+                                                                 int64_t n, int64_t rb) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * kWaves16 + wid;
+  const int64_t nw = (int64_t)gridDim.x * kWaves16;
+  const int64_t ngroups = (n + R - 1) / R;
+
+  // Activation codes of sub-blocks u = lane + 64 j, as int16 pairs in the
+  // order the weight masks produce them.
+  uint32_t xa[JU][16];
+  float xd[JU];
+  int xsum[JU];
+#pragma unroll
+  for (int j = 0; j < JU; ++j) {
+    const int u = lane + 64 * j;
+    const int4* p = reinterpret_cast<const int4*>(xq + 32 * u);
+    const int4 a0 = p[0], a1 = p[1], a2 = p[2], a3 = p[3];
+    const uint32_t w[16] = {(uint32_t)a0.x, (uint32_t)a0.y, (uint32_t)a0.z, (uint32_t)a0.w,
+                            (uint32_t)a1.x, (uint32_t)a1.y, (uint32_t)a1.z, (uint32_t)a1.w,
+                            (uint32_t)a2.x, (uint32_t)a2.y, (uint32_t)a2.z, (uint32_t)a2.w,
+                            (uint32_t)a3.x, (uint32_t)a3.y, (uint32_t)a3.z, (uint32_t)a3.w};  // w[t] = (x[2t], x[2t+1])
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[j][4 * i + 0] = perm(w[2 * i + 1], w[2 * i], 0x05040100u);      // x[4i],      x[4i+2]
+      xa[j][4 * i + 1] = perm(w[2 * i + 1], w[2 * i], 0x07060302u);      // x[4i+1],    x[4i+3]
+      xa[j][4 * i + 2] = perm(w[9 + 2 * i], w[8 + 2 * i], 0x05040100u);  // x[16+4i],   x[16+4i+2]
+      xa[j][4 * i + 3] = perm(w[9 + 2 * i], w[8 + 2 * i], 0x07060302u);  // x[16+4i+1], x[16+4i+3]
+    }
+    xd[j] = DOTS ? 0.0f : dx[u];
+    xsum[j] = DOTS ? 0 : sx[u];
+  }
+  const int g = lane & 7;
+  const bool sc_low = g < 6;
+  const uint32_t sc_sh = sc_low ? 6 * g : 6 * g - 32;
+  const bool m_low = g < 3;
+  const uint32_t m_sh = m_low ? 16 + 6 * g : 6 * g - 16;
+  uint32_t hoff[JU], qoff[JU];
+#pragma unroll
+  for (int j = 0; j < JU; ++j) {
+    const uint32_t b = (uint32_t)(lane >> 3) + 8u * j;
+    hoff[j] = b * 144u;
+    qoff[j] = b * 144u + 16u + 16u * g;
+  }
+
+  for (int64_t grp = gw; grp < ngroups; grp += nw) {
+    const int64_t r0 = grp * R;
+    const int64_t rows = (n - r0) < R ? (n - r0) : R;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + r0 * rb), 0, (int)(rows * rb), kBuf3);
+    u32x4 h[R][JU], q[R][JU];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < JU; ++j) {
+        h[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(hoff[j] + r * rb), 0, 2);
+        q[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(qoff[j] + r * rb), 0, 2);
+      }
+    float outv = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < JU; ++j) {
+        const uint32_t qv[4] = {q[r][j].x, q[r][j].y, q[r][j].z, q[r][j].w};
+        int D = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          D = dot2(qv[i] & 0x000F000Fu, xa[j][4 * i + 0], D);
+          D = dot2((qv[i] >> 8) & 0x000F000Fu, xa[j][4 * i + 1], D);
+          D = dot2((qv[i] >> 4) & 0x000F000Fu, xa[j][4 * i + 2], D);
+          D = dot2((qv[i] >> 12) & 0x000F000Fu, xa[j][4 * i + 3], D);
+        }
+        if constexpr (DOTS) {
+          if (r < rows) dots[(r0 + r) * (64 * JU) + lane + 64 * j] = D;
+          continue;
+        }
+        const u32x4 hh = h[r][j];
+        const float d = half_bits(hh.x & 0xffffu);
+        const float dmin = half_bits(hh.x >> 16);
+        const uint32_t sc = sc_low ? field6(hh.z, hh.y, sc_sh) : field6(hh.w, hh.z, sc_sh);
+        const uint32_t mn = m_low ? field6(hh.w, hh.z, m_sh) : field6(hh.w, hh.w, m_sh);
+        acc = fmaf(xd[j] * (d * (float)sc), (float)D, acc);
+        acc = fmaf(-(xd[j] * (dmin * (float)mn)), (float)xsum[j], acc);
+      }
+      if constexpr (!DOTS) {
+        const float sum = group_sum(acc, 64);
+        if (lane == r) outv = sum;
+      }
+    }
+    if constexpr (!DOTS) {
+      if (lane < rows) y[r0 + lane] = outv;
+    }
+  }
+}
+
+template <int JU, int R, bool DOTS>
+hipError_t launch_ju_t(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
+                       int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
+  auto kern = q4k_s16_kernel<JU, R, DOTS>;
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int64_t ngroups = (n + R - 1) / R;
+  int64_t waves = (int64_t)cus * 3 * kWaves16;  // three resident workgroups per CU, as the int8 kernel
+  if (waves > ngroups) waves = ngroups;
+  const int64_t wgs = (waves + kWaves16 - 1) / kWaves16;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kWaves16 * 64), 0, s, w, xq, dx, sx, y, dots, n,
+                     fmt_row_bytes(kQ4_K, k));
+  return hipGetLastError();
+}
+
+template <int R, bool DOTS>
+hipError_t launch_r(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
+                    int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
+  switch (k / 2048) {
+    case 1: return launch_ju_t<1, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    case 2: return launch_ju_t<2, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    case 3: return launch_ju_t<3, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    default: return launch_ju_t<4, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_s16(const float* x, int16_t* xq, float* dx, int32_t* sx, int64_t nblocks, hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  const int64_t threads = nblocks * 8;
+  hipLaunchKernelGGL(quant_s16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, xq, dx, sx,
+                     nblocks);
+  return hipGetLastError();
+}
+
+bool s16_gemv_ok(int fmt, int64_t n, int64_t k) {
+  return fmt == kQ4_K && n >= 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 4;
+}
+
+hipError_t launch_q4k_s16(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
+                          int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
+  if (!s16_gemv_ok(kQ4_K, n, k)) return hipErrorInvalidValue;
+  // Four rows per wave iteration for large matrices, one for small ones.
+  if (dots) return n >= 8192 ? launch_r<4, true>(w, xq, dx, sx, y, dots, n, k, s)
+                             : launch_r<1, true>(w, xq, dx, sx, y, dots, n, k, s);
+  return n >= 8192 ? launch_r<4, false>(w, xq, dx, sx, y, dots, n, k, s)
+                   : launch_r<1, false>(w, xq, dx, sx, y, dots, n, k, s);
+}
+
+}  // namespace qg

@@ -194,6 +194,21 @@ int qgemv_quantize(qgemv_t h, const float *x, int m, void *ws, size_t ws_bytes,
 int qgemv_run_quantized(qgemv_t h, const void *w, float *y, int m,
                         const void *ws, size_t ws_bytes, void *stream);
 
+/* 16-bit activation variant of qgemv_run for one token: x is quantized to
+ * 32-element blocks of int16 codes with an fp32 scale absmax / 32767 (codes
+ * rounded half away from zero from the IEEE quotient), a quantization step
+ * about 256 times finer than Q8 -- the fix for int8 activation error
+ * compounding over a deep MoE stack in "01 · Phase overview: from 2B to 8B
+ * to MoE" (icman.com.cn, issue ledger item ⑫). Block dots are int16 x 4-bit
+ * products (exact int32). Supported for QFMT_Q4_K plans with k a multiple of
+ * 2048 up to 8192 (QGEMV_EFORMAT / QGEMV_ESHAPE otherwise).
+ * qgemv_workspace_size_s16 gives the workspace bytes: regions, each 256-byte
+ * aligned, "xq" int16 [k] | "dx" fp32 [k/32] | "sx" int32 [k/32], in that
+ * order. Launches the 16-bit quantizer, then the GEMV kernel. */
+int qgemv_workspace_size_s16(qgemv_t h, size_t *bytes);
+int qgemv_run_s16(qgemv_t h, const void *w, const float *x, float *y, void *ws, size_t ws_bytes,
+                  void *stream);
+
 /* Fused FFN sublayer for a QKIND_FFN plan, on one stream with one
  * workspace: quantize x -> gate|up GEMV -> h = silu(gate) * up, re-quantized
  * to Q8 -> down GEMV -> y[m, hidden]. The sublayer is queued on a single
@@ -243,6 +258,17 @@ int qgemv_debug_quantize(const float *x, int8_t *xq, float *dx, int32_t *sx,
 int qgemv_debug_block_dots(qgemv_t h, const void *w, const int8_t *xq,
                            int32_t *dots, int m, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* The 16-bit quantizer alone: x fp32 [m, k] -> xq int16 [m, k], dx fp32
+ * [m, k/32], sx int32 [m, k/32]. k multiple of 32. */
+int qgemv_debug_quantize_s16(const float *x, int16_t *xq, float *dx, int32_t *sx, int m, int64_t k,
+                             void *stream);
+
+/* Exact per-sub-block dots of a Q4_K plan's weights with 16-bit codes xq
+ * int16 [k] (one token): dots int32 [n, k/32] = sum xq*q per 32-element
+ * sub-block, from the production 16-bit GEMV kernel with an integer-store
+ * epilogue. Same shape limits as qgemv_run_s16. */
+int qgemv_debug_block_dots_s16(qgemv_t h, const void *w, const int16_t *xq, int32_t *dots, void *stream);
 
 #ifdef __cplusplus
 }

@@ -182,3 +182,31 @@ def test_attention_validation_before_launch():
     assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, None, sz.value, None) == EINVAL
     assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, a + 16, sz.value, None) == EALIGN
     assert b"workspace" in lib.qgemv_last_error() or b"ws" in lib.qgemv_last_error()
+
+
+def test_s16_validation_before_launch():
+    def plan(fmt, n, k):
+        d = _desc(fmt=fmt, n=n, k=k)
+        h = ctypes.c_void_p()
+        assert lib.qgemv_create(ctypes.byref(h), ctypes.byref(d)) == OK
+        return h
+
+    sz = ctypes.c_size_t()
+    h = plan(3, 64, 4096)  # Q4_K
+    assert lib.qgemv_workspace_size_s16(h, ctypes.byref(sz)) == OK
+    assert sz.value == 8192 + 512 + 512
+    a = 1 << 20  # fake device addresses: every call below fails validation first
+    assert lib.qgemv_run_s16(h, a, a, a, a, sz.value - 1, None) == EWORKSPACE
+    assert lib.qgemv_run_s16(h, a + 8, a, a, a, sz.value, None) == EALIGN
+    assert lib.qgemv_run_s16(h, None, a, a, a, sz.value, None) == EINVAL
+    assert lib.qgemv_debug_block_dots_s16(h, a, a + 2, a, None) == EALIGN
+    lib.qgemv_destroy(h)
+    h8 = plan(2, 64, 4096)  # Q8_0: no 16-bit path
+    assert lib.qgemv_workspace_size_s16(h8, ctypes.byref(sz)) == EFORMAT
+    assert lib.qgemv_run_s16(h8, a, a, a, a, 1 << 30, None) == EFORMAT
+    lib.qgemv_destroy(h8)
+    hk = plan(3, 64, 1024)  # K not a multiple of 2048
+    assert lib.qgemv_run_s16(hk, a, a, a, a, 1 << 30, None) == ESHAPE
+    lib.qgemv_destroy(hk)
+    assert lib.qgemv_debug_quantize_s16(a, a, a, a, 1, 100, None) == ESHAPE
+    assert lib.qgemv_debug_quantize_s16(a + 4, a, a, a, 1, 128, None) == EALIGN
