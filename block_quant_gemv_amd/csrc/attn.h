@@ -22,6 +22,9 @@ struct AttnPlan {
 };
 
 bool attn_supported(const AttnShape& a);
+// Whether stage 1 runs its scores on matrix cores (head dimension 256, 8
+// query heads per key/value head).
+bool attn_uses_mfma(const AttnShape& a);
 AttnPlan attn_plan(const AttnShape& a);
 // Workspace bytes for the chunk partials (0 when one chunk suffices).
 size_t attn_workspace_bytes(const AttnShape& a);

@@ -34,6 +34,10 @@ namespace qg {
 
 namespace {
 
+#ifndef QG_ATTN_MFMA
+#define QG_ATTN_MFMA 0  // 1: scores on matrix cores for head dimension 256 with 8 query heads per key/value head (measured slower)
+#endif
+
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBatch = 2;          // token iterations whose loads are issued together (double-buffered)
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
@@ -82,6 +86,73 @@ QG_DEV void merge_into(AState<G>& a, const float (&mb)[G], const float (&lb)[G],
     a.l[j] = a.l[j] * ca + lb[j] * cb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a.acc[j][i] = a.acc[j][i] * ca + ob[j][i] * cb;
+  }
+}
+
+// Merge the per-lane states of a workgroup through LDS in a fixed order --
+// first the token slots of each wave into slot 0 (one slot per round), then
+// waves 1..3 into wave 0 -- and write the chunk's partial (or, for a single
+// chunk, the normalised output). Lane (slot, dl) holds dimensions
+// 8 dl .. 8 dl + 7 of every head of its group.
+template <int D, int G>
+QG_DEV void attn_finish(AState<G>& st, float (&red)[kAttnWaves][G][2 + D], int wid, int lane, int c, int kvh,
+                        int nchunks, float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl,
+                        float* __restrict__ po) {
+  constexpr int LPT = D / 8;
+  constexpr int TPW = 64 / LPT;
+  const int dl = lane % LPT;
+  const int slot = lane / LPT;
+  auto put = [&](int w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (dl == 0) {
+        red[w][j][0] = st.m[j];
+        red[w][j][1] = st.l[j];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[w][j][2 + 8 * dl + i] = st.acc[j][i];
+    }
+  };
+  auto take = [&](int w) __attribute__((always_inline)) {
+    float mb[G], lb[G], ob[G][8];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      mb[j] = red[w][j][0];
+      lb[j] = red[w][j][1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[j][i] = red[w][j][2 + 8 * dl + i];
+    }
+    merge_into<G>(st, mb, lb, ob);
+  };
+#pragma unroll 1
+  for (int sl = 1; sl < TPW; ++sl) {
+    if (slot == sl) put(wid);
+    __syncthreads();
+    if (slot == 0) take(wid);
+    __syncthreads();
+  }
+  if (slot == 0) put(wid);
+  __syncthreads();
+  if (wid != 0 || slot != 0) return;
+#pragma unroll 1
+  for (int w = 1; w < kAttnWaves; ++w) take(w);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int64_t h = (int64_t)kvh * G + j;
+    if (nchunks == 1) {
+      const float inv = 1.0f / st.l[j];
+      float4* op = reinterpret_cast<float4*>(out + h * D + 8 * dl);
+      op[0] = make_float4(st.acc[j][0] * inv, st.acc[j][1] * inv, st.acc[j][2] * inv, st.acc[j][3] * inv);
+      op[1] = make_float4(st.acc[j][4] * inv, st.acc[j][5] * inv, st.acc[j][6] * inv, st.acc[j][7] * inv);
+    } else {
+      if (dl == 0) {
+        pm[h * nchunks + c] = st.m[j];
+        pl[h * nchunks + c] = st.l[j];
+      }
+      float4* op = reinterpret_cast<float4*>(po + (h * nchunks + c) * D + 8 * dl);
+      op[0] = make_float4(st.acc[j][0], st.acc[j][1], st.acc[j][2], st.acc[j][3]);
+      op[1] = make_float4(st.acc[j][4], st.acc[j][5], st.acc[j][6], st.acc[j][7]);
+    }
   }
 }
 
@@ -213,60 +284,201 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_kernel(
     tb += kBatchTokens;
   }
 
-  // Merge through LDS in a fixed order: first the token slots of each wave
-  // into slot 0 (one slot per round), then waves 1..3 into wave 0.
-  auto put = [&](int w) __attribute__((always_inline)) {
+  attn_finish<D, G>(st, red, wid, lane, c, kvh, nchunks, out, pm, pl, po);
+}
+
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Stage 1 with the scores on matrix cores, for D = 256 and G = 8 (the
+// workload shape). Per wave and tile of 16 tokens, S^T[16 tokens x 16 heads]
+// = K_tile . Q^T is v_mfma_f32_16x16x16_f16 over 16 steps of 4 dimensions
+// (heads 8..15 are zero padding): the A operand is the lane's token row
+// (lane = token + 16 g reads bytes 128 g .. 128 g + 127 of its row, so step
+// s covers dimensions 64 g + 4 s .. + 3), the B operand the query with the
+// same dimension mapping. The fp32 query is split into fp16 halves
+// hi + lo (scaled per head by a power of two that keeps both normal and
+// finite), so two MFMAs per step give the scores to about 2^-22 relative;
+// keys are exact in fp16 and products accumulate in fp32. The output lane
+// (head h = lane % 16, tokens 4 (lane / 16) + r) then runs the lazily
+// rescaled softmax for its head, the weights go through a small LDS table,
+// and P.V runs on the VALU in the layout of the other kernel (lane = token
+// slot x 8 dimensions, all 8 heads).
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_mfma_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po,
+    int64_t n_ctx, int64_t chunk, int nchunks, float qscale) {
+  constexpr int D = 256, G = 8;
+  __shared__ float red[kAttnWaves][G][2 + D];
+  __shared__ float pbuf[kAttnWaves][16][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int dl = lane & 31;   // P.V layout: dimensions 8 dl .. 8 dl + 7
+  const int slot = lane >> 5;  // P.V layout: token slot
+  const int mh = lane & 15;   // MFMA layout: token row (A) or head column (B, D)
+  const int mg = lane >> 4;   // MFMA layout: group of 4 in the reduction / output rows
+
+  // Query operand: head mh (zero for mh >= G), dimensions 64 mg + 4 s + e.
+  // Scale: q * qscale * 2^e with 2^e chosen per head so its largest value
+  // lands in [2^13, 2^14): both fp16 halves stay normal and finite.
+  float qv[64];
+  float qmax = 0.0f;
+  if (mh < G) {
+    const float4* qp = reinterpret_cast<const float4*>(q + ((int64_t)kvh * G + mh) * D + 64 * mg);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (dl == 0) {
-        red[w][j][0] = st.m[j];
-        red[w][j][1] = st.l[j];
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) red[w][j][2 + 8 * dl + i] = st.acc[j][i];
+    for (int i = 0; i < 16; ++i) {
+      const float4 v = qp[i];
+      qv[4 * i] = v.x * qscale; qv[4 * i + 1] = v.y * qscale; qv[4 * i + 2] = v.z * qscale; qv[4 * i + 3] = v.w * qscale;
     }
-  };
-  auto take = [&](int w) __attribute__((always_inline)) {
-    float mb[G], lb[G], ob[G][8];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      mb[j] = red[w][j][0];
-      lb[j] = red[w][j][1];
+    for (int i = 0; i < 64; ++i) qmax = fmaxf(qmax, fabsf(qv[i]));
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ob[j][i] = red[w][j][2 + 8 * dl + i];
-    }
-    merge_into<G>(st, mb, lb, ob);
-  };
-#pragma unroll 1
-  for (int sl = 1; sl < TPW; ++sl) {
-    if (slot == sl) put(wid);
-    __syncthreads();
-    if (slot == 0) take(wid);
-    __syncthreads();
+    for (int i = 0; i < 64; ++i) qv[i] = 0.0f;
   }
-  if (slot == 0) put(wid);
-  __syncthreads();
-  if (wid != 0 || slot != 0) return;
-#pragma unroll 1
-  for (int w = 1; w < kAttnWaves; ++w) take(w);
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  int qe = 0;
+  if (qmax > 0.0f) {
+    (void)frexpf(qmax, &qe);  // qmax in [2^(qe-1), 2^qe)
+    qe = 14 - qe;
+  }
+  const float up = ldexpf(1.0f, qe), down = ldexpf(1.0f, -qe);
+  h16x4 qh[16], ql[16];
+#pragma unroll
+  for (int st = 0; st < 16; ++st)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = qv[4 * st + e] * up;
+      const _Float16 hi = (_Float16)v;
+      qh[st][e] = hi;
+      ql[st][e] = (_Float16)(v - (float)hi);
+    }
+
+  AState<G> st;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const int64_t h = (int64_t)kvh * G + j;
-    if (nchunks == 1) {
-      const float inv = 1.0f / st.l[j];
-      float4* op = reinterpret_cast<float4*>(out + h * D + 8 * dl);
-      op[0] = make_float4(st.acc[j][0] * inv, st.acc[j][1] * inv, st.acc[j][2] * inv, st.acc[j][3] * inv);
-      op[1] = make_float4(st.acc[j][4] * inv, st.acc[j][5] * inv, st.acc[j][6] * inv, st.acc[j][7] * inv);
-    } else {
-      if (dl == 0) {
-        pm[h * nchunks + c] = st.m[j];
-        pl[h * nchunks + c] = st.l[j];
-      }
-      float4* op = reinterpret_cast<float4*>(po + (h * nchunks + c) * D + 8 * dl);
-      op[0] = make_float4(st.acc[j][0], st.acc[j][1], st.acc[j][2], st.acc[j][3]);
-      op[1] = make_float4(st.acc[j][4], st.acc[j][5], st.acc[j][6], st.acc[j][7]);
-    }
+    st.m[j] = -INFINITY;
+    st.l[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[j][i] = 0.0f;
   }
+  float m = -INFINITY;   // reference maximum of head mh (same in its four lanes)
+  float lsum = 0.0f;     // this lane's share of head mh's sum of weights
+
+  const int64_t head_off = (int64_t)kvh * n_ctx * D;
+  const int nbytes = (int)(n_ctx * D * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, nbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, nbytes, kBufWord3);
+  const int64_t t0 = (int64_t)c * chunk;
+  const int64_t t1 = (t0 + chunk) < n_ctx ? (t0 + chunk) : n_ctx;
+
+  // K rows for the MFMA (past the chunk: out of range, zeros) and V rows for
+  // P.V. The next tile's K is requested right after this tile's MFMAs and
+  // each V register set is refilled as soon as P.V has used it, so a tile's
+  // loads are in flight while the previous tile is processed.
+  u32x4 kr[8], vr[8];
+  auto load_k = [&](int64_t tb) __attribute__((always_inline)) {
+    const int64_t tk = tb + mh;
+    const int koff = (int)((tk < t1 ? tk : n_ctx) * (D * 2)) + 128 * mg;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 16 * u, 0, 2);
+  };
+  auto load_v = [&](int64_t tb, int it) __attribute__((always_inline)) {
+    const int64_t tv = tb + 2 * it + slot;
+    const int voff = (int)((tv < t1 ? tv : n_ctx) * (D * 2)) + 16 * dl;
+    vr[it] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 2);
+  };
+  {
+    const int64_t tb = t0 + 16 * (int64_t)wid;
+    load_k(tb);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) load_v(tb, it);
+  }
+  for (int64_t tb = t0 + 16 * (int64_t)wid; tb < t1; tb += 16 * kAttnWaves) {
+    const int64_t tn = tb + 16 * kAttnWaves;  // next tile (past t1: no memory traffic)
+    f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const u32x2 lo = kr[u].xy, hi = kr[u].zw;
+      const h16x4 a0 = __builtin_bit_cast(h16x4, lo), a1 = __builtin_bit_cast(h16x4, hi);
+      sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, qh[2 * u], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, ql[2 * u], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, qh[2 * u + 1], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, ql[2 * u + 1], sc, 0, 0, 0);
+    }
+    load_k(tn);
+    // Scores of head mh for tokens tb + 4 mg + r.
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = (tb + 4 * mg + r < t1) ? sc[r] * down : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool big = mh < G && mx > m + kTau;
+    if (__builtin_amdgcn_ballot_w64(big)) {  // wave-uniform
+      const float mn = fmaxf(m, mx);
+      const float cr = mn == m ? 1.0f : __builtin_amdgcn_exp2f(m - mn);  // m = -inf: 0
+      m = mn;
+      lsum *= cr;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float cj = readlane_f(cr, j);  // head j's factor (lane j holds head j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[j][i] *= cj;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = sv[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - m);
+      lsum += p[r];
+    }
+    if (mh < G) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pbuf[wid][4 * mg + r][mh] = p[r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's weights are in LDS
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const float4* pp = reinterpret_cast<const float4*>(&pbuf[wid][2 * it + slot][0]);
+      const float4 pa = pp[0], pb = pp[1];
+      const float pj[G] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      const uint32_t vw[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = h2f(vw[i]);
+        vf[2 * i + 1] = h2f(vw[i] >> 16);
+      }
+      load_v(tn, it);
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[j][i] = fmaf(pj[j], vf[i], st.acc[j][i]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile overwrites the table
+  }
+
+  // Head sums over the four lanes of each head, then the state in the P.V
+  // layout: every lane gets the heads' maxima; slot 0 carries the sums.
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    st.m[j] = readlane_f(m, j);
+    st.l[j] = slot == 0 ? readlane_f(lsum, j) : 0.0f;
+  }
+  attn_finish<D, G>(st, red, wid, lane, c, kvh, nchunks, out, pm, pl, po);
 }
 
 // grid = (n_heads, D / 64); block = 4 waves. The chunk maxima and sums are
@@ -357,9 +569,14 @@ hipError_t launch_dg(const AttnShape& a, const AttnPlan& pl, const float* q, con
     pm = po + (int64_t)a.n_heads * pl.nchunks * D;
     plv = pm + (int64_t)a.n_heads * pl.nchunks;
   }
-  hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3((unsigned)pl.nchunks, (unsigned)a.n_kv),
-                     dim3(kAttnWaves * 64), 0, s, q, k, v, out, pm, plv, po, a.n_ctx, pl.chunk,
-                     (int)pl.nchunks, qscale);
+  if (attn_uses_mfma(a))
+    hipLaunchKernelGGL(attn_partial_mfma_kernel, dim3((unsigned)pl.nchunks, (unsigned)a.n_kv),
+                       dim3(kAttnWaves * 64), 0, s, q, k, v, out, pm, plv, po, a.n_ctx, pl.chunk,
+                       (int)pl.nchunks, qscale);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3((unsigned)pl.nchunks, (unsigned)a.n_kv),
+                       dim3(kAttnWaves * 64), 0, s, q, k, v, out, pm, plv, po, a.n_ctx, pl.chunk,
+                       (int)pl.nchunks, qscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nchunks == 1) return e;
   hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)a.n_heads, D / 64), dim3(kMergeWaves * 64), 0, s, pm,
@@ -392,6 +609,10 @@ int device_cu_count() {
 
 }  // namespace
 
+bool attn_uses_mfma(const AttnShape& a) {
+  return QG_ATTN_MFMA && a.head_dim == 256 && a.n_heads == 8 * a.n_kv;
+}
+
 bool attn_supported(const AttnShape& a) {
   if (a.head_dim != 128 && a.head_dim != 256) return false;
   if (a.n_kv < 1 || a.n_heads < a.n_kv || a.n_heads % a.n_kv) return false;
@@ -404,8 +625,9 @@ bool attn_supported(const AttnShape& a) {
 
 AttnPlan attn_plan(const AttnShape& a) {
   // Tokens one workgroup iteration covers; a chunk is a whole number of them.
-  const int64_t step = (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
-  const int64_t min_chunk = step * kAttnBatch * 2;
+  const bool mf = attn_uses_mfma(a);
+  const int64_t step = mf ? (int64_t)kAttnWaves * 16 : (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
+  const int64_t min_chunk = mf ? step : step * kAttnBatch * 2;
   // Enough chunks for two workgroups per CU (at most kMaxChunks), none
   // shorter than two batched iterations of the workgroup.
   int64_t want = ((int64_t)device_cu_count() * 2 + a.n_kv - 1) / a.n_kv;

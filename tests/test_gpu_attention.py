@@ -28,7 +28,8 @@ def _run(hq, hkv, d, t, seed, qmul=1.0):
 
 
 @pytest.mark.parametrize("hq,hkv,d,t", [
-    (16, 2, 256, 1), (16, 2, 256, 8), (16, 2, 256, 37), (16, 2, 256, 1000), (16, 2, 256, 4096),
+    (16, 2, 256, 1), (16, 2, 256, 8), (16, 2, 256, 37), (16, 2, 256, 65), (16, 2, 256, 130),
+    (16, 2, 256, 1000), (16, 2, 256, 4096), (8, 1, 256, 3333),
     (8, 8, 128, 777), (8, 4, 128, 5000), (16, 4, 128, 3001), (32, 4, 128, 129), (4, 4, 256, 20000),
 ])
 def test_attention_parity(hq, hkv, d, t):
