@@ -600,8 +600,9 @@ int qattn_decode(const float* q, const void* k_cache, const void* v_cache, float
 namespace {
 int s16_plan(qgemv_t h, const char* fn) {
   if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);
-  if (h->d.fmt != QFMT_Q4_K) return fail(QGEMV_EFORMAT, "%s: 16-bit activations need a Q4_K plan", fn);
-  if (!s16_gemv_ok(kQ4_K, h->d.n, h->d.k))
+  if (h->d.fmt != QFMT_Q4_K && h->d.fmt != QFMT_Q5_K)
+    return fail(QGEMV_EFORMAT, "%s: 16-bit activations need a Q4_K or Q5_K plan", fn);
+  if (!s16_gemv_ok(h->d.fmt, h->d.n, h->d.k))
     return fail(QGEMV_ESHAPE, "%s: k=%lld must be a multiple of 2048 up to 8192", fn, (long long)h->d.k);
   return QGEMV_OK;
 }
@@ -632,8 +633,9 @@ int qgemv_run_s16(qgemv_t h, const void* w, const float* x, float* y, void* ws, 
   int32_t* sx = reinterpret_cast<int32_t*>(base + round_up((size_t)k * 2, 256) + round_up((size_t)(k / 32) * 4, 256));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = check_launch(launch_quant_s16(x, xq, dx, sx, k / 32, s), "quantize s16"))) return rc;
-  return check_launch(launch_q4k_s16(static_cast<const uint8_t*>(w), xq, dx, sx, y, nullptr, h->d.n, k, s),
-                      "gemv s16");
+  return check_launch(
+      launch_kquant_s16(h->d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y, nullptr, h->d.n, k, s),
+      "gemv s16");
 }
 
 int qgemv_debug_quantize_s16(const float* x, int16_t* xq, float* dx, int32_t* sx, int m, int64_t k, void* stream) {
@@ -653,8 +655,8 @@ int qgemv_debug_block_dots_s16(qgemv_t h, const void* w, const int16_t* xq, int3
   if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(dots, 4))
     return fail(QGEMV_EALIGN, "qgemv_debug_block_dots_s16: w and xq need 16-byte alignment");
   if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_debug_block_dots_s16: launch failure injected");
-  return check_launch(launch_q4k_s16(static_cast<const uint8_t*>(w), xq, nullptr, nullptr, nullptr, dots, h->d.n,
-                                     h->d.k, static_cast<hipStream_t>(stream)),
+  return check_launch(launch_kquant_s16(h->d.fmt, static_cast<const uint8_t*>(w), xq, nullptr, nullptr, nullptr,
+                                        dots, h->d.n, h->d.k, static_cast<hipStream_t>(stream)),
                       "block dots s16");
 }
 

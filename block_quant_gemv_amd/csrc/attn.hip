@@ -39,7 +39,10 @@ namespace {
 #endif
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnBatch = 2;          // token iterations whose loads are issued together (double-buffered)
+#ifndef QG_ATTN_BATCH
+#define QG_ATTN_BATCH 2
+#endif
+constexpr int kAttnBatch = QG_ATTN_BATCH;  // token iterations whose loads are issued together (double-buffered)
 constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 family
 
 QG_DEV float h2f(uint32_t bits) { return half_bits(bits & 0xffffu); }

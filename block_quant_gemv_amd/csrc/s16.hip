@@ -7,15 +7,18 @@
 // scale = absmax / 32767 (IEEE fp32 division) and int16 codes rounded half
 // away from zero from the IEEE quotient x / scale.
 //
-// The GEMV is the register-direct single-token Q4_K kernel's layout (lane l
-// owns sub-blocks l, l + 64, ... of every row; the super-block header and the
-// sub-block's 16 code bytes are aligned 128-bit loads) with the int8 dot
+// The GEMV is the register-direct single-token Q4_K / Q5_K kernel's layout
+// (lane l owns sub-blocks l, l + 64, ... of every row; the super-block header
+// and the sub-block's 16 code bytes are aligned 128-bit loads, plus Q5_K's
+// 4-byte word of fifth bits) with the int8 dot
 // products replaced by v_dot2_i32_i16: each dword of packed 4-bit codes is
 // split into four int16 pairs by masks (elements 4i, 4i+2 | 4i+1, 4i+3 |
 // 16+4i, 16+4i+2 | 16+4i+1, 16+4i+3) and the activation codes are permuted
 // into the same pairs once, when the lane loads them. The sub-block dot
-// D = sum x16 * q (|D| <= 32 * 32767 * 15 < 2^24, exact in int32 and in
-// fp32) then takes the scale and min correction as in the int8 path:
+// D = sum x16 * q (|D| <= 32 * 32767 * 31 < 2^25, exact in int32; exact in
+// fp32 for Q4_K, |D| < 2^24, and for Q5_K within one rounding of an fp32
+// product of the kind the epilogue already makes) then takes the scale and
+// min correction as in the int8 path:
 // y += dx * (d * sc) * D - dx * (dmin * m) * sum(x16).
 #include "common.cuh"
 #include "internal.h"
@@ -73,8 +76,9 @@ __global__ __launch_bounds__(256) void quant_s16_kernel(const float* __restrict_
 
 QG_DEV uint32_t field6(uint32_t hi, uint32_t lo, uint32_t sh) { return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u; }
 
-// JU sub-blocks per lane per row (K = 2048 JU); R rows per wave iteration.
-template <int JU, int R, bool DOTS>
+// FMT: kQ4_K or kQ5_K; JU sub-blocks per lane per row (K = 2048 JU); R rows
+// per wave iteration.
+template <int FMT, int JU, int R, bool DOTS>
 __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* __restrict__ W,
                                                                  const int16_t* __restrict__ xq,
                                                                  const float* __restrict__ dx,
@@ -116,12 +120,16 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
   const uint32_t sc_sh = sc_low ? 6 * g : 6 * g - 32;
   const bool m_low = g < 3;
   const uint32_t m_sh = m_low ? 16 + 6 * g : 6 * g - 16;
-  uint32_t hoff[JU], qoff[JU];
+  constexpr bool Q5 = FMT == kQ5_K;
+  constexpr uint32_t BB = Q5 ? 176u : 144u;  // super-block bytes
+  constexpr uint32_t QS = Q5 ? 48u : 16u;    // offset of the low code bits
+  uint32_t hoff[JU], qoff[JU], xoff[JU];
 #pragma unroll
   for (int j = 0; j < JU; ++j) {
     const uint32_t b = (uint32_t)(lane >> 3) + 8u * j;
-    hoff[j] = b * 144u;
-    qoff[j] = b * 144u + 16u + 16u * g;
+    hoff[j] = b * BB;
+    qoff[j] = b * BB + QS + 16u * g;
+    xoff[j] = b * BB + 16u + 4u * g;  // Q5_K: the sub-block's word of fifth bits
   }
 
   for (int64_t grp = gw; grp < ngroups; grp += nw) {
@@ -130,12 +138,14 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + r0 * rb), 0, (int)(rows * rb), kBuf3);
     u32x4 h[R][JU], q[R][JU];
+    uint32_t x5[R][JU];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < JU; ++j) {
         h[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(hoff[j] + r * rb), 0, 2);
         q[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(qoff[j] + r * rb), 0, 2);
+        if constexpr (Q5) x5[r][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(xoff[j] + r * rb), 0, 2);
       }
     float outv = 0.0f;
 #pragma unroll
@@ -147,10 +157,23 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
         int D = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          D = dot2(qv[i] & 0x000F000Fu, xa[j][4 * i + 0], D);
-          D = dot2((qv[i] >> 8) & 0x000F000Fu, xa[j][4 * i + 1], D);
-          D = dot2((qv[i] >> 4) & 0x000F000Fu, xa[j][4 * i + 2], D);
-          D = dot2((qv[i] >> 12) & 0x000F000Fu, xa[j][4 * i + 3], D);
+          uint32_t w0 = qv[i] & 0x000F000Fu, w1 = (qv[i] >> 8) & 0x000F000Fu;
+          uint32_t w2 = (qv[i] >> 4) & 0x000F000Fu, w3 = (qv[i] >> 12) & 0x000F000Fu;
+          if constexpr (Q5) {
+            // Fifth bit of sub-block element e at bit 8 (e % 4) + e / 4 of the
+            // word, moved to bit 4 of its int16 lane: elements 4i, 4i+2 sit at
+            // bits i, 16+i; 4i+1, 4i+3 at 8+i, 24+i; 16+4i, 16+4i+2 at 4+i,
+            // 20+i; 16+4i+1, 16+4i+3 at 12+i, 28+i.
+            const uint32_t f = x5[r][j];
+            w0 |= (f << (4 - i)) & 0x00100010u;
+            w1 |= (f >> (4 + i)) & 0x00100010u;
+            w2 |= (f >> i) & 0x00100010u;
+            w3 |= (f >> (8 + i)) & 0x00100010u;
+          }
+          D = dot2(w0, xa[j][4 * i + 0], D);
+          D = dot2(w1, xa[j][4 * i + 1], D);
+          D = dot2(w2, xa[j][4 * i + 2], D);
+          D = dot2(w3, xa[j][4 * i + 3], D);
         }
         if constexpr (DOTS) {
           if (r < rows) dots[(r0 + r) * (64 * JU) + lane + 64 * j] = D;
@@ -175,10 +198,10 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
   }
 }
 
-template <int JU, int R, bool DOTS>
+template <int FMT, int JU, int R, bool DOTS>
 hipError_t launch_ju_t(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
                        int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
-  auto kern = q4k_s16_kernel<JU, R, DOTS>;
+  auto kern = q4k_s16_kernel<FMT, JU, R, DOTS>;
   static int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -191,19 +214,29 @@ hipError_t launch_ju_t(const uint8_t* w, const int16_t* xq, const float* dx, con
   if (waves > ngroups) waves = ngroups;
   const int64_t wgs = (waves + kWaves16 - 1) / kWaves16;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kWaves16 * 64), 0, s, w, xq, dx, sx, y, dots, n,
-                     fmt_row_bytes(kQ4_K, k));
+                     fmt_row_bytes(FMT, k));
   return hipGetLastError();
 }
 
-template <int R, bool DOTS>
+template <int FMT, int R, bool DOTS>
 hipError_t launch_r(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
                     int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
   switch (k / 2048) {
-    case 1: return launch_ju_t<1, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
-    case 2: return launch_ju_t<2, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
-    case 3: return launch_ju_t<3, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
-    default: return launch_ju_t<4, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    case 1: return launch_ju_t<FMT, 1, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    case 2: return launch_ju_t<FMT, 2, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    case 3: return launch_ju_t<FMT, 3, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
+    default: return launch_ju_t<FMT, 4, R, DOTS>(w, xq, dx, sx, y, dots, n, k, s);
   }
+}
+
+template <int FMT>
+hipError_t launch_fmt16(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
+                        int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
+  // Four rows per wave iteration for large matrices, one for small ones.
+  if (dots) return n >= 8192 ? launch_r<FMT, 4, true>(w, xq, dx, sx, y, dots, n, k, s)
+                             : launch_r<FMT, 1, true>(w, xq, dx, sx, y, dots, n, k, s);
+  return n >= 8192 ? launch_r<FMT, 4, false>(w, xq, dx, sx, y, dots, n, k, s)
+                   : launch_r<FMT, 1, false>(w, xq, dx, sx, y, dots, n, k, s);
 }
 
 }  // namespace
@@ -217,17 +250,14 @@ hipError_t launch_quant_s16(const float* x, int16_t* xq, float* dx, int32_t* sx,
 }
 
 bool s16_gemv_ok(int fmt, int64_t n, int64_t k) {
-  return fmt == kQ4_K && n >= 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 4;
+  return (fmt == kQ4_K || fmt == kQ5_K) && n >= 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 4;
 }
 
-hipError_t launch_q4k_s16(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
-                          int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
-  if (!s16_gemv_ok(kQ4_K, n, k)) return hipErrorInvalidValue;
-  // Four rows per wave iteration for large matrices, one for small ones.
-  if (dots) return n >= 8192 ? launch_r<4, true>(w, xq, dx, sx, y, dots, n, k, s)
-                             : launch_r<1, true>(w, xq, dx, sx, y, dots, n, k, s);
-  return n >= 8192 ? launch_r<4, false>(w, xq, dx, sx, y, dots, n, k, s)
-                   : launch_r<1, false>(w, xq, dx, sx, y, dots, n, k, s);
+hipError_t launch_kquant_s16(int fmt, const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx,
+                             float* y, int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
+  if (!s16_gemv_ok(fmt, n, k)) return hipErrorInvalidValue;
+  return fmt == kQ4_K ? launch_fmt16<kQ4_K>(w, xq, dx, sx, y, dots, n, k, s)
+                      : launch_fmt16<kQ5_K>(w, xq, dx, sx, y, dots, n, k, s);
 }
 
 }  // namespace qg

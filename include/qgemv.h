@@ -199,9 +199,10 @@ int qgemv_run_quantized(qgemv_t h, const void *w, float *y, int m,
  * rounded half away from zero from the IEEE quotient), a quantization step
  * about 256 times finer than Q8 -- the fix for int8 activation error
  * compounding over a deep MoE stack in "01 · Phase overview: from 2B to 8B
- * to MoE" (icman.com.cn, issue ledger item ⑫). Block dots are int16 x 4-bit
- * products (exact int32). Supported for QFMT_Q4_K plans with k a multiple of
- * 2048 up to 8192 (QGEMV_EFORMAT / QGEMV_ESHAPE otherwise).
+ * to MoE" (icman.com.cn, issue ledger item ⑫). Block dots are int16 x 4- or
+ * 5-bit products (exact int32). Supported for QFMT_Q4_K and QFMT_Q5_K plans
+ * with k a multiple of 2048 up to 8192 (QGEMV_EFORMAT / QGEMV_ESHAPE
+ * otherwise).
  * qgemv_workspace_size_s16 gives the workspace bytes: regions, each 256-byte
  * aligned, "xq" int16 [k] | "dx" fp32 [k/32] | "sx" int32 [k/32], in that
  * order. Launches the 16-bit quantizer, then the GEMV kernel. */
@@ -264,7 +265,7 @@ int qgemv_debug_block_dots(qgemv_t h, const void *w, const int8_t *xq,
 int qgemv_debug_quantize_s16(const float *x, int16_t *xq, float *dx, int32_t *sx, int m, int64_t k,
                              void *stream);
 
-/* Exact per-sub-block dots of a Q4_K plan's weights with 16-bit codes xq
+/* Exact per-sub-block dots of a Q4_K or Q5_K plan's weights with 16-bit codes xq
  * int16 [k] (one token): dots int32 [n, k/32] = sum xq*q per 32-element
  * sub-block, from the production 16-bit GEMV kernel with an integer-store
  * epilogue. Same shape limits as qgemv_run_s16. */

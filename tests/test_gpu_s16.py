@@ -35,43 +35,46 @@ def test_quantizer_s16_bit_exact():
     assert np.array_equal(host(sx), s)
 
 
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k"])
 @pytest.mark.parametrize("n,k", [(300, 2048), (100, 4096), (33, 6144), (8195, 4096), (64, 8192)])
-def test_block_dots_s16_bit_exact(n, k):
-    w = synth.weights("q4_k", n, k, seed=61)
+def test_block_dots_s16_bit_exact(fmt, n, k):
+    w = synth.weights(fmt, n, k, seed=61)
     x = synth.activations(62, 1, k)
     q, _, _ = quantize_s16(x)
-    g = qg.GEMV("q4_k", n, k)
+    g = qg.GEMV(fmt, n, k)
     dots = host(g.block_dots_s16(dev(w), dev(q[0])))
     torch.cuda.synchronize()
-    ref = og.block_dots("q4_k", w, n, k, q)[0]
+    ref = og.block_dots(fmt, w, n, k, q)[0]
     assert np.array_equal(dots.astype(np.int64), ref)
 
 
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k"])
 @pytest.mark.parametrize("n,k", [(1, 4096), (100, 2048), (4096, 4096), (8195, 4096), (777, 6144), (12288, 8192)])
-def test_gemv_s16_parity(n, k):
-    w = synth.weights("q4_k", n, k, seed=63)
+def test_gemv_s16_parity(fmt, n, k):
+    w = synth.weights(fmt, n, k, seed=63)
     x = synth.activations(64, 1, k)
-    g = qg.GEMV("q4_k", n, k)
+    g = qg.GEMV(fmt, n, k)
     full, y = guarded(torch, n, torch.float32)
     g.run_s16(dev(w), dev(x), y=y)
     torch.cuda.synchronize()
     assert canary_ok(torch, full, n)
     q, d, _ = quantize_s16(x)
-    e = normwise(host(y)[None], og.gemv_dequant("q4_k", w, n, k, q, d))
-    say(f"s16 gemv n={n} k={k}: normwise {e:.2e}")
+    e = normwise(host(y)[None], og.gemv_dequant(fmt, w, n, k, q, d))
+    say(f"s16 gemv {fmt} n={n} k={k}: normwise {e:.2e}")
     assert e <= TOL
 
 
-def test_gemv_s16_full_size_sampled_rows():
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k"])
+def test_gemv_s16_full_size_sampled_rows(fmt):
     n, k = 24576, 4096
-    w = synth.weights("q4_k", n, k, seed=65)
+    w = synth.weights(fmt, n, k, seed=65)
     x = synth.activations(66, 1, k)
-    g = qg.GEMV("q4_k", n, k)
+    g = qg.GEMV(fmt, n, k)
     y = host(g.run_s16(dev(w), dev(x)))
     torch.cuda.synchronize()
     q, d, _ = quantize_s16(x)
     rows = np.unique(np.linspace(0, n - 1, 800).astype(np.int64))
-    assert normwise(y[:, rows], og.gemv_rows("q4_k", w, n, k, rows, q, d)) <= TOL
+    assert normwise(y[:, rows], og.gemv_rows(fmt, w, n, k, rows, q, d)) <= TOL
 
 
 def test_s16_is_closer_to_unquantized_activations():
