@@ -74,3 +74,32 @@ def test_attention_repeatable_and_in_bounds():
     assert torch.equal(o1, o2)
     assert canary_ok(torch, wfull, wsz) and canary_ok(torch, ofull, 16 * 256)
     assert normwise(host(o1), decode_attention(q, k, v)) <= TOL
+
+
+def test_attention_graph_replays_match_eager():
+    # Captured once (both stages), replayed on new queries with eager calls on
+    # the same workspace in between: every replay equals the eager result.
+    t = 5000
+    _, k, v = synth.attention_inputs(95, 16, 2, 256, t)
+    qs = [synth.attention_inputs(96 + i, 16, 2, 256, 1)[0] for i in range(3)]
+    a = qg.Attention(16, 2, 256)
+    ws = a.workspace(t)
+    kd, vd = dev(k), dev(v)
+    qds = [dev(q) for q in qs]
+    eager = [a.run(q, kd, vd, ws=ws).clone() for q in qds]
+    q_in = qds[0].clone()
+    o = torch.empty((16, 256), dtype=torch.float32, device="cuda")
+    a.run(q_in, kd, vd, out=o, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        a.run(q_in, kd, vd, out=o, ws=ws)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            q_in.copy_(qds[i])
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, eager[i]), f"replay {rep} query {i}"
+            other = a.run(qds[(i + 1) % 3], kd, vd, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager[(i + 1) % 3])

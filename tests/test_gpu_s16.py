@@ -95,3 +95,28 @@ def test_s16_is_closer_to_unquantized_activations():
     e16, e8 = normwise(y16, wh), normwise(y8, wh)
     say(f"error vs unquantized activations: s16 {e16:.2e}, int8 {e8:.2e}")
     assert e16 * 100 < e8
+
+
+def test_s16_graph_replays_match_eager():
+    n, k = 4096, 4096
+    w = dev(synth.weights("q4_k", n, k, seed=69))
+    g = qg.GEMV("q4_k", n, k)
+    ws = g.workspace_s16()
+    xs = [dev(synth.activations(70 + i, 1, k)) for i in range(3)]
+    eager = [g.run_s16(w, x, ws=ws).clone() for x in xs]
+    x_in = xs[0].clone()
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    g.run_s16(w, x_in, y=y, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.run_s16(w, x_in, y=y, ws=ws)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            x_in.copy_(xs[i])
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager[i]), f"replay {rep} input {i}"
+            other = g.run_s16(w, xs[(i + 1) % 3], ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager[(i + 1) % 3])
