@@ -39,6 +39,9 @@ namespace {
 #endif
 
 constexpr int kAttnWaves = 4;
+#ifndef QG_ATTN_WGS_PER_CU
+#define QG_ATTN_WGS_PER_CU 1  // stage-1 workgroups per CU the chunking aims for (measured: 1 beats 2, 3, 4)
+#endif
 #ifndef QG_ATTN_BATCH
 #define QG_ATTN_BATCH 2
 #endif
@@ -631,9 +634,9 @@ AttnPlan attn_plan(const AttnShape& a) {
   const bool mf = attn_uses_mfma(a);
   const int64_t step = mf ? (int64_t)kAttnWaves * 16 : (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
   const int64_t min_chunk = mf ? step : step * kAttnBatch * 2;
-  // Enough chunks for two workgroups per CU (at most kMaxChunks), none
+  // Enough chunks for QG_ATTN_WGS_PER_CU workgroups per CU (at most kMaxChunks), none
   // shorter than two batched iterations of the workgroup.
-  int64_t want = ((int64_t)device_cu_count() * 2 + a.n_kv - 1) / a.n_kv;
+  int64_t want = ((int64_t)device_cu_count() * QG_ATTN_WGS_PER_CU + a.n_kv - 1) / a.n_kv;
   if (want > kMaxChunks) want = kMaxChunks;
   int64_t nch = (a.n_ctx + min_chunk - 1) / min_chunk;
   if (nch > want) nch = want;
