@@ -210,3 +210,22 @@ def test_s16_validation_before_launch():
     lib.qgemv_destroy(hk)
     assert lib.qgemv_debug_quantize_s16(a, a, a, a, 1, 100, None) == ESHAPE
     assert lib.qgemv_debug_quantize_s16(a + 4, a, a, a, 1, 128, None) == EALIGN
+
+
+def test_new_entry_points_report_injected_launch_failure(monkeypatch):
+    # With QGEMV_FAULT=launch a call that passes validation returns EHIP
+    # instead of launching (no device needed).
+    monkeypatch.setenv("QGEMV_FAULT", "launch")
+    a = 1 << 20
+    sz = ctypes.c_size_t()
+    assert lib.qattn_workspace_size(16, 2, 256, 4096, ctypes.byref(sz)) == OK
+    assert lib.qattn_decode(a, a, a, a, 16, 2, 256, 4096, a, sz.value, None) == EHIP
+    assert b"injected" in lib.qgemv_last_error()
+    d = _desc(fmt=3, n=64, k=4096)
+    h = ctypes.c_void_p()
+    assert lib.qgemv_create(ctypes.byref(h), ctypes.byref(d)) == OK
+    assert lib.qgemv_workspace_size_s16(h, ctypes.byref(sz)) == OK
+    assert lib.qgemv_run_s16(h, a, a, a, a, sz.value, None) == EHIP
+    assert lib.qgemv_debug_block_dots_s16(h, a, a, a, None) == EHIP
+    assert lib.qgemv_debug_quantize_s16(a, a, a, a, 1, 4096, None) == EHIP
+    lib.qgemv_destroy(h)
