@@ -103,3 +103,21 @@ def test_attention_graph_replays_match_eager():
             other = a.run(qds[(i + 1) % 3], kd, vd, ws=ws)
             torch.cuda.synchronize()
             assert torch.equal(other, eager[(i + 1) % 3])
+
+
+def _random_attention_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        d = int(rng.choice([128, 256]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.integers(1, 5))
+        t = int(rng.integers(1, 20000))
+        out.append((hkv * g, hkv, d, t))
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv,d,t", _random_attention_cases(12, 2027))
+def test_attention_random_shapes(hq, hkv, d, t):
+    o, ref, _ = _run(hq, hkv, d, t, seed=hq + 3 * t)
+    assert normwise(o, ref) <= TOL

@@ -320,3 +320,31 @@ def test_mfma_batched_parity(fmt, n, k, m):
     e = normwise(host(y).reshape(m, n), ref)
     say(f"  normwise error {e:.3e}")
     assert e <= TOL
+
+
+def _random_cases(count, seed):
+    # Seeded random shapes within the library's limits: every format, row
+    # counts that are not multiples of any tile, K from one block (or
+    # super-block) to 8192, 1..32 tokens (MFMA path from 9 tokens for Q4_K
+    # and Q6_K, token chunks above 16 for the others).
+    rng = np.random.default_rng(seed)
+    fmts = ["q4_0", "q8_0", "q4_k", "q6_k", "iq4_nl", "q5_k", "iq4_xs"]
+    out = []
+    for i in range(count):
+        fmt = fmts[i % len(fmts)]
+        be = 256 if fmt in ("q4_k", "q6_k", "q5_k", "iq4_xs") else 32
+        k = be * int(rng.integers(1, 8192 // be + 1))
+        n = int(rng.integers(1, 3000))
+        m = int(rng.choice([1, 1, 2, 3, 5, 8, 13, 17, 32]))
+        n = max(1, min(n, int(1.5e8 // (m * k))))  # keeps the oracle's integer dots to seconds
+        out.append((fmt, n, k, m))
+    return out
+
+
+@pytest.mark.parametrize("fmt,n,k,m", _random_cases(28, 2026))
+def test_gemv_random_shapes(fmt, n, k, m):
+    say(f"random gemv {fmt} n={n} k={k} m={m}")
+    g, w, x, xq, dx, sx, y, dots, canary, cb = _run_case(fmt, n, k, m, seed=n * 7 + k + m)
+    assert canary, "output guard band overwritten"
+    assert np.array_equal(dots, og.block_dots(fmt, w, n, k, xq, cb))
+    assert normwise(y, og.gemv_dequant(fmt, w, n, k, xq, dx, cb)) <= TOL
