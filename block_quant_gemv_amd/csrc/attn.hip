@@ -42,6 +42,9 @@ constexpr int kAttnWaves = 4;
 #ifndef QG_ATTN_WGS_PER_CU
 #define QG_ATTN_WGS_PER_CU 1  // stage-1 workgroups per CU the chunking aims for (measured: 1 beats 2, 3, 4)
 #endif
+#ifndef QG_ATTN_MIN_BATCHES
+#define QG_ATTN_MIN_BATCHES 2  // shortest chunk, in batched iterations of the workgroup
+#endif
 #ifndef QG_ATTN_BATCH
 #define QG_ATTN_BATCH 2
 #endif
@@ -633,9 +636,9 @@ AttnPlan attn_plan(const AttnShape& a) {
   // Tokens one workgroup iteration covers; a chunk is a whole number of them.
   const bool mf = attn_uses_mfma(a);
   const int64_t step = mf ? (int64_t)kAttnWaves * 16 : (int64_t)kAttnWaves * (64 / (a.head_dim / 8));
-  const int64_t min_chunk = mf ? step : step * kAttnBatch * 2;
+  const int64_t min_chunk = mf ? step : step * kAttnBatch * QG_ATTN_MIN_BATCHES;
   // Enough chunks for QG_ATTN_WGS_PER_CU workgroups per CU (at most kMaxChunks), none
-  // shorter than two batched iterations of the workgroup.
+  // shorter than QG_ATTN_MIN_BATCHES batched iterations of the workgroup.
   int64_t want = ((int64_t)device_cu_count() * QG_ATTN_WGS_PER_CU + a.n_kv - 1) / a.n_kv;
   if (want > kMaxChunks) want = kMaxChunks;
   int64_t nch = (a.n_ctx + min_chunk - 1) / min_chunk;
