@@ -13,7 +13,7 @@ Also reported (same run, after the timed region): microseconds per fused
 FFN sublayer (hidden 4096, intermediate 12288, Q4_K gate|up + Q6_K down),
 the IQ4_NL lm_head (4096 -> 248320), the Q4_0 2048 x 2048 GEMV, the Q5_K and
 IQ4_XS GEMVs (4096 -> 12288), the Q4_K GEMV with 16-bit activations
-(4096 -> 12288), the MoE layer (256 experts, top-8 + shared,
+(4096 -> 12288), the MoE layer (also with 16-bit activations) (256 experts, top-8 + shared,
 hidden 2048, intermediate 512) at M=1 and M=16, and the two-stage decode
 attention (16 query heads, 2 key/value heads, dimension 256) at 4K and 32K
 cached tokens.
@@ -480,6 +480,10 @@ def extras(qg, synth, torch):
         us = time_graph(gm, R, reps=16)
         res[f"moe_m{m}_us"] = round(us, 3)
         log(f"moe m={m}: {us:.2f} us")
+        gm = graph_of(lambda i: mo.run(wr, GU[i % R], DN[i % R], gsh, dsh, x, y=y, ws=ws, s16=True), R)
+        us = time_graph(gm, R, reps=16)
+        res[f"moe_s16_m{m}_us"] = round(us, 3)
+        log(f"moe s16 m={m}: {us:.2f} us")
     del GU, DN
     # Two-stage decode attention, 16 query heads over 2 key/value heads of
     # dimension 256, fp16 KV cache, at 4K and 32K cached tokens

@@ -58,6 +58,7 @@ _lib.qgemv_weight_bytes.argtypes = [_vp, _i32, ctypes.POINTER(_sz)]
 _lib.qgemv_run.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.qffn_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.qmoe_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.qmoe_run_s16.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.qgemv_quantize.argtypes = [_vp, _vp, _i32, _vp, _sz, _vp]
 _lib.qgemv_run_quantized.argtypes = [_vp, _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.qgemv_status_string.argtypes = [_i32]
@@ -71,7 +72,7 @@ _lib.qgemv_debug_quantize_s16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots_s16.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
 _lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
-for _f in ("qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
+for _f in ("qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
            "qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
@@ -314,7 +315,8 @@ class MoE(_Plan):
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
 
     def run(self, w_router, w_gateup, w_down, w_shared_gateup, w_shared_down, x, y=None, ws=None,
-            stream=None):
+            stream=None, s16=False):
+        """One MoE layer (qmoe_run; with s16=True, qmoe_run_s16: 16-bit activations)."""
         m = x.shape[0]
         if x.shape[-1] != self.hidden:
             raise ValueError(f"x must be [m, {self.hidden}]")
@@ -324,12 +326,14 @@ class MoE(_Plan):
             y = torch.empty((m, self.hidden), dtype=torch.float32, device=x.device)
         if ws is None:
             ws = self.workspace(m, x.device)
-        _check(_lib.qmoe_run(self._h, _dev(w_router, torch.float32, "w_router"),
-                             self._check_w(w_gateup, 0, "w_gateup"), self._check_w(w_down, 1, "w_down"),
-                             self._check_w(w_shared_gateup, 2, "w_shared_gateup"),
-                             self._check_w(w_shared_down, 3, "w_shared_down"),
-                             _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
-                             _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qmoe_run")
+        fn = _lib.qmoe_run_s16 if s16 else _lib.qmoe_run
+        _check(fn(self._h, _dev(w_router, torch.float32, "w_router"),
+                  self._check_w(w_gateup, 0, "w_gateup"), self._check_w(w_down, 1, "w_down"),
+                  self._check_w(w_shared_gateup, 2, "w_shared_gateup"),
+                  self._check_w(w_shared_down, 3, "w_shared_down"),
+                  _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
+                  _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+               "qmoe_run_s16" if s16 else "qmoe_run")
         return y
 
 

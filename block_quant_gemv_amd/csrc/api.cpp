@@ -114,6 +114,9 @@ Layout layout_of(const qgemv_plan* h, int m) {
     L.add("hs", slots * (d.inter / 32) * 4);
     L.add("out", slots * d.hidden * 4);
     L.add("tbl", (size_t)moe_table_ints(m, d.top_k) * 4);
+    // 16-bit activation codes of x and h (qmoe_run_s16)
+    L.add("xq16", (size_t)m * d.hidden * 2);
+    L.add("hq16", slots * d.inter * 2);
   }
   return L;
 }
@@ -447,27 +450,32 @@ int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x
   return check_launch(launch_gemv(d.fmt_down, q, false, s), "down gemv");
 }
 
-int qmoe_run(qgemv_t h, const float* w_router, const void* w_experts_gateup, const void* w_experts_down,
-             const void* w_shared_gateup, const void* w_shared_down, const float* x, float* y, int m,
-             void* ws, size_t ws_bytes, void* stream) {
-  if (!h || h->d.kind != QKIND_MOE) return fail(QGEMV_EINVAL, "qmoe_run: not a MoE plan");
+namespace {
+int moe_run(qgemv_t h, const float* w_router, const void* w_experts_gateup, const void* w_experts_down,
+            const void* w_shared_gateup, const void* w_shared_down, const float* x, float* y, int m, void* ws,
+            size_t ws_bytes, void* stream, bool s16, const char* fn) {
+  if (!h || h->d.kind != QKIND_MOE) return fail(QGEMV_EINVAL, "%s: not a MoE plan", fn);
   if (!w_router || !w_experts_gateup || !w_experts_down || !w_shared_gateup || !w_shared_down || !x ||
       !y || !ws)
-    return fail(QGEMV_EINVAL, "qmoe_run: null pointer");
+    return fail(QGEMV_EINVAL, "%s: null pointer", fn);
   if (!aligned(w_router, 16) || !aligned(w_experts_gateup, 16) || !aligned(w_experts_down, 16) ||
       !aligned(w_shared_gateup, 16) || !aligned(w_shared_down, 16) || !aligned(x, 16) ||
       !aligned(y, 4) || !aligned(ws, 256))
-    return fail(QGEMV_EALIGN, "qmoe_run: weights and x need 16-byte, y 4-byte, ws 256-byte alignment");
+    return fail(QGEMV_EALIGN, "%s: weights and x need 16-byte, y 4-byte, ws 256-byte alignment", fn);
   const qgemv_desc& d = h->d;
-  if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "qmoe_run: m=%d not in 1..%d", m, d.max_m);
+  if (m < 1 || m > d.max_m) return fail(QGEMV_ESHAPE, "%s: m=%d not in 1..%d", fn, m, d.max_m);
   const int64_t gu_bytes = 2 * d.inter * fmt_row_bytes(d.fmt_expert, d.hidden);
   const int64_t dn_bytes = d.hidden * fmt_row_bytes(d.fmt_expert, d.inter);
   if (gu_bytes % 16 || dn_bytes % 16)
-    return fail(QGEMV_ESHAPE, "qmoe_run: expert matrices must be multiples of 16 bytes");
+    return fail(QGEMV_ESHAPE, "%s: expert matrices must be multiples of 16 bytes", fn);
+  if (s16 && d.fmt_expert != QFMT_Q4_0)
+    return fail(QGEMV_EFORMAT, "%s: 16-bit activations need Q4_0 experts", fn);
+  if (s16 && (!q40_s16_grouped_ok(d.hidden) || !q40_s16_grouped_ok(d.inter)))
+    return fail(QGEMV_ESHAPE, "%s: 16-bit experts need hidden and inter in {512, 1024, 2048, 4096}", fn);
   const Layout L = layout_of(h, m);
   if (ws_bytes < L.total())
-    return fail(QGEMV_EWORKSPACE, "qmoe_run: workspace %zu < %zu bytes", ws_bytes, L.total());
-  if (fault_injected()) return fail(QGEMV_EHIP, "qmoe_run: launch failure injected (QGEMV_FAULT)");
+    return fail(QGEMV_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, L.total());
+  if (fault_injected()) return fail(QGEMV_EHIP, "%s: launch failure injected (QGEMV_FAULT)", fn);
   MoeCall c;
   c.router = w_router;
   c.gu = static_cast<const uint8_t*>(w_experts_gateup);
@@ -498,7 +506,26 @@ int qmoe_run(qgemv_t h, const float* w_router, const void* w_experts_gateup, con
   c.hs = region<int32_t>(ws, L, "hs");
   c.out = region<float>(ws, L, "out");
   c.tbl = region<int32_t>(ws, L, "tbl");
+  if (s16) {
+    c.xq16 = region<int16_t>(ws, L, "xq16");
+    c.hq16 = region<int16_t>(ws, L, "hq16");
+  }
   return check_launch(launch_moe(c, static_cast<hipStream_t>(stream)), "moe");
+}
+}  // namespace
+
+int qmoe_run(qgemv_t h, const float* w_router, const void* w_experts_gateup, const void* w_experts_down,
+             const void* w_shared_gateup, const void* w_shared_down, const float* x, float* y, int m,
+             void* ws, size_t ws_bytes, void* stream) {
+  return moe_run(h, w_router, w_experts_gateup, w_experts_down, w_shared_gateup, w_shared_down, x, y, m, ws,
+                 ws_bytes, stream, false, "qmoe_run");
+}
+
+int qmoe_run_s16(qgemv_t h, const float* w_router, const void* w_experts_gateup, const void* w_experts_down,
+                 const void* w_shared_gateup, const void* w_shared_down, const float* x, float* y, int m,
+                 void* ws, size_t ws_bytes, void* stream) {
+  return moe_run(h, w_router, w_experts_gateup, w_experts_down, w_shared_gateup, w_shared_down, x, y, m, ws,
+                 ws_bytes, stream, true, "qmoe_run_s16");
 }
 
 int qgemv_debug_quantize(const float* x, int8_t* xq, float* dx, int32_t* sx, int m, int64_t k, void* stream) {

@@ -31,6 +31,11 @@ struct MoeCall {
   int32_t* hs = nullptr;
   float* out = nullptr;      // [m*(top_k+1), hidden]
   int32_t* tbl = nullptr;    // grouping table, moe_table_ints(m, top_k) ints
+  // 16-bit activation variant (Q4_0 experts): when set, x and h are
+  // quantized to int16 codes here (dx/sx and hd/hs then hold their scales
+  // and sums) and the expert GEMVs run on them.
+  int16_t* xq16 = nullptr;   // [m, hidden]
+  int16_t* hq16 = nullptr;   // [m*(top_k+1), inter]
 };
 
 // int32 entries of the expert grouping table for m tokens and top_k slots.

@@ -26,6 +26,7 @@
 #include "common.cuh"
 #include "internal.h"
 #include "moe.h"
+#include "s16.h"
 #include "swiglu.h"
 
 namespace qg {
@@ -296,6 +297,12 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
                      c.xq, c.dx, c.sx, c.n_experts, c.hidden, c.m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool s16 = c.xq16 != nullptr;
+  if (s16) {  // the expert GEMVs read 16-bit codes of x (scales and sums replace the Q8 ones)
+    if (kGroupTokens != 1 || !c.hq16 || !q40_s16_grouped_ok(c.hidden) || !q40_s16_grouped_ok(c.inter))
+      return hipErrorInvalidValue;
+    if ((e = launch_quant_s16(c.x, c.xq16, c.dx, c.sx, (int64_t)c.m * c.hidden / 32, s)) != hipSuccess) return e;
+  }
   // 2. top-k, softmax and grouping
   const int npairs = c.m * c.top_k;
   const size_t lds = (2 * (size_t)c.n_experts + 3 * (size_t)npairs + 1) * 4;
@@ -330,11 +337,31 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   g.k = c.hidden;
   g.m = c.m;
   for (int i = 0; i < 4; ++i) g.cb[i] = c.cb[i];
-  if ((e = launch_gemv(c.fmt, g, false, s)) != hipSuccess) return e;
-  // 4. SwiGLU + re-quantization for every slot row
-  if ((e = launch_swiglu_q8(c.gu_out, 2 * c.inter, c.h, c.hq, c.hd, c.hs, (int64_t)c.m * slots, c.inter,
-                            s)) != hipSuccess)
+  S16Grouped a;
+  if (s16) {
+    a.w = c.gu;
+    a.w_stride = c.gu_stride;
+    a.w_shared = c.gu_shared;
+    a.tbl = c.tbl;
+    a.tbl_stride = 2 + kGroupTokens;
+    a.nprob = maxprob;
+    a.xq = c.xq16;
+    a.dx = c.dx;
+    a.sx = c.sx;
+    a.xs = c.hidden;
+    a.act_div = slots;
+    a.y = c.gu_out;
+    a.ldy = 2 * c.inter;
+    a.n = 2 * c.inter;
+    a.k = c.hidden;
+    if ((e = launch_q40_s16_grouped(a, s)) != hipSuccess) return e;
+  } else if ((e = launch_gemv(c.fmt, g, false, s)) != hipSuccess) {
     return e;
+  }
+  // 4. SwiGLU + re-quantization for every slot row
+  e = s16 ? launch_swiglu_s16(c.gu_out, 2 * c.inter, c.h, c.hq16, c.hd, c.hs, (int64_t)c.m * slots, c.inter, s)
+          : launch_swiglu_q8(c.gu_out, 2 * c.inter, c.h, c.hq, c.hd, c.hs, (int64_t)c.m * slots, c.inter, s);
+  if (e != hipSuccess) return e;
   // 5. down of the used experts and the shared expert
   GemvProblem d = g;
   d.w = c.dn;
@@ -348,7 +375,23 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   d.ldy = c.hidden;
   d.n = c.hidden;
   d.k = c.inter;
-  if ((e = launch_gemv(c.fmt, d, false, s)) != hipSuccess) return e;
+  if (s16) {
+    a.w = c.dn;
+    a.w_stride = c.dn_stride;
+    a.w_shared = c.dn_shared;
+    a.xq = c.hq16;
+    a.dx = c.hd;
+    a.sx = c.hs;
+    a.xs = c.inter;
+    a.act_div = 1;
+    a.y = c.out;
+    a.ldy = c.hidden;
+    a.n = c.hidden;
+    a.k = c.inter;
+    if ((e = launch_q40_s16_grouped(a, s)) != hipSuccess) return e;
+  } else if ((e = launch_gemv(c.fmt, d, false, s)) != hipSuccess) {
+    return e;
+  }
   // 6. weighted combine
   const int64_t total = (int64_t)c.m * c.hidden;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, c.out, c.wts,

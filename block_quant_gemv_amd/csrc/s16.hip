@@ -261,3 +261,186 @@ hipError_t launch_kquant_s16(int fmt, const uint8_t* w, const int16_t* xq, const
 }
 
 }  // namespace qg
+
+// ---------------------------------------------------------------------------
+// MoE experts on 16-bit activations (the layer where the pages used them).
+
+namespace qg {
+
+namespace {
+
+// Grouped single-token Q4_0 GEMV on 16-bit codes. grid = (workgroups per
+// entry, entries); entry e of the grouping table is {expert (-1: shared),
+// token count (1), output row}; its activation row is output row / act_div.
+// LPR lanes per row (one 18-byte block each, JB blocks per lane): a block is
+// read as five aligned dwords around it (its offset is even; rows and
+// matrices are multiples of 4 bytes, so the window never passes the
+// matrix's end), its 16 code bytes re-aligned with one byte shift when the
+// block starts at 2 mod 4. The nibble order is the K-quant sub-block's, so
+// the int16 pairing of the Q4_K kernel applies; the -8 offset is the block
+// sum: D = sum x16 * q - 8 * sum x16.
+template <int LPR, int JB>
+__global__ __launch_bounds__(kWaves16 * 64) void q40_s16_grouped_kernel(
+    const uint8_t* __restrict__ W, int64_t w_stride, const uint8_t* __restrict__ W_shared,
+    const int32_t* __restrict__ tbl, int tbl_stride, const int16_t* __restrict__ xq, const float* __restrict__ dx,
+    const int32_t* __restrict__ sx, int64_t xs, int act_div, float* __restrict__ y, int64_t ldy, int64_t n) {
+  const int prob = blockIdx.y;
+  if (prob >= tbl[0]) return;  // whole workgroup, before any cross-lane step
+  const int32_t* ent = tbl + 1 + (int64_t)prob * tbl_stride;
+  const uint8_t* Wm = ent[0] < 0 ? W_shared : W + (int64_t)ent[0] * w_stride;
+  const int64_t orow = ent[2];
+  const int64_t arow = orow / act_div;
+  constexpr int U = LPR * JB;       // blocks per row
+  constexpr int RPP = 64 / LPR;     // rows per wave pass
+  constexpr int RB = U * 18;        // row bytes
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane / LPR, lb = lane % LPR;
+
+  uint32_t xa[JB][16];
+  float xd[JB];
+  int xsum[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int b = lb + LPR * j;
+    const int4* p = reinterpret_cast<const int4*>(xq + arow * xs + 32 * b);
+    const int4 a0 = p[0], a1 = p[1], a2 = p[2], a3 = p[3];
+    const uint32_t w[16] = {(uint32_t)a0.x, (uint32_t)a0.y, (uint32_t)a0.z, (uint32_t)a0.w,
+                            (uint32_t)a1.x, (uint32_t)a1.y, (uint32_t)a1.z, (uint32_t)a1.w,
+                            (uint32_t)a2.x, (uint32_t)a2.y, (uint32_t)a2.z, (uint32_t)a2.w,
+                            (uint32_t)a3.x, (uint32_t)a3.y, (uint32_t)a3.z, (uint32_t)a3.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xa[j][4 * i + 0] = perm(w[2 * i + 1], w[2 * i], 0x05040100u);
+      xa[j][4 * i + 1] = perm(w[2 * i + 1], w[2 * i], 0x07060302u);
+      xa[j][4 * i + 2] = perm(w[9 + 2 * i], w[8 + 2 * i], 0x05040100u);
+      xa[j][4 * i + 3] = perm(w[9 + 2 * i], w[8 + 2 * i], 0x07060302u);
+    }
+    xd[j] = dx[arow * (xs / 32) + b];
+    xsum[j] = sx[arow * (xs / 32) + b];
+  }
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Wm), 0, (int)(n * RB), kBuf3);
+  const int64_t gw = (int64_t)blockIdx.x * kWaves16 + wid;
+  const int64_t nw = (int64_t)gridDim.x * kWaves16;
+  for (int64_t r0 = gw * RPP; r0 < n; r0 += nw * RPP) {
+    const int64_t row = r0 + lr;
+    float acc = 0.0f;
+    if (row < n) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int off = (int)(row * RB) + 18 * (lb + LPR * j);
+        const int base = off & ~3;
+        uint32_t dw[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) dw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, base + 4 * i, 0, 2);
+        const bool odd = (off & 3) != 0;  // block starts at 2 mod 4
+        const float d = half_bits(odd ? (dw[0] >> 16) : (dw[0] & 0xffffu));
+        int D = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t q = odd ? dw[i + 1] : alignbyte(dw[i + 1], dw[i], 2);
+          D = dot2(q & 0x000F000Fu, xa[j][4 * i + 0], D);
+          D = dot2((q >> 8) & 0x000F000Fu, xa[j][4 * i + 1], D);
+          D = dot2((q >> 4) & 0x000F000Fu, xa[j][4 * i + 2], D);
+          D = dot2((q >> 12) & 0x000F000Fu, xa[j][4 * i + 3], D);
+        }
+        D -= 8 * xsum[j];
+        acc = fmaf(xd[j] * d, (float)D, acc);
+      }
+    }
+    const float sum = group_sum(acc, LPR);
+    if (lb == 0 && row < n) y[orow * ldy + row] = sum;
+  }
+}
+
+// SwiGLU + 16-bit re-quantization of h, eight lanes per 32-element block
+// (the stand-alone SwiGLU kernel's layout with the 16-bit rule).
+__global__ __launch_bounds__(256) void swiglu_s16_kernel(const float* __restrict__ gu, int64_t gu_ld,
+                                                         float* __restrict__ h, int16_t* __restrict__ hq,
+                                                         float* __restrict__ hd, int32_t* __restrict__ hs,
+                                                         int64_t rows, int64_t inter) {
+  const int64_t nbr = inter / 32;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gt >> 3;
+  const int part = (int)(gt & 7);
+  if (blk >= rows * nbr) return;  // whole groups of eight lanes leave together
+  const int64_t r = blk / nbr, b = blk - r * nbr;
+  const int64_t col = b * 32 + part * 4;
+  const float4 g = *reinterpret_cast<const float4*>(gu + r * gu_ld + col);
+  const float4 u = *reinterpret_cast<const float4*>(gu + r * gu_ld + inter + col);
+  float4 v;
+  v.x = g.x / (1.0f + expf(-g.x)) * u.x;
+  v.y = g.y / (1.0f + expf(-g.y)) * u.y;
+  v.z = g.z / (1.0f + expf(-g.z)) * u.z;
+  v.w = g.w / (1.0f + expf(-g.w)) * u.w;
+  *reinterpret_cast<float4*>(h + r * inter + col) = v;
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = max8(a);
+  const float d = (a > 0.0f) ? a / 32767.0f : 0.0f;
+  int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+  if (d != 0.0f) {
+    q0 = code16(v.x, d);
+    q1 = code16(v.y, d);
+    q2 = code16(v.z, d);
+    q3 = code16(v.w, d);
+  }
+  uint2 packed;
+  packed.x = ((uint32_t)q0 & 0xffffu) | ((uint32_t)q1 << 16);
+  packed.y = ((uint32_t)q2 & 0xffffu) | ((uint32_t)q3 << 16);
+  *reinterpret_cast<uint2*>(hq + r * inter + col) = packed;
+  int s = q0 + q1 + q2 + q3;
+  s = sum4(s);
+  s += other_quad(s);
+  if (part == 0) {
+    hd[r * nbr + b] = d;
+    hs[r * nbr + b] = s;
+  }
+}
+
+template <int LPR, int JB>
+hipError_t launch_q40g(const S16Grouped& a, hipStream_t s) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  // Workgroups per entry: enough row passes for every wave, and no more
+  // workgroups in all than about four per CU resident at once.
+  constexpr int RPP = 64 / LPR;
+  int64_t per = ((int64_t)cus * 4 + a.nprob - 1) / a.nprob;
+  const int64_t need = (a.n + (int64_t)kWaves16 * RPP - 1) / ((int64_t)kWaves16 * RPP);
+  if (per > need) per = need;
+  if (per < 1) per = 1;
+  hipLaunchKernelGGL((q40_s16_grouped_kernel<LPR, JB>), dim3((unsigned)per, (unsigned)a.nprob),
+                     dim3(kWaves16 * 64), 0, s, a.w, a.w_stride, a.w_shared, a.tbl, a.tbl_stride, a.xq, a.dx, a.sx,
+                     a.xs, a.act_div, a.y, a.ldy, a.n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool q40_s16_grouped_ok(int64_t k) { return k == 512 || k == 1024 || k == 2048 || k == 4096; }
+
+hipError_t launch_q40_s16_grouped(const S16Grouped& a, hipStream_t s) {
+  if (!q40_s16_grouped_ok(a.k) || a.n < 1 || a.nprob < 1) return hipErrorInvalidValue;
+  switch (a.k) {
+    case 512: return launch_q40g<16, 1>(a, s);
+    case 1024: return launch_q40g<32, 1>(a, s);
+    case 2048: return launch_q40g<64, 1>(a, s);
+    default: return launch_q40g<64, 2>(a, s);
+  }
+}
+
+hipError_t launch_swiglu_s16(const float* gu, int64_t gu_ld, float* h, int16_t* hq, float* hd, int32_t* hs,
+                             int64_t rows, int64_t inter, hipStream_t s) {
+  const int64_t threads = rows * (inter / 32) * 8;
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_s16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, gu, gu_ld, h,
+                     hq, hd, hs, rows, inter);
+  return hipGetLastError();
+}
+
+}  // namespace qg

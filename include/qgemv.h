@@ -235,6 +235,21 @@ int qmoe_run(qgemv_t h, const float *w_router, const void *w_experts_gateup,
              void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable text of a status code (static string). */
+/* qmoe_run with 16-bit activations: x and every expert's h are quantized to
+ * 32-element blocks of int16 codes (scale absmax / 32767), the fix the
+ * issue ledger of "01 · Phase overview: from 2B to 8B to MoE" (icman.com.cn,
+ * item ⑫) applied to its MoE FFN when int8 activation error compounded over
+ * 48 layers. Router, top-k, grouping and combine are those of qmoe_run; the
+ * expert GEMVs run on int16 x 4-bit products. Needs QFMT_Q4_0 experts
+ * (QGEMV_EFORMAT) with hidden and inter in {512, 1024, 2048, 4096}
+ * (QGEMV_ESHAPE). Same workspace as qmoe_run: it also writes the regions
+ * "xq16" (int16 [m, hidden]) and "hq16" (int16 [m*(top_k+1), inter]); "dx",
+ * "sx", "hd", "hs" then hold the 16-bit blocks' scales and sums. */
+int qmoe_run_s16(qgemv_t h, const float *w_router, const void *w_experts_gateup,
+                 const void *w_experts_down, const void *w_shared_gateup,
+                 const void *w_shared_down, const float *x, float *y, int m,
+                 void *ws, size_t ws_bytes, void *stream);
+
 const char *qgemv_status_string(int status);
 /* Message of the calling thread's last failed call ("" if none). */
 const char *qgemv_last_error(void);

@@ -19,7 +19,9 @@ Readings:
 * The shared expert has the shape and format of a routed expert and is added
   with weight 1.
 * Every expert of a token uses that token's single Q8 quantization of x; each
-  expert's h is re-quantized to Q8 before its down projection.
+  expert's h is re-quantized to Q8 before its down projection. The 16-bit
+  variant (quant=quantize_s16) uses the 16-bit rule for both ("01 · Phase
+  overview: from 2B to 8B to MoE", icman.com.cn, issue ledger item ⑫).
 * The combine sums slots 0..k-1 in order, then adds the shared expert.
 """
 from __future__ import annotations
@@ -55,11 +57,12 @@ def topk_weights(logits, ids):
     return z / z.sum(axis=1, keepdims=True)
 
 
-def expert_chain(w_gu, w_dn, xq, dx, hidden, inter, fmt="q4_0"):
-    """One expert on quantized input: returns dict(gu, h, hq, hd, hs, out)."""
+def expert_chain(w_gu, w_dn, xq, dx, hidden, inter, fmt="q4_0", quant=quantize_q8):
+    """One expert on quantized input: returns dict(gu, h, hq, hd, hs, out).
+    quant re-quantizes h (Q8, or the 16-bit variant)."""
     gu = gemv_dequant(fmt, w_gu, 2 * inter, hidden, xq, dx)
     h = swiglu(gu, inter)
-    hq, hd, hs = quantize_q8(h.astype(np.float32))
+    hq, hd, hs = quant(h.astype(np.float32))
     out = gemv_dequant(fmt, w_dn, hidden, inter, hq, hd)
     return {"gu": gu, "h": h, "hq": hq, "hd": hd, "hs": hs, "out": out}
 
@@ -77,7 +80,7 @@ def combine(outs, w, shared_out):
 
 
 def moe_ref(w_router, gu_all, dn_all, gu_shared, dn_shared, x, hidden, inter, top_k,
-            fmt="q4_0"):
+            fmt="q4_0", quant=quantize_q8):
     """Fully independent chain for every token. Returns dict of stages."""
     from .formats import row_bytes as _rb
     x = np.atleast_2d(np.asarray(x, np.float32))
@@ -89,13 +92,13 @@ def moe_ref(w_router, gu_all, dn_all, gu_shared, dn_shared, x, hidden, inter, to
     w = topk_weights(logits, ids)
     y = np.zeros((m, hidden), np.float64)
     for t in range(m):
-        xq, dx, _ = quantize_q8(x[t:t + 1])
+        xq, dx, _ = quant(x[t:t + 1])
         outs = []
         for kk in range(top_k):
             e = int(ids[t, kk])
             ch = expert_chain(gu_all[e * sz_gu:(e + 1) * sz_gu], dn_all[e * sz_dn:(e + 1) * sz_dn],
-                              xq, dx, hidden, inter, fmt)
+                              xq, dx, hidden, inter, fmt, quant)
             outs.append(ch["out"][0])
-        sh = expert_chain(gu_shared, dn_shared, xq, dx, hidden, inter, fmt)["out"][0]
+        sh = expert_chain(gu_shared, dn_shared, xq, dx, hidden, inter, fmt, quant)["out"][0]
         y[t] = combine(outs, w[t], sh)
     return {"logits": logits, "ids": ids, "w": w, "y": y}

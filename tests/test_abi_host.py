@@ -229,3 +229,22 @@ def test_new_entry_points_report_injected_launch_failure(monkeypatch):
     assert lib.qgemv_debug_block_dots_s16(h, a, a, a, None) == EHIP
     assert lib.qgemv_debug_quantize_s16(a, a, a, a, 1, 4096, None) == EHIP
     lib.qgemv_destroy(h)
+
+
+def test_moe_s16_validation_before_launch():
+    a = 1 << 20
+    d = qg._Desc()
+    d.kind, d.layout_version, d.max_m = 2, 1, 1
+    d.hidden, d.inter, d.n_experts, d.top_k, d.fmt_expert = 2048, 512, 16, 4, 2  # Q8_0 experts
+    h = ctypes.c_void_p()
+    assert lib.qgemv_create(ctypes.byref(h), ctypes.byref(d)) == OK
+    sz = ctypes.c_size_t()
+    assert lib.qgemv_workspace_size(h, 1, ctypes.byref(sz)) == OK
+    assert lib.qmoe_run_s16(h, a, a, a, a, a, a, a, 1, a, sz.value, None) == EFORMAT
+    lib.qgemv_destroy(h)
+    d.fmt_expert, d.inter = 1, 768  # Q4_0, but inter not in {512, 1024, 2048, 4096}
+    assert lib.qgemv_create(ctypes.byref(h), ctypes.byref(d)) == OK
+    assert lib.qgemv_workspace_size(h, 1, ctypes.byref(sz)) == OK
+    assert lib.qmoe_run_s16(h, a, a, a, a, a, a, a, 1, a, sz.value, None) == ESHAPE
+    assert lib.qmoe_run_s16(h, a, a, a, a, a, None, a, 1, a, sz.value, None) == EINVAL
+    lib.qgemv_destroy(h)
