@@ -14,6 +14,8 @@ precision:
 * `quant.quantize_q8`: the on-device activation quantizer (32-element int8
   blocks with an fp32 scale), whose decisions are taken in fp32 as the method
   states them.
+* `quant.quantize_s16`: its 16-bit variant (int16 codes, scale absmax/32767),
+  used by the 16-bit GEMV and MoE paths.
 * `formats`: the seven block layouts (five from the decode workloads, plus
   Q5_K and IQ4_XS), byte-level decode and encode.
 * `gemv`: the GEMV y = W_hat . x_hat in two independent forms -- the
