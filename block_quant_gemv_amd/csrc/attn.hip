@@ -83,84 +83,107 @@ struct AState {
   float m[G], l[G], acc[G][8];
 };
 
-// Merge state b into a (both over disjoint token sets), base-2 exponents.
-template <int G>
-QG_DEV void merge_into(AState<G>& a, const float (&mb)[G], const float (&lb)[G], const float (&ob)[G][8]) {
+// One row of the merge buffer: the 8-dimension sums of every lane at 0 .. D-1
+// (16-byte aligned for 128-bit LDS accesses), then m and l.
+template <int D>
+constexpr int kRedRow = D + 4;
+
+// Combine the states of the two halves of the lane set that a lane swap
+// pairs up (the permlane call returns both partners' values in every lane).
+template <int G, bool ROWS16>
+QG_DEV void swap_merge(AState<G>& st) {
+  auto sw = [](float v) __attribute__((always_inline)) {
+    if constexpr (ROWS16) return __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    else return __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  };
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const float M = fmaxf(a.m[j], mb[j]);
-    const float ca = a.m[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.m[j] - M);
-    const float cb = mb[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb[j] - M);
-    a.m[j] = M;
-    a.l[j] = a.l[j] * ca + lb[j] * cb;
+    const auto mm = sw(st.m[j]);
+    const auto ll = sw(st.l[j]);
+    const float ma = __uint_as_float(mm[0]), mb = __uint_as_float(mm[1]);
+    const float M = fmaxf(ma, mb);
+    const float ca = ma == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ma - M);
+    const float cb = mb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - M);
+    st.m[j] = M;
+    st.l[j] = __uint_as_float(ll[0]) * ca + __uint_as_float(ll[1]) * cb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a.acc[j][i] = a.acc[j][i] * ca + ob[j][i] * cb;
+    for (int i = 0; i < 8; ++i) {
+      const auto aa = sw(st.acc[j][i]);
+      st.acc[j][i] = __uint_as_float(aa[0]) * ca + __uint_as_float(aa[1]) * cb;
+    }
   }
 }
 
-// Merge the per-lane states of a workgroup through LDS in a fixed order --
-// first the token slots of each wave into slot 0 (one slot per round), then
-// waves 1..3 into wave 0 -- and write the chunk's partial (or, for a single
-// chunk, the normalised output). Lane (slot, dl) holds dimensions
-// 8 dl .. 8 dl + 7 of every head of its group.
+// Merge the per-lane states of a workgroup in a fixed order and write the
+// chunk's partial (or, for a single chunk, the normalised output). Lane
+// (slot, dl) holds dimensions 8 dl .. 8 dl + 7 of every head of its group.
+// First the token slots of each wave: with two slots (32-lane halves) one
+// cross-half swap per value; with four (16-lane rows) a row swap, then the
+// half swap, so every slot ends up with the wave's total. Then each wave
+// stores its state in LDS and the G heads are spread over the workgroup's
+// slots: the slot that owns head j merges waves 0, 1, 2, 3 in that order.
 template <int D, int G>
-QG_DEV void attn_finish(AState<G>& st, float (&red)[kAttnWaves][G][2 + D], int wid, int lane, int c, int kvh,
-                        int nchunks, float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl,
-                        float* __restrict__ po) {
+QG_DEV void attn_finish(AState<G>& st, float (&red)[kAttnWaves][G][kRedRow<D>], int wid, int lane, int c,
+                        int kvh, int nchunks, float* __restrict__ out, float* __restrict__ pm,
+                        float* __restrict__ pl, float* __restrict__ po) {
   constexpr int LPT = D / 8;
   constexpr int TPW = 64 / LPT;
+  static_assert(TPW == 2 || TPW == 4, "token slots per wave");
   const int dl = lane % LPT;
   const int slot = lane / LPT;
-  auto put = [&](int w) __attribute__((always_inline)) {
+  if constexpr (TPW == 4) swap_merge<G, true>(st);
+  swap_merge<G, false>(st);
+  if (slot == 0) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       if (dl == 0) {
-        red[w][j][0] = st.m[j];
-        red[w][j][1] = st.l[j];
+        red[wid][j][D] = st.m[j];
+        red[wid][j][D + 1] = st.l[j];
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) red[w][j][2 + 8 * dl + i] = st.acc[j][i];
+      float4* r = reinterpret_cast<float4*>(&red[wid][j][8 * dl]);
+      r[0] = make_float4(st.acc[j][0], st.acc[j][1], st.acc[j][2], st.acc[j][3]);
+      r[1] = make_float4(st.acc[j][4], st.acc[j][5], st.acc[j][6], st.acc[j][7]);
     }
-  };
-  auto take = [&](int w) __attribute__((always_inline)) {
-    float mb[G], lb[G], ob[G][8];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      mb[j] = red[w][j][0];
-      lb[j] = red[w][j][1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ob[j][i] = red[w][j][2 + 8 * dl + i];
-    }
-    merge_into<G>(st, mb, lb, ob);
-  };
-#pragma unroll 1
-  for (int sl = 1; sl < TPW; ++sl) {
-    if (slot == sl) put(wid);
-    __syncthreads();
-    if (slot == 0) take(wid);
-    __syncthreads();
   }
-  if (slot == 0) put(wid);
   __syncthreads();
-  if (wid != 0 || slot != 0) return;
+  constexpr int kOwners = kAttnWaves * TPW;
 #pragma unroll 1
-  for (int w = 1; w < kAttnWaves; ++w) take(w);
+  for (int j = wid * TPW + slot; j < G; j += kOwners) {
+    float m = red[0][j][D], l = red[0][j][D + 1];
+    float a[8];
+    {
+      const float4* r = reinterpret_cast<const float4*>(&red[0][j][8 * dl]);
+      const float4 u = r[0], v = r[1];
+      a[0] = u.x, a[1] = u.y, a[2] = u.z, a[3] = u.w, a[4] = v.x, a[5] = v.y, a[6] = v.z, a[7] = v.w;
+    }
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
+    for (int w = 1; w < kAttnWaves; ++w) {
+      const float mb = red[w][j][D], lb = red[w][j][D + 1];
+      const float4* r = reinterpret_cast<const float4*>(&red[w][j][8 * dl]);
+      const float4 u = r[0], v = r[1];
+      const float b[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+      const float M = fmaxf(m, mb);
+      const float ca = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      const float cb = mb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - M);
+      m = M;
+      l = l * ca + lb * cb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = a[i] * ca + b[i] * cb;
+    }
     const int64_t h = (int64_t)kvh * G + j;
     if (nchunks == 1) {
-      const float inv = 1.0f / st.l[j];
+      const float inv = 1.0f / l;
       float4* op = reinterpret_cast<float4*>(out + h * D + 8 * dl);
-      op[0] = make_float4(st.acc[j][0] * inv, st.acc[j][1] * inv, st.acc[j][2] * inv, st.acc[j][3] * inv);
-      op[1] = make_float4(st.acc[j][4] * inv, st.acc[j][5] * inv, st.acc[j][6] * inv, st.acc[j][7] * inv);
+      op[0] = make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+      op[1] = make_float4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
     } else {
       if (dl == 0) {
-        pm[h * nchunks + c] = st.m[j];
-        pl[h * nchunks + c] = st.l[j];
+        pm[h * nchunks + c] = m;
+        pl[h * nchunks + c] = l;
       }
       float4* op = reinterpret_cast<float4*>(po + (h * nchunks + c) * D + 8 * dl);
-      op[0] = make_float4(st.acc[j][0], st.acc[j][1], st.acc[j][2], st.acc[j][3]);
-      op[1] = make_float4(st.acc[j][4], st.acc[j][5], st.acc[j][6], st.acc[j][7]);
+      op[0] = make_float4(a[0], a[1], a[2], a[3]);
+      op[1] = make_float4(a[4], a[5], a[6], a[7]);
     }
   }
 }
@@ -174,7 +197,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_kernel(
     int64_t n_ctx, int64_t chunk, int nchunks, float qscale) {
   constexpr int LPT = D / 8;          // lanes per token
   constexpr int TPW = 64 / LPT;       // tokens per wave load
-  __shared__ float red[kAttnWaves][G][2 + D];
+  __shared__ __align__(16) float red[kAttnWaves][G][kRedRow<D>];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_mfma_kernel(
     float* __restrict__ out, float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po,
     int64_t n_ctx, int64_t chunk, int nchunks, float qscale) {
   constexpr int D = 256, G = 8;
-  __shared__ float red[kAttnWaves][G][2 + D];
+  __shared__ __align__(16) float red[kAttnWaves][G][kRedRow<D>];
   __shared__ float pbuf[kAttnWaves][16][G];
 
   const int lane = threadIdx.x & 63;
