@@ -520,7 +520,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_mfma_kernel(
 // block (one per lane, up to 16 loads in flight), and wave 0 adds the four
 // sums in wave order.
 constexpr int kMergeWaves = 4;
-constexpr int kMergeUnroll = 16;
+#ifndef QG_MERGE_UNROLL
+#define QG_MERGE_UNROLL 32
+#endif
+constexpr int kMergeUnroll = QG_MERGE_UNROLL;  // partial outputs a merge wave loads per pass
 constexpr int kMaxChunks = 1024;
 
 QG_DEV float block_reduce(float v, float* sh, bool is_max) {
@@ -554,30 +557,48 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(const floa
   const int w = tid >> 6;
   const float* m = pm + h * nchunks;
   const float* l = pl + h * nchunks;
-  float M = -INFINITY;
-  for (int c = tid; c < nchunks; c += kMergeWaves * 64) M = fmaxf(M, m[c]);
+  const int d = blockIdx.y * 64 + lane;
+  const float* o = po + h * nchunks * D + d;
+  // Every load of the first pass is issued up front: the chunk maxima and
+  // sums of this thread's first chunk and the wave's first kMergeUnroll
+  // partial outputs (they do not depend on the weights), so their latencies
+  // overlap instead of following each other.
+  const float m0 = tid < nchunks ? m[tid] : -INFINITY;
+  const float l0 = tid < nchunks ? l[tid] : 0.0f;
+  float x[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const int c = w + u * kMergeWaves;
+    x[u] = c < nchunks ? o[(int64_t)c * D] : 0.0f;
+  }
+  float M = m0;
+  for (int c = tid + kMergeWaves * 64; c < nchunks; c += kMergeWaves * 64) M = fmaxf(M, m[c]);
   M = block_reduce(M, sh, true);
   float Lp = 0.0f;
-  for (int c = tid; c < nchunks; c += kMergeWaves * 64) {
+  if (tid < nchunks) {
+    const float wt = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+    wts[tid] = wt;
+    Lp = l0 * wt;
+  }
+  for (int c = tid + kMergeWaves * 64; c < nchunks; c += kMergeWaves * 64) {
     const float wt = m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[c] - M);
     wts[c] = wt;
     Lp = fmaf(l[c], wt, Lp);
   }
   const float L = block_reduce(Lp, sh, false);  // its barriers also publish wts
-  const int d = blockIdx.y * 64 + lane;
-  const float* o = po + h * nchunks * D + d;
   float acc = 0.0f;
-  for (int c0 = w; c0 < nchunks; c0 += kMergeWaves * kMergeUnroll) {
-    float x[kMergeUnroll];
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const int c = c0 + u * kMergeWaves;
-      x[u] = c < nchunks ? o[(int64_t)c * D] : 0.0f;
-    }
+  for (int c0 = w;;) {
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int c = c0 + u * kMergeWaves;
       if (c < nchunks) acc = fmaf(x[u], wts[c], acc);
+    }
+    c0 += kMergeWaves * kMergeUnroll;
+    if (c0 >= nchunks) break;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int c = c0 + u * kMergeWaves;
+      x[u] = c < nchunks ? o[(int64_t)c * D] : 0.0f;
     }
   }
   red[w][lane] = acc;
