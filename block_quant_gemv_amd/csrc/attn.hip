@@ -206,15 +206,16 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_kernel(
   const int dl = lane % LPT;          // this lane's 8 dimensions: 8 dl .. 8 dl + 7
   const int slot = lane / LPT;        // token slot within a wave load
 
-  // Query rows of the group, this lane's dimensions, pre-scaled.
-  float qr[G][8];
+  // Query rows of the group, this lane's dimensions (scaled below, once the
+  // first K/V batches have been requested, so the latencies overlap).
+  float4 qa[G], qb[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const float4* qp = reinterpret_cast<const float4*>(q + ((int64_t)kvh * G + j) * D + 8 * dl);
-    const float4 a = qp[0], b = qp[1];
-    qr[j][0] = a.x * qscale; qr[j][1] = a.y * qscale; qr[j][2] = a.z * qscale; qr[j][3] = a.w * qscale;
-    qr[j][4] = b.x * qscale; qr[j][5] = b.y * qscale; qr[j][6] = b.z * qscale; qr[j][7] = b.w * qscale;
+    qa[j] = qp[0];
+    qb[j] = qp[1];
   }
+  float qr[G][8];
 
   AState<G> st;
 #pragma unroll
@@ -306,13 +307,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_partial_kernel(
   u32x4 kA[kAttnBatch], vA[kAttnBatch], kB[kAttnBatch], vB[kAttnBatch];
   int64_t tb = t0 + (int64_t)wid * TPW;
   if (tb < t1) fetch(kA, vA, tb);
+  if (tb + kBatchTokens < t1) fetch(kB, vB, tb + kBatchTokens);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float4 a = qa[j], b = qb[j];
+    qr[j][0] = a.x * qscale; qr[j][1] = a.y * qscale; qr[j][2] = a.z * qscale; qr[j][3] = a.w * qscale;
+    qr[j][4] = b.x * qscale; qr[j][5] = b.y * qscale; qr[j][6] = b.z * qscale; qr[j][7] = b.w * qscale;
+  }
+  // Two batches in flight: each buffer is refilled with the batch after
+  // next as soon as it has been consumed.
   while (tb < t1) {
-    if (tb + kBatchTokens < t1) fetch(kB, vB, tb + kBatchTokens);
     consume(kA, vA, tb);
+    if (tb + 2 * kBatchTokens < t1) fetch(kA, vA, tb + 2 * kBatchTokens);
     tb += kBatchTokens;
     if (tb >= t1) break;
-    if (tb + kBatchTokens < t1) fetch(kA, vA, tb + kBatchTokens);
     consume(kB, vB, tb);
+    if (tb + 2 * kBatchTokens < t1) fetch(kB, vB, tb + 2 * kBatchTokens);
     tb += kBatchTokens;
   }
 
