@@ -150,3 +150,16 @@ def gemv_rows(fmt, raw, n, k, rows, xq, dx, codebook=None):
 def fp32_gemv(w, x):
     """Plain fp64 product of an fp32 matrix w[n, k] with fp32 x[m, k] -> [m, n]."""
     return np.atleast_2d(np.asarray(x, np.float64)) @ np.asarray(w, np.float64).T
+
+
+def gemv_float_act(fmt, raw, n, k, x, codebook=None):
+    """Float-activation form: y[m, n] = x . W_hat^T in fp64, with x the fp32
+    activations as given (no activation quantization) and W_hat the exact
+    dequantized weights. The batched (prefill) path computes this when int8
+    activations cost too much accuracy: in "01 · Phase overview: from 2B to
+    8B to MoE" (icman.com.cn, issue ledger item ⑮) int8 activations in
+    prefill raised perplexity by about 3 %, float activations by about 0.2 %.
+    """
+    xa = np.atleast_2d(np.asarray(x, np.float32)).astype(np.float64)
+    return xa @ formats.values(fmt, raw, n, k, codebook).T
+

@@ -164,3 +164,46 @@ def test_iq4_xs_sub_scales_scale_each_sub_block():
     sl = slice(256 + 160, 256 + 192)
     part = (dx[0, sl.start // 32] * xq[0, sl].astype(np.float64)) @ (0.25 * cb[q[:, 1, 160:192]].T)
     assert np.allclose(y2 - y1, (48 - 32 - (40 - 32)) * part, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_float_act_equals_quantized_form_on_the_q8_grid(fmt):
+    # Activations that Q8 quantization reproduces exactly (codes with a +-127
+    # in every block, power-of-two block scales): the float-activation form
+    # and the quantized dequantize form must then give the same products.
+    n, m, k = 23, 3, 512
+    rng = np.random.default_rng(31)
+    raw = synth.weights(fmt, n, k, seed=6)
+    cb = _cb()
+    q = rng.integers(-127, 128, size=(m, k // 32, 32))
+    q[..., 0] = np.where(rng.random((m, k // 32)) < 0.5, 127, -127)
+    dx = np.exp2(rng.integers(-6, 3, size=(m, k // 32))).astype(np.float32)
+    x = (q * dx[..., None]).reshape(m, k).astype(np.float32)
+    xq, dx2, _ = quantize_q8(x)
+    assert np.array_equal(xq.astype(np.int64), q.reshape(m, k)) and np.array_equal(dx2, dx)
+    yf = gemv.gemv_float_act(fmt, raw, n, k, x, cb)
+    yq = gemv.gemv_dequant(fmt, raw, n, k, xq, dx2, cb)
+    assert np.linalg.norm(yf - yq) <= 1e-13 * np.linalg.norm(yq)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_float_act_one_hot_inputs_pick_weight_columns(fmt):
+    # x = e_j (token 0) and 2 e_j (token 1): y[t, r] = (t + 1) W_hat[r, j], with
+    # W_hat[r, j] = d * code from the stored bytes, read here directly.
+    n, k = 5, 64
+    raw = synth.weights(fmt, n, k, seed=8)
+    bb = formats.BLOCK_BYTES[fmt]
+    rb = formats.row_bytes(fmt, k)
+    rows = np.asarray(raw, np.uint8)[: n * rb].reshape(n, rb)[:, : (k // 32) * bb].reshape(n, k // 32, bb)
+    for j in (0, 17, 33, 63):
+        x = np.zeros((2, k), np.float32)
+        x[0, j], x[1, j] = 1.0, 2.0
+        y = gemv.gemv_float_act(fmt, raw, n, k, x)
+        b, e = divmod(j, 32)
+        d = rows[:, b, 0:2].copy().view(np.float16).astype(np.float64)[:, 0]
+        if fmt == "q8_0":
+            code = rows[:, b, 2 + e].astype(np.int8).astype(np.float64)
+        else:
+            byte = rows[:, b, 2 + (e % 16)]
+            code = ((byte & 0xF) if e < 16 else (byte >> 4)).astype(np.float64) - 8
+        assert np.array_equal(y[0], d * code) and np.array_equal(y[1], 2 * d * code)
