@@ -445,6 +445,25 @@ def extras(qg, synth, torch):
     res[f"s16_q4_k_{k}x{n}_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
     log(f"s16 q4_k {k}x{n}: {us:.2f} us, {res[f's16_q4_k_{k}x{n}_gbps']} GB/s")
     del Ws
+    # Float activations (qgemv_run_f32act, fp32 matrix cores): Q8_0 and Q4_0,
+    # 4096 -> 12288, one token and 32 tokens (2 * m * n * k flops per call)
+    n, k = 12288, 4096
+    for fmt in ("q8_0", "q4_0"):
+        g = qg.GEMV(fmt, n, k, max_m=32)
+        b = n * synth.row_bytes(fmt, k)
+        R = copies_for(b, cap=64)
+        Ws = rotated(synth.weights(fmt, n, k, seed=337), R)
+        for m in (1, 32):
+            x = dev(synth.activations(338, m, k))
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            gg = graph_of(lambda i: g.run_f32act(Ws[i % R], x, y=y), R)
+            us = time_graph(gg, R, reps=4)
+            key = f"f32act_{fmt}_{k}x{n}_m{m}"
+            res[key + "_us"] = round(us, 3)
+            res[key + "_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
+            res[key + "_tflops"] = round(2 * m * n * k / (us * 1e-6) / 1e12, 2)
+            log(f"f32act {fmt} {k}x{n} m={m}: {us:.2f} us, {res[key + '_gbps']} GB/s, {res[key + '_tflops']} TFLOP/s")
+        del Ws
     # M=32 batched GEMMs on int8 MFMA (Q4_K 4096 -> 12288, Q6_K 12288 -> 4096)
     for fmt, n, k in (("q4_k", 12288, 4096), ("q6_k", 4096, 12288)):
         g = qg.GEMV(fmt, n, k, max_m=32)

@@ -21,6 +21,7 @@
 #include "attn.h"
 #include "moe.h"
 #include "s16.h"
+#include "fact.h"
 #include "mfma.h"
 #include "swiglu.h"
 
@@ -663,6 +664,20 @@ int qgemv_run_s16(qgemv_t h, const void* w, const float* x, float* y, void* ws, 
   return check_launch(
       launch_kquant_s16(h->d.fmt, static_cast<const uint8_t*>(w), xq, dx, sx, y, nullptr, h->d.n, k, s),
       "gemv s16");
+}
+
+int qgemv_run_f32act(qgemv_t h, const void* w, const float* x, float* y, int m, void* stream) {
+  if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "qgemv_run_f32act: not a GEMV plan");
+  if (!fact_supported(h->d.fmt))
+    return fail(QGEMV_EFORMAT, "qgemv_run_f32act: float activations need a Q4_0 or Q8_0 plan");
+  if (m < 1 || m > 32) return fail(QGEMV_ESHAPE, "qgemv_run_f32act: m=%d not in 1..32", m);
+  if (!w || !x || !y) return fail(QGEMV_EINVAL, "qgemv_run_f32act: null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return fail(QGEMV_EALIGN, "qgemv_run_f32act: w and x need 16-byte, y 4-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run_f32act: launch failure injected (QGEMV_FAULT)");
+  return check_launch(launch_fact(h->d.fmt, static_cast<const uint8_t*>(w), x, y, m, h->d.n, h->d.k,
+                                  static_cast<hipStream_t>(stream)),
+                      "gemv f32act");
 }
 
 int qgemv_debug_quantize_s16(const float* x, int16_t* xq, float* dx, int32_t* sx, int m, int64_t k, void* stream) {

@@ -1,0 +1,158 @@
+// Float-activation batched GEMV for the 32-element block formats (Q4_0,
+// Q8_0): y[m, n] = x[m, k] . W_hat[n, k]^T with the activations kept in
+// fp32, no activation quantization. In prefill, int8 activations cost about
+// 3 % perplexity where float activations cost about 0.2 % ("01 · Phase
+// overview: from 2B to 8B to MoE", icman.com.cn, issue ledger item ⑮), so
+// this is the batched path's accuracy variant.
+//
+// The product is a dense contraction over up to 32 tokens, so it runs on
+// fp32 matrix cores: v_mfma_f32_16x16x4_f32 takes a 16 x 4 tile of weights
+// (lane = row + 16 g) and a 4 x 16 tile of activations (lane = token + 16 g)
+// and accumulates the 16 x 16 products in fp32. Each weight value d * q is
+// exact in fp32 (an 11-bit fp16 significand times a code of at most 8 bits).
+// Within one 32-element block, lane group g owns elements 8 g .. 8 g + 7 for
+// both operands, so step s of 8 feeds element 8 g + s of the weights and of
+// the activations; the k-order inside an MFMA does not change the sum.
+//
+// A workgroup computes 16 rows for all tokens; its 4 waves take the row
+// tile's blocks in turn (wave w: blocks w, w + 4, ...), so at any time the 4
+// waves read neighbouring blocks of the same 16 rows. The 4 partial tiles are
+// added in wave order through LDS, and wave 0 stores y.
+#include "common.cuh"
+#include "fact.h"
+
+namespace qg {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFaWaves = 4;
+
+// Bytes per block: fp16 d, then the codes (Q4_0: 16 bytes of nibbles, element
+// e < 16 in the low nibble of byte e, element e >= 16 in the high nibble of
+// byte e - 16; Q8_0: 32 int8 codes).
+template <int FMT>
+constexpr int kFaBlockBytes = FMT == 1 ? 18 : 34;
+
+// The 8 dequantized weights of elements 8 g .. 8 g + 7 of one block (2-byte
+// aligned loads: blocks are 18 or 34 bytes long).
+template <int FMT>
+QG_DEV void fa_weights(const uint8_t* __restrict__ blk, int g, float (&w)[8]) {
+  const uint16_t* p16 = reinterpret_cast<const uint16_t*>(blk);
+  const float d = half_bits(p16[0]);
+  if constexpr (FMT == 2) {
+    const uint16_t* c = p16 + 1 + 4 * g;  // bytes 2 + 8 g ..
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = c[i];
+      w[2 * i] = d * (float)(int8_t)(v & 0xffu);
+      w[2 * i + 1] = d * (float)(int8_t)(v >> 8);
+    }
+  } else {
+    const uint16_t* c = p16 + 1 + 4 * (g & 1);  // bytes 2 + 8 (g & 1) ..
+    const int sh = g < 2 ? 0 : 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = c[i];
+      w[2 * i] = d * (float)((int)((v >> sh) & 0xfu) - 8);
+      w[2 * i + 1] = d * (float)((int)((v >> (8 + sh)) & 0xfu) - 8);
+    }
+  }
+}
+
+QG_DEV void fa_acts(const float* __restrict__ p, bool ok, float (&a)[8]) {
+  if (ok) {
+    const float4 u = reinterpret_cast<const float4*>(p)[0];
+    const float4 v = reinterpret_cast<const float4*>(p)[1];
+    a[0] = u.x, a[1] = u.y, a[2] = u.z, a[3] = u.w, a[4] = v.x, a[5] = v.y, a[6] = v.z, a[7] = v.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+  }
+}
+
+// NT: token tiles of 16 (1 for m <= 16, 2 for m <= 32).
+template <int FMT, int NT>
+__global__ __launch_bounds__(kFaWaves * 64) void fact_kernel(const uint8_t* __restrict__ w,
+                                                             const float* __restrict__ x, float* __restrict__ y,
+                                                             int m, int64_t n, int64_t k) {
+  constexpr int BB = kFaBlockBytes<FMT>;
+  __shared__ f32x4 red[kFaWaves][NT][64];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15;  // weight row of the A operand, token of the B operand
+  const int g = lane >> 4;  // element group within a block
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  const int64_t nb = k / 32;
+  const bool row_ok = r0 + i < n;
+  const uint8_t* wr = w + (row_ok ? r0 + i : 0) * nb * BB;
+  bool tok_ok[NT];
+  const float* xr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    tok_ok[t] = 16 * t + i < m;
+    xr[t] = x + (int64_t)(tok_ok[t] ? 16 * t + i : 0) * k + 8 * g;
+  }
+  // Two accumulators per token tile (even and odd steps) so consecutive
+  // MFMAs do not wait on each other's result.
+  f32x4 acc[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t b = wid; b < nb; b += kFaWaves) {
+    float wv[8];
+    if (row_ok) {
+      fa_weights<FMT>(wr + b * BB, g, wv);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) wv[s] = 0.0f;
+    }
+    float xa[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) fa_acts(xr[t] + b * 32, tok_ok[t], xa[t]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[s], xa[t][s], acc[t][s & 1], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) red[wid][t][lane] = acc[t][0] + acc[t][1];
+  __syncthreads();
+  if (wid != 0) return;
+  // Output lane layout: token 16 t + (lane & 15), rows r0 + 4 g + 0..3.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x4 v = red[0][t][lane];
+#pragma unroll
+    for (int ww = 1; ww < kFaWaves; ++ww) v += red[ww][t][lane];
+    const int tok = 16 * t + i;
+    if (tok >= m) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = r0 + 4 * g + r;
+      if (row < n) y[(int64_t)tok * n + row] = v[r];
+    }
+  }
+}
+
+}  // namespace
+
+bool fact_supported(int fmt) { return fmt == 1 || fmt == 2; }
+
+hipError_t launch_fact(int fmt, const uint8_t* w, const float* x, float* y, int m, int64_t n, int64_t k,
+                       hipStream_t s) {
+  if (!fact_supported(fmt) || m < 1 || m > 32 || n < 1 || k < 32 || k % 32) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((n + 15) / 16)), block(kFaWaves * 64);
+  if (fmt == 1) {
+    if (m <= 16) hipLaunchKernelGGL((fact_kernel<1, 1>), grid, block, 0, s, w, x, y, m, n, k);
+    else hipLaunchKernelGGL((fact_kernel<1, 2>), grid, block, 0, s, w, x, y, m, n, k);
+  } else {
+    if (m <= 16) hipLaunchKernelGGL((fact_kernel<2, 1>), grid, block, 0, s, w, x, y, m, n, k);
+    else hipLaunchKernelGGL((fact_kernel<2, 2>), grid, block, 0, s, w, x, y, m, n, k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -210,6 +210,18 @@ int qgemv_workspace_size_s16(qgemv_t h, size_t *bytes);
 int qgemv_run_s16(qgemv_t h, const void *w, const float *x, float *y, void *ws, size_t ws_bytes,
                   void *stream);
 
+/* Float-activation variant of qgemv_run for 1 <= m <= 32 tokens: y[m, n] =
+ * x . W_hat^T with x kept in fp32 (no activation quantization) and each
+ * weight dequantized exactly (d * code) -- the accuracy variant for the
+ * batched (prefill) path, where int8 activations cost about 3 % perplexity
+ * and float activations about 0.2 % in "01 · Phase overview: from 2B to 8B
+ * to MoE" (icman.com.cn, issue ledger item ⑮). Products and sums are fp32
+ * (fp32 matrix cores). Supported for QFMT_Q4_0 and QFMT_Q8_0 plans
+ * (QGEMV_EFORMAT otherwise); m outside 1..32 is QGEMV_ESHAPE (the plan's
+ * max_m does not apply: no workspace is used). x: fp32 [m, k], 16-byte
+ * aligned; w 16-byte aligned; y: fp32 [m, n]. One kernel on `stream`. */
+int qgemv_run_f32act(qgemv_t h, const void *w, const float *x, float *y, int m, void *stream);
+
 /* Fused FFN sublayer for a QKIND_FFN plan, on one stream with one
  * workspace: quantize x -> gate|up GEMV -> h = silu(gate) * up, re-quantized
  * to Q8 -> down GEMV -> y[m, hidden]. The sublayer is queued on a single

@@ -248,3 +248,25 @@ def test_moe_s16_validation_before_launch():
     assert lib.qmoe_run_s16(h, a, a, a, a, a, a, a, 1, a, sz.value, None) == ESHAPE
     assert lib.qmoe_run_s16(h, a, a, a, a, a, None, a, 1, a, sz.value, None) == EINVAL
     lib.qgemv_destroy(h)
+
+
+def test_f32act_validation_before_launch():
+    def plan(fmt, n, k):
+        d = _desc(fmt=fmt, n=n, k=k)
+        h = ctypes.c_void_p()
+        assert lib.qgemv_create(ctypes.byref(h), ctypes.byref(d)) == OK
+        return h
+
+    a = 1 << 20  # fake device addresses: every call below fails validation first
+    h = plan(2, 64, 4096)  # Q8_0
+    assert lib.qgemv_run_f32act(h, a, a, a, 0, None) == ESHAPE
+    assert lib.qgemv_run_f32act(h, a, a, a, 33, None) == ESHAPE
+    assert lib.qgemv_run_f32act(h, None, a, a, 1, None) == EINVAL
+    assert lib.qgemv_run_f32act(h, a, a + 4, a, 1, None) == EALIGN
+    assert lib.qgemv_run_f32act(h, a + 8, a, a, 1, None) == EALIGN
+    assert lib.qgemv_run_f32act(None, a, a, a, 1, None) == EINVAL
+    lib.qgemv_destroy(h)
+    hk = plan(3, 64, 4096)  # Q4_K: no float-activation kernel
+    assert lib.qgemv_run_f32act(hk, a, a, a, 1, None) == EFORMAT
+    lib.qgemv_destroy(hk)
+
