@@ -16,7 +16,8 @@
 //
 // A workgroup computes 16 rows for all tokens; its 4 waves take the row
 // tile's blocks in turn (wave w: blocks w, w + 4, ...), so at any time the 4
-// waves read neighbouring blocks of the same 16 rows. The 4 partial tiles are
+// waves read neighbouring blocks of the same 16 rows; each wave loads several
+// of its blocks before it multiplies them. The 4 partial tiles are
 // added in wave order through LDS, and wave 0 stores y.
 #include "common.cuh"
 #include "fact.h"
@@ -28,6 +29,10 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFaWaves = 4;
+#ifndef QG_FA_UNROLL
+#define QG_FA_UNROLL 1  // measured: 4 and 8 are slower (the loads are not latency-bound)
+#endif
+constexpr int kFaUnroll = QG_FA_UNROLL;  // blocks per wave per loop iteration
 
 // Bytes per block: fp16 d, then the codes (Q4_0: 16 bytes of nibbles, element
 // e < 16 in the low nibble of byte e, element e >= 16 in the high nibble of
@@ -61,15 +66,10 @@ QG_DEV void fa_weights(const uint8_t* __restrict__ blk, int g, float (&w)[8]) {
   }
 }
 
-QG_DEV void fa_acts(const float* __restrict__ p, bool ok, float (&a)[8]) {
-  if (ok) {
-    const float4 u = reinterpret_cast<const float4*>(p)[0];
-    const float4 v = reinterpret_cast<const float4*>(p)[1];
-    a[0] = u.x, a[1] = u.y, a[2] = u.z, a[3] = u.w, a[4] = v.x, a[5] = v.y, a[6] = v.z, a[7] = v.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = 0.0f;
-  }
+QG_DEV void fa_acts(const float* __restrict__ p, float (&a)[8]) {
+  const float4 u = reinterpret_cast<const float4*>(p)[0];
+  const float4 v = reinterpret_cast<const float4*>(p)[1];
+  a[0] = u.x, a[1] = u.y, a[2] = u.z, a[3] = u.w, a[4] = v.x, a[5] = v.y, a[6] = v.z, a[7] = v.w;
 }
 
 // NT: token tiles of 16 (1 for m <= 16, 2 for m <= 32).
@@ -99,22 +99,41 @@ __global__ __launch_bounds__(kFaWaves * 64) void fact_kernel(const uint8_t* __re
   f32x4 acc[NT][2];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t b = wid; b < nb; b += kFaWaves) {
-    float wv[8];
-    if (row_ok) {
-      fa_weights<FMT>(wr + b * BB, g, wv);
-    } else {
+  // kFaUnroll blocks per iteration: all their loads are issued before the
+  // first MFMA, so one memory latency covers several blocks. A block past
+  // the end contributes zeros.
+  for (int64_t b0 = wid; b0 < nb; b0 += kFaWaves * kFaUnroll) {
+    float wv[kFaUnroll][8];
+    float xa[kFaUnroll][NT][8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) wv[s] = 0.0f;
+    for (int u = 0; u < kFaUnroll; ++u) {
+      // Loads are unconditional, from clamped (always valid) addresses, and
+      // the values of a row, token or block out of range are then replaced
+      // by zeros: no load sits in a divergent branch whose other side would
+      // have to wait for it.
+      const int64_t b = b0 + (int64_t)u * kFaWaves;
+      const bool ok = b < nb;
+      const int64_t bc = ok ? b : nb - 1;
+      fa_weights<FMT>(wr + bc * BB, g, wv[u]);
+      const bool wok = row_ok && ok;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) wv[u][s] = wok ? wv[u][s] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        fa_acts(xr[t] + bc * 32, xa[u][t]);
+        const bool xok = tok_ok[t] && ok;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xa[u][t][s] = xok ? xa[u][t][s] : 0.0f;
+      }
     }
-    float xa[NT][8];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) fa_acts(xr[t] + b * 32, tok_ok[t], xa[t]);
+    for (int u = 0; u < kFaUnroll; ++u) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[s], xa[t][s], acc[t][s & 1], 0, 0, 0);
+        for (int t = 0; t < NT; ++t)
+          acc[t][s & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][s], xa[u][t][s], acc[t][s & 1], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
