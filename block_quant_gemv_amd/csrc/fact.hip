@@ -28,7 +28,10 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFaWaves = 4;
+#ifndef QG_FA_WAVES
+#define QG_FA_WAVES 4
+#endif
+constexpr int kFaWaves = QG_FA_WAVES;  // waves per workgroup, splitting the row tile's blocks
 #ifndef QG_FA_UNROLL
 #define QG_FA_UNROLL 1  // measured: 4 and 8 are slower (the loads are not latency-bound)
 #endif
