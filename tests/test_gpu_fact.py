@@ -2,8 +2,9 @@
 the oracle's float-activation form: within the normwise bound for Q4_0 and
 Q8_0 over ragged row counts, K below one block per wave, 1..32 tokens (one
 and two token tiles) and the full dense-layer size; no write outside y;
-repeat calls bit-identical; and the accuracy it exists for: far closer to the
-unquantized-activation product than the int8 path."""
+repeat calls and graph replays bit-identical to eager calls; and the accuracy
+it exists for: far closer to the unquantized-activation product than the int8
+path."""
 import numpy as np
 import pytest
 
@@ -66,3 +67,27 @@ def test_f32act_more_accurate_than_int8(fmt):
     ef, eq = normwise(yf, truth), normwise(yq, truth)
     say(f"{fmt}: float activations {ef:.2e}, int8 activations {eq:.2e}")
     assert ef * 100 < eq
+
+
+def test_f32act_graph_replays_match_eager():
+    n, k, m = 4096, 4096, 24
+    w = dev(synth.weights("q8_0", n, k, seed=77))
+    g = qg.GEMV("q8_0", n, k, max_m=32)
+    xs = [dev(synth.activations(78 + i, m, k)) for i in range(3)]
+    eager = [g.run_f32act(w, x).clone() for x in xs]
+    x_in = xs[0].clone()
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    g.run_f32act(w, x_in, y=y)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.run_f32act(w, x_in, y=y)
+    for rep in range(3):
+        for i in (2, 0, 1):
+            x_in.copy_(xs[i])
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager[i]), f"replay {rep} input {i}"
+            other = g.run_f32act(w, xs[(i + 1) % 3])
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager[(i + 1) % 3])
