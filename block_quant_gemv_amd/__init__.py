@@ -14,7 +14,8 @@ import os
 
 import torch  # loads torch's HIP runtime first; the library then binds to it
 
-__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "debug_quantize_s16", "lib_path", "LAYOUT_VERSION"]
+__all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "debug_quantize_s16",
+           "clear_launch_cache", "lib_path", "LAYOUT_VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libqgemv.so")
@@ -71,9 +72,10 @@ _lib.qgemv_run_s16.argtypes = [_vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.qgemv_run_f32act.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, _vp]
 _lib.qgemv_debug_quantize_s16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots_s16.argtypes = [_vp, _vp, _vp, _vp, _vp]
+_lib.qgemv_debug_clear_launch_cache.argtypes = []
 _lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
 _lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
-for _f in ("qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
+for _f in ("qgemv_debug_clear_launch_cache", "qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
            "qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
@@ -371,6 +373,12 @@ def debug_quantize_s16(x: torch.Tensor, stream=None):
     _check(_lib.qgemv_debug_quantize_s16(_dev(x, torch.float32, "x"), xq.data_ptr(), dx.data_ptr(), sx.data_ptr(),
                                          m, k, _stream(stream)), "qgemv_debug_quantize_s16")
     return xq, dx, sx
+
+
+def clear_launch_cache():
+    """Forget the library's cached launch facts (per-device CU counts and
+    kernel residencies): the next launch of each kernel queries them again."""
+    _check(_lib.qgemv_debug_clear_launch_cache(), "qgemv_debug_clear_launch_cache")
 
 
 class Attention:

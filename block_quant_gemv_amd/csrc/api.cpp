@@ -702,4 +702,9 @@ int qgemv_debug_block_dots_s16(qgemv_t h, const void* w, const int16_t* xq, int3
                       "block dots s16");
 }
 
+int qgemv_debug_clear_launch_cache(void) {
+  clear_launch_cache();
+  return QGEMV_OK;
+}
+
 }  // extern "C"

@@ -29,6 +29,7 @@
 // With a single chunk stage 1 normalises and writes o itself.
 #include "attn.h"
 #include "common.cuh"
+#include "internal.h"
 
 namespace qg {
 
@@ -659,17 +660,6 @@ hipError_t launch_d(const AttnShape& a, const AttnPlan& pl, const float* q, cons
   }
 }
 
-int device_cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 }  // namespace
 
 bool attn_uses_mfma(const AttnShape& a) {
@@ -693,7 +683,7 @@ AttnPlan attn_plan(const AttnShape& a) {
   const int64_t min_chunk = mf ? step : step * kAttnBatch * QG_ATTN_MIN_BATCHES;
   // Enough chunks for QG_ATTN_WGS_PER_CU workgroups per CU (at most kMaxChunks), none
   // shorter than QG_ATTN_MIN_BATCHES batched iterations of the workgroup.
-  int64_t want = ((int64_t)device_cu_count() * QG_ATTN_WGS_PER_CU + a.n_kv - 1) / a.n_kv;
+  int64_t want = ((int64_t)device_cus() * QG_ATTN_WGS_PER_CU + a.n_kv - 1) / a.n_kv;
   if (want > kMaxChunks) want = kMaxChunks;
   int64_t nch = (a.n_ctx + min_chunk - 1) / min_chunk;
   if (nch > want) nch = want;

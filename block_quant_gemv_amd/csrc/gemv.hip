@@ -67,7 +67,7 @@ constexpr int tile_cap(int fmt) {
 }
 // 16-byte chunks a step can span (alignment adds up to two), per lane.
 template <int FMT> constexpr int loads_per_lane() { return (tile_cap(FMT) + 32 + 1023) / 1024; }
-constexpr int kLdsLimit = 160 * 1024;
+constexpr int kLdsLimit = kLdsBytes;
 // Word 3 of a raw (unswizzled, unformatted) buffer resource on gfx9-family
 // GPUs, gfx950 included.
 constexpr int kBufferDword3 = 0x00020000;
@@ -755,18 +755,6 @@ static int floor_pow2(int v) {
   return r;
 }
 
-static int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 // Largest passes-per-step the kernels are instantiated for, per token tile.
 static int max_passes(int mt) { return mt <= 2 ? 8 : mt == 4 ? 4 : mt == 8 ? 2 : 1; }
 
@@ -817,29 +805,13 @@ template <int FMT, int MT, int P, bool DOTS, bool FUSEQ>
 static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   auto kern = gemv_kernel<FMT, MT, P, DOTS, FUSEQ>;
   const size_t lds = (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf;
-  static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   // Persistent grid: no more workgroups than can be resident at once, so
   // every wave walks its share of the steps without a second launch round.
   // Resident workgroups per CU depend on the LDS size (activations vary with
-  // K); cache the occupancy answer per LDS size for this kernel.
-  static size_t cached_lds[8] = {0};
-  static int cached_nb[8] = {0};
-  int per_cu = 0;
-  for (int i = 0; i < 8; ++i)
-    if (cached_lds[i] == lds && cached_nb[i] > 0) per_cu = cached_nb[i];
-  if (!per_cu) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kWavesPerWG * 64, lds) != hipSuccess || nb < 1) nb = 1;
-    per_cu = nb;
-    for (int i = 0; i < 8; ++i)
-      if (cached_nb[i] == 0) { cached_lds[i] = lds; cached_nb[i] = per_cu; break; }
-  }
+  // K); the answer is cached per kernel, LDS size and device.
+  int per_cu = 0, cus = 0;
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kWavesPerWG * 64, lds, true, &per_cu, &cus);
+  if (qe != hipSuccess) return qe;
   // A single matrix streams best with fewer resident workgroups than fit;
   // grouped launches (many small problems) use all of them.
   if (a.p.nprob == 1 && QG_WGS_PER_CU > 0 && QG_WGS_PER_CU < per_cu) per_cu = QG_WGS_PER_CU;
@@ -847,7 +819,7 @@ static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   // every wave the same number of row tiles (ceil), so no wave runs a
   // lone extra step at the end.
   // Grouped launches split the resident waves among their problems.
-  const int64_t cap_waves = (int64_t)device_cus() * per_cu * kWavesPerWG;
+  const int64_t cap_waves = (int64_t)cus * per_cu * kWavesPerWG;
   int64_t wmax = cap_waves / a.p.nprob;
   if (wmax < kWavesPerWG) wmax = kWavesPerWG;
 #if QG_BALANCE

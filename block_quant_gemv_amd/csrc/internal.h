@@ -82,6 +82,19 @@ hipError_t launch_tile_codes(const int8_t* xq, int8_t* xqt, int m, int kblocks, 
 bool kdirect_ok(int fmt, const GemvProblem& p, bool dots);
 hipError_t launch_kdirect(int fmt, const GemvProblem& p, bool dots, hipStream_t s);
 
+// Launch facts of the current device (launch_cache.cpp), looked up and
+// filled under one lock, keyed by device: safe from several threads at once.
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
+int device_cus();
+// Resident workgroups per CU of kernel `kern` launched with `threads` threads
+// and `lds` bytes of dynamic LDS (at least 1); with raise_lds the kernel's
+// dynamic-LDS limit is first raised to kLdsBytes (once per kernel and
+// device). cus (optional) receives the device's compute-unit count.
+hipError_t kernel_residency(const void* kern, int threads, size_t lds, bool raise_lds, int* per_cu,
+                            int* cus = nullptr);
+// Forgets every cached fact (the next launch of each kernel queries again).
+void clear_launch_cache();
+
 // Largest token count one GEMV launch handles.
 constexpr int kGemvMaxTokens = 16;
 // From this many tokens on, Q4_K and Q6_K GEMVs run on int8 MFMA (the VALU

@@ -196,18 +196,10 @@ __global__ __launch_bounds__(kDirectWaves * 64) void kdirect_kernel(const uint8_
 template <int FMT, int JU, int R, bool DOTS>
 hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
   auto kern = kdirect_kernel<FMT, JU, R, DOTS>;
-  static int per_cu = 0;  // resident workgroups per CU (occupancy query, once)
-  static int cus = 0;
-  if (!per_cu) {
-    int dev = 0, nb = 0, c = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-      c = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kDirectWaves * 64, 0) != hipSuccess || nb < 1)
-      nb = 1;
-    cus = c;
-    per_cu = QG_DIRECT_WGS_PER_CU > 0 && QG_DIRECT_WGS_PER_CU < nb ? QG_DIRECT_WGS_PER_CU : nb;
-  }
+  int nb = 0, cus = 0;  // resident workgroups per CU (cached occupancy query), compute units
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kDirectWaves * 64, 0, false, &nb, &cus);
+  if (qe != hipSuccess) return qe;
+  const int per_cu = QG_DIRECT_WGS_PER_CU > 0 && QG_DIRECT_WGS_PER_CU < nb ? QG_DIRECT_WGS_PER_CU : nb;
   const int64_t ngroups = (p.n + R - 1) / R;
   int64_t waves = (int64_t)cus * per_cu * kDirectWaves;
   if (waves > ngroups) waves = ngroups;

@@ -359,13 +359,9 @@ hipError_t launch_t(const uint8_t* w, const int8_t* xqt, const float* dx, const 
   size_t lds = (size_t)G::TILE + stage;
   if (lds < red) lds = red;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;  // raise the dynamic-LDS limit once per kernel
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  int per_cu = 0;  // raises the dynamic-LDS limit (once per kernel and device)
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kNW * 64, lds, true, &per_cu);
+  if (qe != hipSuccess) return qe;
   const unsigned tiles = (unsigned)((n + kRows - 1) / kRows);
   hipLaunchKernelGGL(kern, dim3(tiles, (unsigned)splits), dim3(kNW * 64), lds, s, w, xqt, dx, sx, out, dots, n,
                      k, m, sps);

@@ -202,13 +202,7 @@ template <int FMT, int JU, int R, bool DOTS>
 hipError_t launch_ju_t(const uint8_t* w, const int16_t* xq, const float* dx, const int32_t* sx, float* y,
                        int32_t* dots, int64_t n, int64_t k, hipStream_t s) {
   auto kern = q4k_s16_kernel<FMT, JU, R, DOTS>;
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+  const int cus = device_cus();
   const int64_t ngroups = (n + R - 1) / R;
   int64_t waves = (int64_t)cus * 3 * kWaves16;  // three resident workgroups per CU, as the int8 kernel
   if (waves > ngroups) waves = ngroups;
@@ -400,13 +394,7 @@ __global__ __launch_bounds__(256) void swiglu_s16_kernel(const float* __restrict
 
 template <int LPR, int JB>
 hipError_t launch_q40g(const S16Grouped& a, hipStream_t s) {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+  const int cus = device_cus();
   // Workgroups per entry: enough row passes for every wave, and no more
   // workgroups in all than about four per CU resident at once.
   constexpr int RPP = 64 / LPR;

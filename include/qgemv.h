@@ -35,6 +35,10 @@
  *  - Handles (qgemv_t) are immutable host-side plans that own only host
  *    memory. One handle may be used concurrently from several threads and
  *    streams, provided each concurrent call has its own workspace and output.
+ *    The launch facts the library caches (compute units per device, resident
+ *    workgroups per kernel, raised LDS limits) are kept per device and filled
+ *    under a lock, so first calls from several threads, on several devices
+ *    or inside stream capture are safe.
  *  - Layouts are row-major. A weight matrix with N rows and K inputs is N
  *    rows of (K / block_elems) blocks, block_bytes each, rows contiguous,
  *    starting at a 16-byte aligned address. The buffer must be readable up to
@@ -141,14 +145,28 @@ typedef struct qgemv_desc {
 
 typedef struct qgemv_plan *qgemv_t;
 
-/* Create / destroy a plan. The descriptor is validated here (kind, version,
- * format, shapes, codebook). */
+/* Create a plan: the descriptor (kind, version, format, shapes, codebook)
+ * is validated and copied into a host-side handle. A plan is the "load once,
+ * then call per token" half of the pure-C device module in "01 · Phase
+ * overview: from 2B to 8B to MoE" (icman.com.cn, section 一 and ledger item
+ * ①); the format and shape fields describe the packed GGUF-style blocks of
+ * "Why expert caching can't save dense models" (xhh.club, Q&A on computing
+ * GGUF blocks without FP16 expansion). *out is NULL on failure. Errors:
+ * QGEMV_EINVAL (null argument, unknown kind, missing or unsorted codebook),
+ * QGEMV_EVERSION, QGEMV_EFORMAT, QGEMV_ESHAPE. */
 int qgemv_create(qgemv_t *out, const qgemv_desc *desc);
+/* Free a plan's host memory (NULL is accepted). Calls already enqueued with
+ * the plan are unaffected: nothing on the device refers to it. */
 int qgemv_destroy(qgemv_t h);
 
 /* Bytes of caller-allocated device workspace needed for a call with m
- * tokens (the workspace is reused across calls; one workspace per concurrent
- * call). */
+ * tokens (1 <= m <= max_m, else QGEMV_ESHAPE). The workspace holds the
+ * quantized activations and every intermediate of the call; it is reused
+ * across calls and owned by the caller -- the buffer pool that "01 · Phase
+ * overview: from 2B to 8B to MoE" (icman.com.cn, ledger item ⑦) keeps off
+ * the per-token path, and the single reused workspace of the fused FFN in
+ * "Why expert caching can't save dense models" (xhh.club, single-stream
+ * fusion section). One workspace per concurrent call. */
 int qgemv_workspace_size(qgemv_t h, int m, size_t *bytes);
 
 /* Byte offsets, inside the workspace for m tokens, of the named
@@ -170,7 +188,12 @@ int qgemv_workspace_offset(qgemv_t h, int m, const char *name, size_t *offset);
  * 1 = all experts' down, 2 = shared gate|up, 3 = shared down, 4 = router. */
 int qgemv_weight_bytes(qgemv_t h, int which, size_t *bytes);
 
-/* y[m, n] = W . x for a QKIND_GEMV plan (decode GEMV, 1 <= m <= max_m).
+/* y[m, n] = W . x for a QKIND_GEMV plan (decode GEMV, 1 <= m <= max_m):
+ * the activations are quantized on the device to 32-element int8 blocks
+ * with an fp32 scale, and each packed weight block is decoded in registers
+ * and combined with them by integer dot products, then scaled ("Why expert
+ * caching can't save dense models", xhh.club, in-place compute section and
+ * its Q&A on computing GGUF blocks without FP16 expansion).
  * x: fp32 [m, k], 16-byte aligned. y: fp32 [m, n]. ws: workspace of at
  * least qgemv_workspace_size(h, m) bytes, 256-byte aligned. Launches on
  * `stream`: for k <= 2048 and m <= 16 one GEMV kernel that quantizes x in its
@@ -246,7 +269,6 @@ int qmoe_run(qgemv_t h, const float *w_router, const void *w_experts_gateup,
              const void *w_shared_down, const float *x, float *y, int m,
              void *ws, size_t ws_bytes, void *stream);
 
-/* Human-readable text of a status code (static string). */
 /* qmoe_run with 16-bit activations: x and every expert's h are quantized to
  * 32-element blocks of int16 codes (scale absmax / 32767), the fix the
  * issue ledger of "01 · Phase overview: from 2B to 8B to MoE" (icman.com.cn,
@@ -262,6 +284,7 @@ int qmoe_run_s16(qgemv_t h, const float *w_router, const void *w_experts_gateup,
                  const void *w_shared_down, const float *x, float *y, int m,
                  void *ws, size_t ws_bytes, void *stream);
 
+/* Human-readable text of a status code (static string). */
 const char *qgemv_status_string(int status);
 /* Message of the calling thread's last failed call ("" if none). */
 const char *qgemv_last_error(void);
@@ -297,6 +320,12 @@ int qgemv_debug_quantize_s16(const float *x, int16_t *xq, float *dx, int32_t *sx
  * sub-block, from the production 16-bit GEMV kernel with an integer-store
  * epilogue. Same shape limits as qgemv_run_s16. */
 int qgemv_debug_block_dots_s16(qgemv_t h, const void *w, const int16_t *xq, int32_t *dots, void *stream);
+
+/* Forget the cached launch facts of every kernel on every device (the next
+ * launch of each kernel queries them again). For tests that need a kernel's
+ * first use to happen at a chosen point (inside stream capture, from several
+ * threads at once). Never needed for correctness. */
+int qgemv_debug_clear_launch_cache(void);
 
 #ifdef __cplusplus
 }
