@@ -119,8 +119,9 @@ QG_DEV float wave_sum(float v) {
   return v;
 }
 
-// Code of one element: round-half-away(fl32(x / d)), clamped to +-127, for a
-// block scale d = fl32(absmax / 127) > 0 (r = v_rcp(d)).
+// Code of one element: round-half-away(fl32(x / d)), for a block scale
+// d = fl32(absmax / 127) > 0 (r = v_rcp(d)). |x| <= absmax, so the code lies
+// in -127..127 without a clamp.
 //
 // fl32(x / d) is the correctly rounded quotient; computing it with the IEEE
 // division sequence for every element is the costly part of quantization.
@@ -128,37 +129,39 @@ QG_DEV float wave_sum(float v) {
 // product adds half an ulp, so |v' - x/d| <= 1.5 * 2^-23 * |x/d| < 2^-15.4
 // (|x/d| <= 127.0001), and fl32(x/d) is within 2^-18 of x/d. Rounding to an
 // integer only depends on which side of the nearest half-integer the value
-// lies, so whenever v' is at least 2^-14 away from every half-integer,
-// roundf(v') equals roundf(fl32(x/d)). Only within 2^-14 of a half-integer
-// (about 1 element in 8000) is the exact division taken. Tiny scales whose
-// reciprocal could be flushed also take the exact path.
+// lies, so whenever v' is at least 2^-14 away from every half-integer the
+// code of v' is the code of fl32(x/d); and then v' + copysign(0.5, v') is at
+// least 2^-14 away from every integer, so its fp32 sum (error <= 2^-17 below
+// 128) truncates to that code. Only within 2^-14 of a half-integer (about 1
+// element in 8000) is the exact division taken, rounded by roundf (half away
+// from zero). Tiny scales whose reciprocal could leave the normal range also
+// take the exact path.
 QG_DEV int q8_code(float x, float d, float r) {
-  float v = x * r;
-  const float m = fabsf(v);
-  const float f = m - floorf(m);
-  if (fabsf(f - 0.5f) < 0x1p-14f || d < 0x1p-100f) v = x / d;
-  const float q = fminf(fmaxf(roundf(v), -127.0f), 127.0f);
-  return (int)q;
+  const float v = x * r;
+  int q = (int)(v + __builtin_copysignf(0.5f, v));  // truncating conversion
+  const float f = __builtin_amdgcn_fractf(fabsf(v));
+  if (fabsf(f - 0.5f) < 0x1p-14f || d < 0x1p-100f) q = (int)roundf(x / d);
+  return q;
+}
+
+// Low bytes of four int32 codes packed little-endian into one dword.
+QG_DEV uint32_t pack4_bytes(int q0, int q1, int q2, int q3) {
+  const uint32_t lo = perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u);  // q0.b0, q1.b0, 0, 0
+  const uint32_t hi = perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);  // 0, 0, q2.b0, q3.b0
+  return lo | hi;
 }
 
 // Q8 quantization of 4 consecutive elements of a 32-element block whose
-// absolute maximum is `amax`: d = amax / 127 (IEEE division), codes =
-// round-half-away(x / d) clamped to +-127; all zero when amax == 0.
-// Returns the 4 codes packed little-endian in one dword and their sum.
+// scale is d = amax / 127 (IEEE division; 0 when amax == 0): codes =
+// round-half-away(x / d), all zero when d == 0. Returns the 4 codes packed
+// little-endian in one dword and their sum.
 QG_DEV uint32_t q8_pack4(float4 v, float d, int& sum) {
-  const float e[4] = {v.x, v.y, v.z, v.w};
   uint32_t packed = 0;
-  int s = 0;
   if (d != 0.0f) {
     const float r = __builtin_amdgcn_rcpf(d);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = q8_code(e[i], d, r);
-      s += q;
-      packed |= ((uint32_t)(q & 0xff)) << (8 * i);
-    }
+    packed = pack4_bytes(q8_code(v.x, d, r), q8_code(v.y, d, r), q8_code(v.z, d, r), q8_code(v.w, d, r));
   }
-  sum = s;
+  sum = dot4((int)packed, 0x01010101, 0);
   return packed;
 }
 
