@@ -73,9 +73,10 @@ _lib.qgemv_run_f32act.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, _vp]
 _lib.qgemv_debug_quantize_s16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots_s16.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.qgemv_debug_clear_launch_cache.argtypes = []
+_lib.qgemv_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp]
 _lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
 _lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
-for _f in ("qgemv_debug_clear_launch_cache", "qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
+for _f in ("qgemv_run_noalloc", "qgemv_debug_clear_launch_cache", "qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
            "qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
@@ -208,6 +209,21 @@ class GEMV(_Plan):
         wp = self._check_w(w, 0, "w")
         _check(_lib.qgemv_run(self._h, wp, _dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"), m,
                               _dev(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "qgemv_run")
+        return y
+
+    def run_noalloc(self, w, x, y=None, stream=None):
+        """qgemv_run with the library's fixed device scratch as the workspace
+        (qgemv_run_noalloc): no device allocation by the library; calls that
+        overlap on one GPU race."""
+        m = x.shape[0] if x.dim() == 2 else 1
+        if x.dim() not in (1, 2) or x.shape[-1] != self.k:
+            raise ValueError(f"x must be [m, {self.k}]")
+        if y is None:
+            y = torch.empty((m, self.n), dtype=torch.float32, device=x.device)
+        if y.numel() != m * self.n:
+            raise ValueError("y has the wrong size")
+        _check(_lib.qgemv_run_noalloc(self._h, self._check_w(w, 0, "w"), _dev(x, torch.float32, "x"),
+                                      _dev(y, torch.float32, "y"), m, _stream(stream)), "qgemv_run_noalloc")
         return y
 
     def quantize(self, x, ws=None, stream=None):

@@ -332,15 +332,12 @@ int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* w
 
 }  // namespace
 
-int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* ws, size_t ws_bytes,
-              void* stream) {
-  int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_run");
-  if (rc) return rc;
-  if (!w || !x || !y) return fail(QGEMV_EINVAL, "qgemv_run: null pointer");
-  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4))
-    return fail(QGEMV_EALIGN, "qgemv_run: w and x need 16-byte, y 4-byte alignment");
-  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run: launch failure injected (QGEMV_FAULT)");
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+
+// qgemv_run after validation: the workspace `ws` holds at least
+// layout_of(h, m).total() bytes.
+int gemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* ws, hipStream_t s) {
+  int rc;
   const qgemv_desc& d = h->d;
   if (m > kGemvMaxTokens || d.k > kFusedQuantMaxK || (m >= kMfmaMinTokens && mfma_supported(d.fmt))) {
     if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
@@ -366,6 +363,38 @@ int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* w
   p.m = m;
   memcpy(p.cb, h->cbw, sizeof p.cb);
   return check_launch(launch_gemv(d.fmt, p, false, s), "gemv");
+}
+
+}  // namespace
+
+int qgemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* ws, size_t ws_bytes,
+              void* stream) {
+  int rc = validate_gemv_call(h, m, ws, ws_bytes, "qgemv_run");
+  if (rc) return rc;
+  if (!w || !x || !y) return fail(QGEMV_EINVAL, "qgemv_run: null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return fail(QGEMV_EALIGN, "qgemv_run: w and x need 16-byte, y 4-byte alignment");
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run: launch failure injected (QGEMV_FAULT)");
+  return gemv_run(h, w, x, y, m, ws, static_cast<hipStream_t>(stream));
+}
+
+int qgemv_run_noalloc(qgemv_t h, const void* w, const float* x, float* y, int m, void* stream) {
+  if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "qgemv_run_noalloc: not a GEMV plan");
+  if (m < 1 || m > h->d.max_m) return fail(QGEMV_ESHAPE, "qgemv_run_noalloc: m=%d not in 1..%d", m, h->d.max_m);
+  if (!w || !x || !y) return fail(QGEMV_EINVAL, "qgemv_run_noalloc: null pointer");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4))
+    return fail(QGEMV_EALIGN, "qgemv_run_noalloc: w and x need 16-byte, y 4-byte alignment");
+  const size_t need = layout_of(h, m).total();
+  if (need > kNoAllocScratchBytes)
+    return fail(QGEMV_EWORKSPACE,
+                "qgemv_run_noalloc: this call needs %zu bytes of workspace, more than the fixed %zu-byte device "
+                "scratch; use qgemv_run with a caller-allocated workspace",
+                need, kNoAllocScratchBytes);
+  if (fault_injected()) return fail(QGEMV_EHIP, "qgemv_run_noalloc: launch failure injected (QGEMV_FAULT)");
+  void* ws = nullptr;
+  int rc = check_launch(noalloc_scratch(&ws), "qgemv_run_noalloc: device scratch");
+  if (rc) return rc;
+  return gemv_run(h, w, x, y, m, ws, static_cast<hipStream_t>(stream));
 }
 
 int qgemv_quantize(qgemv_t h, const float* x, int m, void* ws, size_t ws_bytes, void* stream) {

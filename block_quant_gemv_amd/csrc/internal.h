@@ -95,6 +95,12 @@ hipError_t kernel_residency(const void* kern, int threads, size_t lds, bool rais
 // Forgets every cached fact (the next launch of each kernel queries again).
 void clear_launch_cache();
 
+// Bytes of the fixed device scratch behind the allocation-free GEMV entry
+// point (noalloc.hip), and the address of the current device's copy of it
+// (looked up once per device with that device current).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Largest token count one GEMV launch handles.
 constexpr int kGemvMaxTokens = 16;
 // From this many tokens on, Q4_K and Q6_K GEMVs run on int8 MFMA (the VALU

@@ -204,6 +204,19 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t *bytes);
 int qgemv_run(qgemv_t h, const void *w, const float *x, float *y, int m,
               void *ws, size_t ws_bytes, void *stream);
 
+/* qgemv_run for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as qgemv_run, with the workspace taken from
+ * a fixed scratch array that the library holds in device memory, one copy
+ * per GPU for the life of the process, instead of a caller-allocated one.
+ * The call allocates nothing. Limit: the call's workspace
+ * (qgemv_workspace_size(h, m)) must fit in 4 MiB, else QGEMV_EWORKSPACE
+ * (every m = 1 call fits: k <= 65536 needs 80 KiB). Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (on two streams
+ * or from two threads) race and must be serialized by the caller. Other
+ * errors as qgemv_run; a failure to find the scratch is QGEMV_EHIP. */
+int qgemv_run_noalloc(qgemv_t h, const void *w, const float *x, float *y, int m, void *stream);
+
 /* The two halves of qgemv_run, for callers that apply several GEMVs to one
  * input (quantize once, then run each projection on the same quantized
  * activations -- the same-input projection sharing of "01 · Phase
