@@ -272,7 +272,7 @@ namespace {
 
 // Largest K for which qgemv_run fuses the activation quantizer into the GEMV.
 #ifndef QG_FUSED_MAXK
-#define QG_FUSED_MAXK 2048
+#define QG_FUSED_MAXK 4096
 #endif
 constexpr int64_t kFusedQuantMaxK = QG_FUSED_MAXK;
 

@@ -28,6 +28,7 @@
 //    partial sums per row; the LPR lanes of a row are summed by a butterfly
 //    and one lane stores y. No atomics: results are bitwise reproducible.
 #include "common.cuh"
+#include "formats.cuh"
 #include "internal.h"
 
 namespace qg {
@@ -54,8 +55,18 @@ namespace qg {
 #ifndef QG_WAVES_PER_WG
 #define QG_WAVES_PER_WG 4
 #endif
+#ifndef QG_FUSED_WAVES
+#define QG_FUSED_WAVES 16   // waves per workgroup when the kernel quantizes x itself
+#endif
+#ifndef QG_FUSED_WGS_PER_CU
+#define QG_FUSED_WGS_PER_CU 1
+#endif
 
 constexpr int kWavesPerWG = QG_WAVES_PER_WG;
+// With the quantizer in the prologue every workgroup quantizes all of x, so
+// fewer, larger workgroups quantize it fewer times (measured on MI355X at
+// K = 4096: 16 waves, one workgroup per CU).
+template <bool FUSEQ> constexpr int waves_per_wg() { return FUSEQ ? QG_FUSED_WAVES : kWavesPerWG; }
 // Packed bytes per step (max), per format. Measured on MI355X: smaller steps
 // give each wave more steps (a shorter pipeline tail after its last load)
 // and leave LDS for more resident waves; below ~2.5 KB the per-step overhead
@@ -71,291 +82,6 @@ constexpr int kLdsLimit = kLdsBytes;
 // Word 3 of a raw (unswizzled, unformatted) buffer resource on gfx9-family
 // GPUs, gfx950 included.
 constexpr int kBufferDword3 = 0x00020000;
-
-// ------------------------------------------------------------ activations --
-
-struct Act {
-  int x[8];     // 32 int8 codes, element order
-  float dx;     // block scale
-  int sa, sb;   // sums of codes 0..15 and 16..31
-};
-
-QG_DEV Act load_act(const uint8_t* tok, int U, int u) {
-  Act a;
-  const int4 lo = *reinterpret_cast<const int4*>(tok + 16 * u);
-  const int4 hi = *reinterpret_cast<const int4*>(tok + 16 * U + 16 * u);
-  const int2 mt = *reinterpret_cast<const int2*>(tok + 32 * U + 8 * u);
-  a.x[0] = lo.x; a.x[1] = lo.y; a.x[2] = lo.z; a.x[3] = lo.w;
-  a.x[4] = hi.x; a.x[5] = hi.y; a.x[6] = hi.z; a.x[7] = hi.w;
-  a.dx = __int_as_float(mt.x);
-  a.sa = (int)(int16_t)(mt.y & 0xffff);
-  a.sb = mt.y >> 16;
-  return a;
-}
-
-__host__ __device__ constexpr int act_token_bytes(int U) { return (40 * U + 15) / 16 * 16; }
-
-// ---------------------------------------------------------------- formats --
-
-struct FmtQ4_0 {
-  static constexpr int kUPB = 1, kBB = 18;
-  struct W { uint32_t q[4]; float d; };
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int, const uint32_t*) {
-    W w;
-    w.d = half_bits(lds_u16(t, off));
-    lds_read_unaligned<4>(t, off + 2, w.q);
-    return w;
-  }
-  // sum xq * (q - 8)
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s = dot4((int)(w.q[i] & 0x0F0F0F0Fu), a.x[i], s);
-      s = dot4((int)((w.q[i] >> 4) & 0x0F0F0F0Fu), a.x[4 + i], s);
-    }
-    return s - 8 * (a.sa + a.sb);
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    return fmaf((float)idot(w, a), a.dx * w.d, acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-struct FmtQ8_0 {
-  static constexpr int kUPB = 1, kBB = 34;
-  struct W { uint32_t q[8]; float d; };
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int, const uint32_t*) {
-    W w;
-    w.d = half_bits(lds_u16(t, off));
-    lds_read_unaligned<8>(t, off + 2, w.q);
-    return w;
-  }
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4((int)w.q[i], a.x[i], s);
-    return s;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    return fmaf((float)idot(w, a), a.dx * w.d, acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-// 4 codebook indices (one per byte, 0..15) -> 4 int8 codebook values.
-// Entries 0..7 come from {cb1:cb0}, 8..15 from {cb3:cb2}; bit 3 of each
-// index then picks between the two candidates with a third byte permute.
-// cb[4] holds the identity selector 0x03020100 in a register, so the pick
-// is one and-or (a register operand instead of a second literal).
-// b3 holds bit 3 of each index at bit 2 of its byte (any other bits of b3
-// are ignored).
-QG_DEV uint32_t cb_lookup4(uint32_t sel7, uint32_t b3, const uint32_t* cb) {
-  const uint32_t lo = perm(cb[1], cb[0], sel7);
-  const uint32_t hi = perm(cb[3], cb[2], sel7);
-  return perm(hi, lo, (b3 & 0x04040404u) | cb[4]);
-}
-// The 8 indices of one dword of packed nibbles (low nibbles, then high).
-QG_DEV void cb_lookup8(uint32_t q, const uint32_t* cb, uint32_t& vlo, uint32_t& vhi) {
-  vlo = cb_lookup4(q & 0x07070707u, q >> 1, cb);
-  vhi = cb_lookup4((q >> 4) & 0x07070707u, q >> 5, cb);
-}
-
-struct FmtIQ4_NL {
-  static constexpr int kUPB = 1, kBB = 18;
-  struct W { uint32_t v[8]; float d; };
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int, const uint32_t* cb) {
-    W w;
-    uint32_t q[4];
-    w.d = half_bits(lds_u16(t, off));
-    lds_read_unaligned<4>(t, off + 2, q);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cb_lookup8(q[i], cb, w.v[i], w.v[4 + i]);
-    return w;
-  }
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4((int)w.v[i], a.x[i], s);
-    return s;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    return fmaf((float)idot(w, a), a.dx * w.d, acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-struct FmtQ4_K {
-  static constexpr int kUPB = 8, kBB = 144;
-  struct W { uint32_t q[4]; float dsc, dmm; };
-  // off = byte offset of the super-block (16-byte aligned), g = sub-block.
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t*) {
-    W w;
-    const uint4 h = *reinterpret_cast<const uint4*>(t + off);
-    const uint4 q = *reinterpret_cast<const uint4*>(t + off + 16 + 16 * g);
-    w.q[0] = q.x; w.q[1] = q.y; w.q[2] = q.z; w.q[3] = q.w;
-    const float d = half_bits(h.x & 0xffffu);
-    const float dmin = half_bits(h.x >> 16);
-    const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);   // stream bits 0..63
-    const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);   // stream bits 32..95
-    const uint32_t sc = (uint32_t)(s_lo >> (6 * g)) & 63u;
-    const uint32_t mn = (uint32_t)(s_hi >> (16 + 6 * g)) & 63u;
-    w.dsc = d * (float)sc;
-    w.dmm = dmin * (float)mn;
-    return w;
-  }
-  // sum xq * q (codes 0..15)
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s = dot4((int)(w.q[i] & 0x0F0F0F0Fu), a.x[i], s);
-      s = dot4((int)((w.q[i] >> 4) & 0x0F0F0F0Fu), a.x[4 + i], s);
-    }
-    return s;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    acc = fmaf(a.dx * w.dsc, (float)idot(w, a), acc);
-    return fmaf(-(a.dx * w.dmm), (float)(a.sa + a.sb), acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-// Q4_K with a fifth code bit: sub-block j's fifth bits are the word
-// qh[4j..4j+3], element i (0..31) at bit 8 (i % 4) + i / 4. The four codes of
-// code dword i (elements 4i..4i+3, low nibbles) then take bit i of each
-// byte, and those of the high nibbles (elements 16 + 4i ..) bit 4 + i: one
-// shift and one mask move four fifth bits to bit 4 of their bytes.
-struct FmtQ5_K {
-  static constexpr int kUPB = 8, kBB = 176;
-  struct W { uint32_t c[8]; float dsc, dmm; };
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t*) {
-    W w;
-    const uint4 h = *reinterpret_cast<const uint4*>(t + off);
-    const uint32_t qh = *reinterpret_cast<const uint32_t*>(t + off + 16 + 4 * g);
-    const uint4 q = *reinterpret_cast<const uint4*>(t + off + 48 + 16 * g);
-    const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w.c[i] = (qq[i] & 0x0F0F0F0Fu) | ((qh << (4 - i)) & 0x10101010u);
-      w.c[4 + i] = ((qq[i] >> 4) & 0x0F0F0F0Fu) | ((qh >> i) & 0x10101010u);
-    }
-    const float d = half_bits(h.x & 0xffffu);
-    const float dmin = half_bits(h.x >> 16);
-    const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
-    const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
-    w.dsc = d * (float)((uint32_t)(s_lo >> (6 * g)) & 63u);
-    w.dmm = dmin * (float)((uint32_t)(s_hi >> (16 + 6 * g)) & 63u);
-    return w;
-  }
-  // sum xq * q (codes 0..31)
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4((int)w.c[i], a.x[i], s);
-    return s;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    acc = fmaf(a.dx * w.dsc, (float)idot(w, a), acc);
-    return fmaf(-(a.dx * w.dmm), (float)(a.sa + a.sb), acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-// IQ4_NL codes on a 256-element super-block with 6-bit sub-scales: header
-// d | scales_h | scales_l[4] (8 bytes), then sub-block j's 16 code bytes at
-// 8 + 16 j. Super-blocks (136 B) are 8-byte aligned in every step.
-struct FmtIQ4_XS {
-  static constexpr int kUPB = 8, kBB = 136;
-  struct W { uint32_t v[8]; float ds; };
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t* cb) {
-    W w;
-    const uint2 h = *reinterpret_cast<const uint2*>(t + off);
-    const uint2 qa = *reinterpret_cast<const uint2*>(t + off + 8 + 16 * g);
-    const uint2 qb = *reinterpret_cast<const uint2*>(t + off + 16 + 16 * g);
-    const uint32_t q[4] = {qa.x, qa.y, qb.x, qb.y};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cb_lookup8(q[i], cb, w.v[i], w.v[4 + i]);
-    const uint32_t ls = ((h.y >> (4 * g)) & 0xFu) | (((h.x >> (16 + 2 * g)) & 3u) << 4);
-    w.ds = half_bits(h.x & 0xffffu) * (float)((int)ls - 32);
-    return w;
-  }
-  QG_DEV static int idot(const W& w, const Act& a) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4((int)w.v[i], a.x[i], s);
-    return s;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    return fmaf((float)idot(w, a), a.dx * w.ds, acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) { out[0] = idot(w, a); }
-  static constexpr int kDotsPerUnit = 1;
-};
-
-struct FmtQ6_K {
-  static constexpr int kUPB = 8, kBB = 210;
-  struct W { uint32_t c[8]; float d; int sca, scb; };
-  // High 2 bits of the 4 codes in code dword w sit at bits 2*(w/2) of the
-  // bytes of qh dword (w & 1); move them to bits 4..5.
-  QG_DEV static uint32_t hi2(uint32_t qh, int k) {
-    const uint32_t v = (k == 0) ? (qh << 4) : (k == 1) ? (qh << 2) : (k == 2) ? qh : (qh >> 2);
-    return v & 0x30303030u;
-  }
-  QG_DEV static W load(const uint8_t* t, uint32_t off, int g, const uint32_t*) {
-    W w;
-    w.d = half_bits(lds_u16(t, off));
-    const uint32_t scs = lds_u16(t, off + 2 + 2 * g);
-    w.sca = (int)(int8_t)(scs & 0xffu);
-    w.scb = (int)(int8_t)(scs >> 8);
-    uint32_t ql[4], qh[2];
-    lds_read_unaligned<4>(t, off + 18 + 16 * g, ql);
-    lds_read_unaligned<2>(t, off + 146 + 8 * g, qh);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w.c[i] = (ql[i] & 0x0F0F0F0Fu) | hi2(qh[i & 1], i >> 1);
-      w.c[4 + i] = ((ql[i] >> 4) & 0x0F0F0F0Fu) | hi2(qh[(4 + i) & 1], (4 + i) >> 1);
-    }
-    return w;
-  }
-  // 16-element partial sums of xq * (q - 32)
-  QG_DEV static void pdot(const W& w, const Act& a, int& p0, int& p1) {
-    int s0 = 0, s1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s0 = dot4((int)w.c[i], a.x[i], s0);
-      s1 = dot4((int)w.c[4 + i], a.x[4 + i], s1);
-    }
-    p0 = s0 - 32 * a.sa;
-    p1 = s1 - 32 * a.sb;
-  }
-  QG_DEV static float fma(const W& w, const Act& a, float acc) {
-    int p0, p1;
-    pdot(w, a, p0, p1);
-    return fmaf(a.dx * w.d, (float)(w.sca * p0 + w.scb * p1), acc);
-  }
-  QG_DEV static void dots(const W& w, const Act& a, int32_t* out) {
-    int p0, p1;
-    pdot(w, a, p0, p1);
-    out[0] = p0;
-    out[1] = p1;
-  }
-  static constexpr int kDotsPerUnit = 2;
-};
-
-template <int FMT> struct FmtOf;
-template <> struct FmtOf<kQ4_0> { using T = FmtQ4_0; };
-template <> struct FmtOf<kQ8_0> { using T = FmtQ8_0; };
-template <> struct FmtOf<kIQ4_NL> { using T = FmtIQ4_NL; };
-template <> struct FmtOf<kQ4_K> { using T = FmtQ4_K; };
-template <> struct FmtOf<kQ6_K> { using T = FmtQ6_K; };
-template <> struct FmtOf<kQ5_K> { using T = FmtQ5_K; };
-template <> struct FmtOf<kIQ4_XS> { using T = FmtIQ4_XS; };
 
 // ------------------------------------------------------------ the kernel --
 
@@ -497,7 +223,8 @@ QG_DEV void stage_activations(uint8_t* smem, const GemvProblem& p, int U, int mc
 // before any pass's arithmetic); DOTS: integer-store checking epilogue;
 // FUSEQ: quantize fp32 activations in the prologue.
 template <int FMT, int MT, int P, bool DOTS, bool FUSEQ>
-__global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs args) {
+__global__ __launch_bounds__(waves_per_wg<FUSEQ>() * 64) void gemv_kernel(const GemvArgs args) {
+  constexpr int kWPG = waves_per_wg<FUSEQ>();
   using F = typename FmtOf<FMT>::T;
   extern __shared__ __align__(16) uint8_t smem[];
   const GemvProblem& p = args.p;
@@ -524,7 +251,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   uint8_t* tile = smem + g.act_bytes + wid * g.tile_buf;
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerWG;
+  const int64_t nwaves = (int64_t)gridDim.x * kWPG;
   const int LPR = g.LPR, RPP = g.RPP;  // powers of two: use shifts, not divisions
   const int lpr_log = g.lpr_log, rpp_log = 6 - g.lpr_log;
   const int lam = lane & (LPR - 1);
@@ -549,7 +276,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void gemv_kernel(const GemvArgs a
   // This wave's steps: row tiles rt_first + i * nwaves, each in nseg
   // K-segments. One register buffer holds the next step while the current
   // one is decoded from LDS.
-  const int64_t rt_first = (int64_t)blockIdx.x * kWavesPerWG + wid;
+  const int64_t rt_first = (int64_t)blockIdx.x * kWPG + wid;
   constexpr int kLPL = loads_per_lane<FMT>();
   // Loads go through a buffer resource that spans exactly the step's 16-byte
   // chunks: lanes past the end (and a whole wave past the last step) read
@@ -761,7 +488,7 @@ static int max_passes(int mt) { return mt <= 2 ? 8 : mt == 4 ? 4 : mt == 8 ? 2 :
 // Choose the step geometry for a format, shape and token tile; returns P.
 // nprob: problems sharing the launch (grouped mode), which together spread
 // over the chip.
-static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, int nprob, GemvGeom& g) {
+static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, bool fused, int nprob, GemvGeom& g) {
   g = GemvGeom{};
   const int upb = fmt_block_elems(fmt) / 32;
   const int bb = fmt_block_bytes(fmt);
@@ -776,7 +503,9 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, int nprob
   if (g.rb * g.RPP <= cap) {
     g.nseg = 1;
     g.SU = g.U;
-    const int pm = dots ? 1 : max_passes(MT);
+    // Fused-quantizer instances run 16 waves per workgroup (128 registers
+    // per lane): at most 4 passes, more would spill.
+    const int pm = dots ? 1 : (fused && max_passes(MT) > 4 ? 4 : max_passes(MT));
     while (P * 2 <= pm && g.rb * g.RPP * P * 2 <= cap) P *= 2;
     // Keep enough steps to spread the matrix over the whole chip.
     const int64_t want_waves = (int64_t)device_cus() * 8;
@@ -804,39 +533,41 @@ static int plan_geom(int fmt, int64_t n, int64_t k, int MT, bool dots, int nprob
 template <int FMT, int MT, int P, bool DOTS, bool FUSEQ>
 static hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   auto kern = gemv_kernel<FMT, MT, P, DOTS, FUSEQ>;
-  const size_t lds = (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf;
+  constexpr int kWPG = waves_per_wg<FUSEQ>();
+  const size_t lds = (size_t)a.g.act_bytes + (size_t)kWPG * a.g.tile_buf;
   // Persistent grid: no more workgroups than can be resident at once, so
   // every wave walks its share of the steps without a second launch round.
   // Resident workgroups per CU depend on the LDS size (activations vary with
   // K); the answer is cached per kernel, LDS size and device.
   int per_cu = 0, cus = 0;
-  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kWavesPerWG * 64, lds, true, &per_cu, &cus);
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kWPG * 64, lds, true, &per_cu, &cus);
   if (qe != hipSuccess) return qe;
   // A single matrix streams best with fewer resident workgroups than fit;
   // grouped launches (many small problems) use all of them.
-  if (a.p.nprob == 1 && QG_WGS_PER_CU > 0 && QG_WGS_PER_CU < per_cu) per_cu = QG_WGS_PER_CU;
+  const int cap = FUSEQ ? QG_FUSED_WGS_PER_CU : QG_WGS_PER_CU;
+  if (a.p.nprob == 1 && cap > 0 && cap < per_cu) per_cu = cap;
   // Waves available to each problem, then the fewest waves that still give
   // every wave the same number of row tiles (ceil), so no wave runs a
   // lone extra step at the end.
   // Grouped launches split the resident waves among their problems.
-  const int64_t cap_waves = (int64_t)cus * per_cu * kWavesPerWG;
+  const int64_t cap_waves = (int64_t)cus * per_cu * kWPG;
   int64_t wmax = cap_waves / a.p.nprob;
-  if (wmax < kWavesPerWG) wmax = kWavesPerWG;
+  if (wmax < kWPG) wmax = kWPG;
 #if QG_BALANCE
   const int64_t per_wave = (a.g.nrowtiles + wmax - 1) / wmax;
   const int64_t waves = (a.g.nrowtiles + per_wave - 1) / per_wave;
 #else
   const int64_t waves = a.g.nrowtiles < wmax ? a.g.nrowtiles : wmax;
 #endif
-  int64_t wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
+  int64_t wgs = (waves + kWPG - 1) / kWPG;
   // Grouped launches: never more workgroups than fit at once in all, so no
   // problem waits for a second round.
   if (a.p.nprob > 1) {
-    int64_t fit = cap_waves / kWavesPerWG / a.p.nprob;
+    int64_t fit = cap_waves / kWPG / a.p.nprob;
     if (fit < 1) fit = 1;
     if (wgs > fit) wgs = fit;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)wgs, (unsigned)a.p.nprob), dim3(kWavesPerWG * 64), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs, (unsigned)a.p.nprob), dim3(kWPG * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -846,7 +577,7 @@ static hipError_t launch_p(const GemvArgs& a, int P, hipStream_t s) {
     return launch_t<FMT, MT, 1, true, false>(a, s);
   } else {
     switch (P) {
-      case 8: if constexpr (MT <= 2) return launch_t<FMT, MT, 8, false, FUSEQ>(a, s); break;
+      case 8: if constexpr (MT <= 2 && !FUSEQ) return launch_t<FMT, MT, 8, false, FUSEQ>(a, s); break;
       case 4: if constexpr (MT <= 4) return launch_t<FMT, MT, 4, false, FUSEQ>(a, s); break;
       case 2: if constexpr (MT <= 8) return launch_t<FMT, MT, 2, false, FUSEQ>(a, s); break;
       default: break;
@@ -903,13 +634,14 @@ hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStr
   int mt = token_tile(p.tbl ? kGroupTokens : p.m);
   GemvArgs a;
   a.p = p;
-  int P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.tbl ? p.nprob : 1, a.g);
+  int P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.xf != nullptr, p.tbl ? p.nprob : 1, a.g);
+  const size_t wpg = p.xf ? (size_t)waves_per_wg<true>() : (size_t)waves_per_wg<false>();
   // Keep the staged activations within LDS; fall back to smaller token tiles.
-  while ((size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit && mt > 1) {
+  while ((size_t)a.g.act_bytes + wpg * a.g.tile_buf > (size_t)kLdsLimit && mt > 1) {
     mt >>= 1;
-    P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.tbl ? p.nprob : 1, a.g);
+    P = plan_geom(fmt, p.n, p.k, mt, dots_epilogue, p.xf != nullptr, p.tbl ? p.nprob : 1, a.g);
   }
-  if (P == 0 || (size_t)a.g.act_bytes + (size_t)kWavesPerWG * a.g.tile_buf > (size_t)kLdsLimit)
+  if (P == 0 || (size_t)a.g.act_bytes + wpg * a.g.tile_buf > (size_t)kLdsLimit)
     return hipErrorInvalidValue;
   if (p.tbl && mt < kGroupTokens) return hipErrorInvalidValue;  // entries cannot be split
   if (mt >= p.m || p.tbl) return launch_any(fmt, a, mt, P, dots_epilogue, s);

@@ -31,8 +31,8 @@
 #ifndef QG_Q5K_RBIG
 #define QG_Q5K_RBIG 4            // rows per wave iteration for large Q5_K matrices
 #endif
-#ifndef QG_Q4K_DIRECT_PF
-#define QG_Q4K_DIRECT_PF 1   // row groups in flight per wave (1 or 2)
+#ifndef QG_DIRECT_FUSED_WGS_PER_CU
+#define QG_DIRECT_FUSED_WGS_PER_CU 1
 #endif
 
 namespace qg {
@@ -48,40 +48,43 @@ QG_DEV uint32_t field6(uint32_t hi, uint32_t lo, uint32_t sh) {
   return __builtin_amdgcn_alignbit(hi, lo, sh) & 63u;
 }
 
+// Kernel arguments.
+struct DirectArgs {
+  const uint8_t* w;
+  const int8_t* xq;      // quantized activations (unfused)
+  const float* dx;
+  const float* xf;       // fp32 activations (fused quantization)
+  int8_t* xq_out;        // fused: workgroup 0 writes the codes here (optional)
+  float* dx_out;
+  int32_t* sx_out;
+  float* y;
+  int32_t* dots;
+  int64_t n, rb;
+};
+
 // FMT: kQ4_K or kQ5_K; R rows per iteration; JU sub-blocks per lane per row.
 // DOTS: store the exact per-sub-block integer dots D (int32 [n, 64 JU])
-// instead of y.
-template <int FMT, int JU, int R, bool DOTS>
-__global__ __launch_bounds__(kDirectWaves * 64) void kdirect_kernel(const uint8_t* __restrict__ W,
-                                                                     const int8_t* __restrict__ xq,
-                                                                     const float* __restrict__ dx,
-                                                                     float* __restrict__ y,
-                                                                     int32_t* __restrict__ dots, int64_t n,
-                                                                     int64_t rb) {
+// instead of y. FUSEQ: quantize the fp32 activations in the prologue (once
+// per workgroup, into LDS) instead of reading codes written by a separate
+// launch; NW waves per workgroup.
+template <int FMT, int JU, int R, bool DOTS, bool FUSEQ, int NW>
+__global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
+  const uint8_t* __restrict__ W = A.w;
+  float* __restrict__ y = A.y;
+  int32_t* __restrict__ dots = A.dots;
+  const int64_t n = A.n, rb = A.rb;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * kDirectWaves + wid;
-  const int64_t nw = (int64_t)gridDim.x * kDirectWaves;
+  const int64_t gw = (int64_t)blockIdx.x * NW + wid;
+  const int64_t nw = (int64_t)gridDim.x * NW;
   const int64_t ngroups = (n + R - 1) / R;
 
   // Activations of this lane's sub-blocks u = lane + 64 j: codes, scale and
-  // code sum.
+  // code sum (filled below, after the first weight loads are issued).
   int xa[JU][8];
   float xd[JU];
   int xsum[JU];
-#pragma unroll
-  for (int j = 0; j < JU; ++j) {
-    const int u = lane + 64 * j;
-    const int4 lo = reinterpret_cast<const int4*>(xq)[2 * u];
-    const int4 hi = reinterpret_cast<const int4*>(xq)[2 * u + 1];
-    xa[j][0] = lo.x; xa[j][1] = lo.y; xa[j][2] = lo.z; xa[j][3] = lo.w;
-    xa[j][4] = hi.x; xa[j][5] = hi.y; xa[j][6] = hi.z; xa[j][7] = hi.w;
-    xd[j] = DOTS ? 0.0f : dx[u];
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4(xa[j][i], 0x01010101, s);
-    xsum[j] = s;
-  }
+
   // Sub-block g = lane % 8 of its super-block. Scale field sc_g sits at bit
   // 6g of the 96-bit stream (header dwords 1..3), min m_g at bit 48 + 6g.
   const int g = lane & 7;
@@ -168,44 +171,104 @@ __global__ __launch_bounds__(kDirectWaves * 64) void kdirect_kernel(const uint8_
     }
   };
 
-#if QG_Q4K_DIRECT_PF > 1
-  // Two row groups in flight per wave: A holds group grp, B the next one;
-  // each buffer is refilled with the group two ahead once consumed.
-  u32x4 hA[R][JU], qA[R][JU], hB[R][JU], qB[R][JU];
-  uint32_t xA[R][JU], xB[R][JU];
-  load(hA, qA, xA, gw);
-  load(hB, qB, xB, gw + nw);
-  for (int64_t grp = gw; grp < ngroups; grp += 2 * nw) {
-    consume(hA, qA, xA, grp);
-    load(hA, qA, xA, grp + 2 * nw);
-    if (grp + nw >= ngroups) break;
-    consume(hB, qB, xB, grp + nw);
-    load(hB, qB, xB, grp + 3 * nw);
-  }
-#else
   // One row group in flight per wave; other resident waves cover the wait.
+  // The first group is requested before the activations are prepared, so
+  // both round trips overlap.
   u32x4 hA[R][JU], qA[R][JU];
   uint32_t xA[R][JU];
-  for (int64_t grp = gw; grp < ngroups; grp += nw) {
-    load(hA, qA, xA, grp);
-    consume(hA, qA, xA, grp);
+  load(hA, qA, xA, gw);
+
+  if constexpr (FUSEQ) {
+    // Quantize x once per workgroup into LDS: eight lanes per 32-element
+    // block, the activation quantizer's arithmetic; workgroup 0 also stores
+    // the codes for the caller.
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int U = 64 * JU;
+    uint32_t* s_codes = reinterpret_cast<uint32_t*>(smem);            // [U][8] dwords
+    float* s_dx = reinterpret_cast<float*>(smem + U * 32);             // [U]
+    int* s_sum = reinterpret_cast<int*>(smem + U * 36);                // [U]
+    const bool wb = A.xq_out && blockIdx.x == 0;
+    for (int i = threadIdx.x; i < U * 8; i += NW * 64) {  // whole 8-lane groups in or out
+      const float4 v = reinterpret_cast<const float4*>(A.xf)[i];
+      const int u = i >> 3, part = i & 7;
+      const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
+      int sm;
+      const uint32_t packed = q8_pack4(v, d, sm);
+      sm = sum4(sm);
+      sm += other_quad(sm);
+      s_codes[i] = packed;
+      if (part == 0) {
+        s_dx[u] = d;
+        s_sum[u] = sm;
+      }
+      if (wb) {
+        reinterpret_cast<uint32_t*>(A.xq_out)[i] = packed;
+        if (part == 0) {
+          A.dx_out[u] = d;
+          if (A.sx_out) A.sx_out[u] = sm;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < JU; ++j) {
+      const int u = lane + 64 * j;
+      const int4 lo = *reinterpret_cast<const int4*>(s_codes + 8 * u);
+      const int4 hi = *reinterpret_cast<const int4*>(s_codes + 8 * u + 4);
+      xa[j][0] = lo.x; xa[j][1] = lo.y; xa[j][2] = lo.z; xa[j][3] = lo.w;
+      xa[j][4] = hi.x; xa[j][5] = hi.y; xa[j][6] = hi.z; xa[j][7] = hi.w;
+      xd[j] = s_dx[u];
+      xsum[j] = s_sum[u];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < JU; ++j) {
+      const int u = lane + 64 * j;
+      const int4 lo = reinterpret_cast<const int4*>(A.xq)[2 * u];
+      const int4 hi = reinterpret_cast<const int4*>(A.xq)[2 * u + 1];
+      xa[j][0] = lo.x; xa[j][1] = lo.y; xa[j][2] = lo.z; xa[j][3] = lo.w;
+      xa[j][4] = hi.x; xa[j][5] = hi.y; xa[j][6] = hi.z; xa[j][7] = hi.w;
+      xd[j] = DOTS ? 0.0f : A.dx[u];
+      int sm = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm = dot4(xa[j][i], 0x01010101, sm);
+      xsum[j] = sm;
+    }
   }
-#endif
+
+  for (int64_t grp = gw; grp < ngroups; grp += nw) {
+    consume(hA, qA, xA, grp);
+    if (grp + nw < ngroups) load(hA, qA, xA, grp + nw);
+  }
 }
 
-template <int FMT, int JU, int R, bool DOTS>
+template <int FMT, int JU, int R, bool DOTS, bool FUSEQ, int NW>
 hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
-  auto kern = kdirect_kernel<FMT, JU, R, DOTS>;
+  auto kern = kdirect_kernel<FMT, JU, R, DOTS, FUSEQ, NW>;
+  const size_t lds = FUSEQ ? (size_t)64 * JU * 40 : 0;
   int nb = 0, cus = 0;  // resident workgroups per CU (cached occupancy query), compute units
-  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kDirectWaves * 64, 0, false, &nb, &cus);
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), NW * 64, lds, false, &nb, &cus);
   if (qe != hipSuccess) return qe;
-  const int per_cu = QG_DIRECT_WGS_PER_CU > 0 && QG_DIRECT_WGS_PER_CU < nb ? QG_DIRECT_WGS_PER_CU : nb;
+  const int cap = FUSEQ ? QG_DIRECT_FUSED_WGS_PER_CU : QG_DIRECT_WGS_PER_CU;
+  const int per_cu = cap > 0 && cap < nb ? cap : nb;
   const int64_t ngroups = (p.n + R - 1) / R;
-  int64_t waves = (int64_t)cus * per_cu * kDirectWaves;
+  int64_t waves = (int64_t)cus * per_cu * NW;
   if (waves > ngroups) waves = ngroups;
-  const int64_t wgs = (waves + kDirectWaves - 1) / kDirectWaves;
-  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kDirectWaves * 64), 0, s, p.w, p.xq, p.dx, p.y, p.dots,
-                     p.n, fmt_row_bytes(FMT, p.k));
+  const int64_t wgs = (waves + NW - 1) / NW;
+  DirectArgs a;
+  a.w = p.w;
+  a.xq = p.xq;
+  a.dx = p.dx;
+  a.xf = p.xf;
+  a.xq_out = p.xq_out;
+  a.dx_out = p.dx_out;
+  a.sx_out = p.sx_out;
+  a.y = p.y;
+  a.dots = p.dots;
+  a.n = p.n;
+  a.rb = fmt_row_bytes(FMT, p.k);
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -213,17 +276,48 @@ hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
 
 
 bool kdirect_ok(int fmt, const GemvProblem& p, bool dots) {
-  return (fmt == kQ4_K || fmt == kQ5_K) && p.m == 1 && !p.tbl && !p.xf && p.xq && (dots ? p.dots != nullptr : (p.dx && p.y)) &&
-         p.k % 2048 == 0 && p.k / 2048 >= 1 && p.k / 2048 <= 4 && p.n >= 1;
+  // fused quantization: one token, K up to 4096 (64 x 2 sub-blocks per lane)
+  const bool acts = p.xf ? (!dots && p.k <= 4096 && (!p.xq_out || p.dx_out)) : (p.xq != nullptr);
+  return (fmt == kQ4_K || fmt == kQ5_K) && p.m == 1 && !p.tbl && acts &&
+         (dots ? p.dots != nullptr : ((p.xf || p.dx) && p.y)) && p.k % 2048 == 0 && p.k / 2048 >= 1 &&
+         p.k / 2048 <= 4 && p.n >= 1;
 }
 
-template <int FMT, int R, bool DOTS>
+// Waves per workgroup for the fused kernel (one workgroup per CU): the
+// count that gives every wave the fewest row groups, then the one that
+// keeps the most CUs busy (12 waves: 3072 on 256 CUs, so 12288 and 24576
+// rows in groups of four divide evenly; 16 waves: 4096 single rows).
+static int fused_waves(int64_t ngroups) {
+  const int64_t cus = device_cus();
+  int best = 16;
+  int64_t best_gpw = 0, best_wgs = 0;
+  for (int nw : {16, 12}) {
+    const int64_t waves = cus * nw;
+    const int64_t gpw = (ngroups + waves - 1) / waves;
+    int64_t wgs = (ngroups + gpw * nw - 1) / (gpw * nw);
+    if (wgs > cus) wgs = cus;
+    if (best_gpw == 0 || gpw < best_gpw || (gpw == best_gpw && wgs > best_wgs)) {
+      best = nw;
+      best_gpw = gpw;
+      best_wgs = wgs;
+    }
+  }
+  return best;
+}
+
+template <int FMT, int R, bool DOTS, bool FUSEQ>
 static hipError_t launch_ju(const GemvProblem& p, hipStream_t s) {
-  switch (p.k / 2048) {
-    case 1: return launch_t<FMT, 1, R, DOTS>(p, s);
-    case 2: return launch_t<FMT, 2, R, DOTS>(p, s);
-    case 3: return launch_t<FMT, 3, R, DOTS>(p, s);
-    default: return launch_t<FMT, 4, R, DOTS>(p, s);
+  if constexpr (FUSEQ) {
+    const bool w12 = fused_waves((p.n + R - 1) / R) == 12;
+    if (p.k == 2048) return w12 ? launch_t<FMT, 1, R, DOTS, true, 12>(p, s) : launch_t<FMT, 1, R, DOTS, true, 16>(p, s);
+    return w12 ? launch_t<FMT, 2, R, DOTS, true, 12>(p, s) : launch_t<FMT, 2, R, DOTS, true, 16>(p, s);
+  } else {
+    switch (p.k / 2048) {
+      case 1: return launch_t<FMT, 1, R, DOTS, false, kDirectWaves>(p, s);
+      case 2: return launch_t<FMT, 2, R, DOTS, false, kDirectWaves>(p, s);
+      case 3: return launch_t<FMT, 3, R, DOTS, false, kDirectWaves>(p, s);
+      default: return launch_t<FMT, 4, R, DOTS, false, kDirectWaves>(p, s);
+    }
   }
 }
 
@@ -233,8 +327,9 @@ static hipError_t launch_fmt(const GemvProblem& p, bool dots, hipStream_t s) {
   // bytes in flight per wave) once there are enough rows to still give every
   // CU several waves, one row for smaller matrices (more waves).
   constexpr int RB = FMT == kQ5_K ? QG_Q5K_RBIG : QG_Q4K_RBIG;
-  if (p.n >= 8192) return dots ? launch_ju<FMT, RB, true>(p, s) : launch_ju<FMT, RB, false>(p, s);
-  return dots ? launch_ju<FMT, 1, true>(p, s) : launch_ju<FMT, 1, false>(p, s);
+  if (dots) return p.n >= 8192 ? launch_ju<FMT, RB, true, false>(p, s) : launch_ju<FMT, 1, true, false>(p, s);
+  if (p.xf) return p.n >= 8192 ? launch_ju<FMT, RB, false, true>(p, s) : launch_ju<FMT, 1, false, true>(p, s);
+  return p.n >= 8192 ? launch_ju<FMT, RB, false, false>(p, s) : launch_ju<FMT, 1, false, false>(p, s);
 }
 
 hipError_t launch_kdirect(int fmt, const GemvProblem& p, bool dots, hipStream_t s) {

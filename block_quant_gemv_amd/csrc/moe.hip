@@ -26,8 +26,13 @@
 #include "common.cuh"
 #include "internal.h"
 #include "moe.h"
+#include "route.cuh"
 #include "s16.h"
 #include "swiglu.h"
+
+#ifndef QG_MOE_FUSED
+#define QG_MOE_FUSED 1  // expert stage in two launches when the shapes allow it
+#endif
 
 namespace qg {
 
@@ -97,41 +102,6 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
   }
 }
 
-// Order-preserving 64-bit key of (logit, expert): larger logit first, then
-// the lower expert index.
-QG_DEV uint64_t route_key(float v, int e) {
-  uint32_t b = __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)(0x7fffffff - e);
-}
-
-template <int CTRL>
-QG_DEV uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-QG_DEV uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Largest key of the wave, in every lane (DPP within rows of 16, then the
-// four rows).
-QG_DEV uint64_t wave_max_key(uint64_t k) {
-  uint64_t o;
-  o = dpp_u64<0xB1>(k); k = o > k ? o : k;    // quad_perm [1,0,3,2]
-  o = dpp_u64<0x4E>(k); k = o > k ? o : k;    // quad_perm [2,3,0,1]
-  o = dpp_u64<0x141>(k); k = o > k ? o : k;   // row_half_mirror
-  o = dpp_u64<0x140>(k); k = o > k ? o : k;   // row_mirror
-  const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
-  const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
-  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-  return a > b ? a : b;
-}
-
 // One workgroup of 64 * m threads. Wave t selects token t's top_k experts and
 // their softmax weights; then the (token, slot) pairs are grouped by expert
 // into the table read by the grouped GEMV, in entries of at most
@@ -183,12 +153,10 @@ __global__ void route_kernel(const float* __restrict__ logits, int32_t* __restri
         if (!((taken >> i) & 1ull) && key > best) best = key;
       }
       best = wave_max_key(best);
-      const int bi = 0x7fffffff - (int)(uint32_t)best;
+      const int bi = route_key_expert(best);
       if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
       if (lane == k) {
-        uint32_t b = (uint32_t)(best >> 32);
-        b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
-        my_v = __uint_as_float(b);
+        my_v = route_key_value(best);
         my_i = bi;
       }
     }
@@ -298,6 +266,7 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool s16 = c.xq16 != nullptr;
+  if (QG_MOE_FUSED && !s16 && moe_fused_ok(c)) return launch_moe_fused(c, s);
   if (s16) {  // the expert GEMVs read 16-bit codes of x (scales and sums replace the Q8 ones)
     if (kGroupTokens != 1 || !c.hq16 || !q40_s16_grouped_ok(c.hidden) || !q40_s16_grouped_ok(c.inter))
       return hipErrorInvalidValue;

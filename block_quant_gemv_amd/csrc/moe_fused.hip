@@ -1,0 +1,592 @@
+// The MoE expert stage in two launches: routing + gate|up + SwiGLU +
+// re-quantization, then down + weighted combine.
+//
+// The router scores every expert and only the selected experts run; their
+// outputs are summed with the softmax weights of the selected logits, plus
+// the shared expert ("Understanding Qwen3.6-35B-A3B in llama.cpp", cnblogs,
+// section 1.1). Router, top-k, softmax, expert gate/up, SwiGLU, down and the
+// weighted sum all stay on the device ("01 · Phase overview: from 2B to 8B
+// to MoE", icman.com.cn, stage three); a launch costs several microseconds
+// of host and device time, so the stage is merged into as few launches as
+// its dependencies allow (the same page's issue ledger, items ㉓ and ㉘:
+// merged launches gained more than graph capture alone).
+//
+// moe_up_kernel: every workgroup first re-derives the routing from the
+// router's logits (at most 16 tokens x 4096 experts of fp32 in L2): top-k per
+// token by repeated wave-wide maxima of an order-preserving (logit, expert)
+// key, softmax over the selected logits, then the table of entries -- one
+// per distinct selected expert, in order of first selection (token-major,
+// slot order), holding every token that chose it, plus the shared expert
+// with all tokens. All workgroups build the same table, so no grid-wide
+// hand-off is needed, and each distinct expert's weights are read once for
+// all of its tokens. An item is (entry, 32 consecutive elements of h): the
+// 32 gate rows and the 32 matching up rows of the expert, so the workgroup
+// holds both halves of SwiGLU and a whole Q8 block of h, which it
+// re-quantizes itself. Sixteen waves take four rows each, loaded as one
+// coalesced range and decoded from LDS with the format views the decode GEMV
+// uses; the activations (the router launch's Q8 codes of x) are staged in
+// LDS per entry.
+//
+// moe_down_kernel: an item is (token, block of output rows). Wave s takes
+// slot s (routed slots in order, then the shared expert): its expert's rows
+// of the block as one coalesced range, the slot's re-quantized h in
+// registers. The slots' row sums meet in LDS and are combined in slot order
+// (weight times routed output, then plus the shared output), so the result
+// is bitwise reproducible without atomics.
+#include "common.cuh"
+#include "formats.cuh"
+#include "internal.h"
+#include "moe.h"
+#include "route.cuh"
+
+namespace qg {
+
+namespace {
+
+constexpr int kUpWaves = 16;        // waves per moe_up_kernel workgroup
+constexpr int kUpRows = 4;          // rows per wave per item (16 waves x 4 = 64 = 32 gate + 32 up)
+constexpr int kUpTok = 4;         // tokens per accumulation pass
+constexpr int kUpLPL = 9;           // 16-byte loads per lane: a wave's four rows, at most 9216 B
+constexpr int kDnLPL = 5;           // 16-byte loads per lane in moe_down_kernel
+constexpr int kMaxTok = 16;         // tokens a launch can hold
+// Tokens up to which the two-launch expert stage is used. Measured on MI355X
+// (256 experts, top-8 + shared, hidden 2048, expert intermediate 512, Q4_0,
+// expert weights from HBM): 18.1 / 25.8 / 33.6 us at 1 / 2 / 4 tokens against
+// 24.4 / 29.2 / 37.7 us for the six-launch path, but 56.5 / 100 us against
+// 52.4 / 81.0 us at 8 / 16 tokens, where each workgroup walks several items
+// one after another and the item's load, decode and re-quantization do not
+// overlap.
+constexpr int kFusedMaxTok = 4;
+constexpr int kMaxPairs = kMaxTok * 16;
+constexpr int kBufDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+// Routing of one call, identical in every workgroup (LDS).
+constexpr int kMaxExperts = 1024;
+
+struct alignas(16) Route {
+  int32_t ids[kMaxPairs];       // [token][slot] selected expert
+  float wts[kMaxPairs];         // [token][slot] softmax weight
+  int32_t ent_expert[kMaxPairs + 1];
+  uint32_t ent_mask[kMaxPairs + 1];  // tokens of the entry, bit t
+  uint32_t tok_mask[kMaxExperts];    // per expert: tokens that chose it
+  int32_t first_pair[kMaxExperts];   // per expert: its first (token, slot) pair
+  int32_t wave_first[kMaxPairs / 64];
+  int32_t n_entries;
+};
+
+// Wave `wid` < m selects token wid's top_k experts (ties to the lower index)
+// and their softmax weights; then the entries are built. Ends with a barrier.
+// NPL: logits per lane (n_experts <= 64 * NPL).
+template <int NPL>
+QG_DEV void build_route(Route& R, const float* __restrict__ logits, int n_experts, int top_k, int m, int wid,
+                        int lane, int nthreads) {
+  const int tid = threadIdx.x;
+  if (wid < m) {
+    const float* lg = logits + (int64_t)wid * n_experts;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < n_experts ? lg[e] : 0.0f;
+    }
+    uint32_t taken = 0;  // bit i: expert lane + 64 i selected (or absent)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i >= n_experts) taken |= 1u << i;
+    float my_v = -INFINITY;  // lane k keeps the k-th selection
+    int my_i = 0;
+    for (int k = 0; k < top_k; ++k) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const uint64_t key = route_key(v[i], lane + 64 * i);
+        if (!((taken >> i) & 1u) && key > best) best = key;
+      }
+      best = wave_max_key(best);
+      const int bi = route_key_expert(best);
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == k) {
+        my_v = route_key_value(best);
+        my_i = bi;
+      }
+    }
+    const float v0 = __shfl(my_v, 0, 64);
+    const float ez = (lane < top_k) ? expf(my_v - v0) : 0.0f;
+    const float den = wave_sum(ez);
+    if (lane < top_k) {
+      R.ids[wid * top_k + lane] = my_i;
+      R.wts[wid * top_k + lane] = ez / den;
+    }
+  }
+  for (int i = tid; i < n_experts; i += nthreads) {
+    R.tok_mask[i] = 0u;
+    R.first_pair[i] = 0x7fffffff;
+  }
+  __syncthreads();
+  // Pair p (token p / top_k, slot p % top_k) opens an entry when no earlier
+  // pair chose the same expert; the entry holds every token that chose it.
+  const int np = m * top_k;
+  if (tid < np) {
+    const int ex = R.ids[tid];
+    atomicOr(&R.tok_mask[ex], 1u << (tid / top_k));
+    atomicMin(&R.first_pair[ex], tid);
+  }
+  __syncthreads();
+  bool first = false;
+  uint32_t mask = 0;
+  int e = -1;
+  if (tid < np) {
+    e = R.ids[tid];
+    first = R.first_pair[e] == tid;
+    mask = R.tok_mask[e];
+  }
+  // Entry index = number of first pairs before this one (np <= 256: at most
+  // four waves of pairs).
+  const uint64_t bal = __ballot(first);
+  if (lane == 0 && wid < kMaxPairs / 64) R.wave_first[wid] = __popcll(bal);
+  __syncthreads();
+  if (first) {
+    int idx = __popcll(bal & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wid; ++w) idx += R.wave_first[w];
+    R.ent_expert[idx] = e;
+    R.ent_mask[idx] = mask;
+  }
+  if (tid == 0) {
+    int nr = 0;
+    for (int w = 0; w < (np + 63) / 64; ++w) nr += R.wave_first[w];
+    R.ent_expert[nr] = -1;  // the shared expert, every token
+    R.ent_mask[nr] = m >= 32 ? 0xffffffffu : ((1u << m) - 1u);
+    R.n_entries = nr + 1;
+  }
+  __syncthreads();
+}
+
+// Slot of expert e in token t's selection (the shared expert: top_k).
+QG_DEV int slot_of(const Route& R, int t, int e, int top_k) {
+  if (e < 0) return top_k;
+  int s = 0;
+  for (int k = 0; k < top_k; ++k)
+    if (R.ids[t * top_k + k] == e) s = k;
+  return s;
+}
+
+}  // namespace
+
+struct MoeFusedArgs {
+  const float* logits;
+  int n_experts, top_k, m;
+  int32_t* ids_out;
+  float* wts_out;
+  const uint8_t *gu, *gu_shared, *dn, *dn_shared;
+  int64_t gu_stride, dn_stride;
+  const int8_t* xq;
+  const float* dx;
+  int64_t hidden, inter;
+  int64_t rb_gu, rb_dn;     // row bytes of gate|up (K = hidden) and down (K = inter)
+  float* gu_out;            // [m * (top_k + 1), 2 inter]
+  float* h_out;             // [m * (top_k + 1), inter]
+  int8_t* hq;
+  float* hd;
+  int32_t* hs;
+  float* y;                 // [m, hidden]
+  uint32_t cb[4];
+  int act_bytes;            // LDS bytes of the staged activations (m tokens)
+  int tile_bytes;           // LDS bytes of one wave's weight tile
+  int dn_rows;              // output rows per down item
+};
+
+// ------------------------------------------------------------ gate|up --
+
+// LPL: 16-byte loads per lane (a wave's four rows); NPL: logits per lane in
+// the routing prologue (n_experts <= 64 NPL).
+template <int FMT, int LPL, int NPL>
+__global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArgs a) {
+  using F = typename FmtOf<FMT>::T;
+  extern __shared__ __align__(16) uint8_t smem[];
+  Route& R = *reinterpret_cast<Route*>(smem);
+  float* s_gu = reinterpret_cast<float*>(smem + sizeof(Route));         // [kMaxTok][64]
+  uint8_t* act = smem + sizeof(Route) + kMaxTok * 64 * sizeof(float);   // staged activations
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  uint8_t* tile = act + a.act_bytes + wid * a.tile_bytes;
+
+  const int U = (int)(a.hidden / 32);      // 32-element units per row (multiple of 64)
+  const int tokb = act_token_bytes(U);
+  // Activations of every token (the router launch's Q8 codes of x), staged
+  // once per workgroup: token t at act + t * tokb. The loads are issued
+  // before the routing's logit loads so both round trips overlap.
+  constexpr int kStage = 2;  // (token, unit) tasks per thread: m * U <= 2048
+  int4 st_lo[kStage], st_hi[kStage];
+  float st_d[kStage];
+#pragma unroll
+  for (int r = 0; r < kStage; ++r) {
+    const int i = threadIdx.x + r * kUpWaves * 64;
+    if (i < a.m * U) {
+      const int t = i / U, u = i - t * U;
+      const int4* xr = reinterpret_cast<const int4*>(a.xq + (int64_t)t * a.hidden);
+      st_lo[r] = xr[2 * u];
+      st_hi[r] = xr[2 * u + 1];
+      st_d[r] = a.dx[(int64_t)t * U + u];
+    }
+  }
+  build_route<NPL>(R, a.logits, a.n_experts, a.top_k, a.m, wid, lane, blockDim.x);
+#pragma unroll
+  for (int r = 0; r < kStage; ++r) {
+    const int i = threadIdx.x + r * kUpWaves * 64;
+    if (i < a.m * U) {
+      const int t = i / U, u = i - t * U;
+      uint8_t* tok = act + t * tokb;
+      const int ones = 0x01010101;
+      const int4 lo = st_lo[r], hi = st_hi[r];
+      const int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
+      const int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
+      *reinterpret_cast<int4*>(tok + 16 * u) = lo;
+      *reinterpret_cast<int4*>(tok + 16 * U + 16 * u) = hi;
+      *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) = make_int2(__float_as_int(st_d[r]), (sa & 0xffff) | (sb << 16));
+    }
+  }
+  __syncthreads();
+  const int np = a.m * a.top_k;
+  if (blockIdx.x == 0)
+    for (int p = threadIdx.x; p < np; p += blockDim.x) {
+      a.ids_out[p] = R.ids[p];
+      a.wts_out[p] = R.wts[p];
+    }
+
+  const int tiles = (int)(a.inter / 32);
+  const int n_items = R.n_entries * tiles;
+  const int S1 = a.top_k + 1;
+  uint32_t cbr[5] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3], 0x03020100u};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int en = item / tiles, j = item - en * tiles;
+    const int e = R.ent_expert[en];
+    const uint32_t mask = R.ent_mask[en];
+    const int c = __popc(mask);
+    const uint8_t* W = e < 0 ? a.gu_shared : a.gu + (int64_t)e * a.gu_stride;
+    // This wave's four rows: virtual rows 4 wid .. 4 wid + 3 of the item
+    // (0..31 gate, 32..63 up), contiguous in the matrix.
+    const int v0 = kUpRows * wid;
+    const int64_t row0 = v0 < 32 ? (int64_t)32 * j + v0 : a.inter + (int64_t)32 * j + (v0 - 32);
+    const int64_t b0 = row0 * a.rb_gu;
+    const int64_t a0 = b0 & ~(int64_t)15;
+    const int nch = (int)(((b0 + kUpRows * a.rb_gu + 15) & ~(int64_t)15) - a0) >> 4;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + a0), 0, nch * 16, kBufDword3);
+    u32x4 buf[LPL];
+#pragma unroll
+    for (int i = 0; i < LPL; ++i)
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, kNonTemporal);
+
+    // Weights to the wave's LDS tile, then decode: lane l takes units
+    // l + 64 jj of each row.
+#pragma unroll
+    for (int i = 0; i < LPL; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
+    }
+    const uint32_t base = (uint32_t)(b0 - a0);
+    // Tokens in chunks of kUpTok (accumulators stay in registers); the
+    // weights are decoded from LDS again for each chunk.
+    uint32_t mrem = mask;  // tokens of the entry not yet taken, ascending
+    for (int t0 = 0; t0 < c; t0 += kUpTok) {
+      int tok[kUpTok];  // token ids of this chunk
+#pragma unroll
+      for (int t = 0; t < kUpTok; ++t) {
+        tok[t] = mrem ? __builtin_ctz(mrem) : 0;
+        mrem &= mrem - 1;
+      }
+      float acc[kUpRows][kUpTok];
+#pragma unroll
+      for (int r = 0; r < kUpRows; ++r)
+#pragma unroll
+        for (int t = 0; t < kUpTok; ++t) acc[r][t] = 0.0f;
+      for (int u = lane; u < U; u += 64) {
+        const uint32_t uoff = (uint32_t)((u / F::kUPB) * F::kBB);
+        const int sub = u % F::kUPB;
+        Act x[kUpTok];
+#pragma unroll
+        for (int t = 0; t < kUpTok; ++t)
+          if (t0 + t < c) x[t] = load_act(act + tok[t] * tokb, U, u);
+#pragma unroll
+        for (int r = 0; r < kUpRows; ++r) {
+          const typename F::W w = F::load(tile, base + (uint32_t)(r * a.rb_gu) + uoff, sub, cbr);
+#pragma unroll
+          for (int t = 0; t < kUpTok; ++t)
+            if (t0 + t < c) acc[r][t] = F::fma(w, x[t], acc[r][t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kUpTok; ++t) {
+        if (t0 + t < c) {
+#pragma unroll
+          for (int r = 0; r < kUpRows; ++r) {
+            const float sum = group_sum(acc[r][t], 64);
+            if (lane == 0) s_gu[(t0 + t) * 64 + v0 + r] = sum;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // SwiGLU and Q8 re-quantization of the item's 32 elements of h, eight
+    // lanes per token (the activation quantizer's arithmetic).
+    if ((int)threadIdx.x < 8 * c) {
+      const int i = threadIdx.x >> 3, part = threadIdx.x & 7;
+      int t = -1;
+      for (int q = 0; q <= i; ++q) t = __builtin_ffs(mask >> (t + 1)) + t;
+      const int64_t row = (int64_t)t * S1 + slot_of(R, t, e, a.top_k);
+      const float4 g = *reinterpret_cast<const float4*>(s_gu + i * 64 + 4 * part);
+      const float4 up = *reinterpret_cast<const float4*>(s_gu + i * 64 + 32 + 4 * part);
+      float4 h;
+      h.x = g.x / (1.0f + expf(-g.x)) * up.x;
+      h.y = g.y / (1.0f + expf(-g.y)) * up.y;
+      h.z = g.z / (1.0f + expf(-g.z)) * up.z;
+      h.w = g.w / (1.0f + expf(-g.w)) * up.w;
+      const int64_t col = (int64_t)32 * j + 4 * part;
+      *reinterpret_cast<float4*>(a.gu_out + row * 2 * a.inter + col) = g;
+      *reinterpret_cast<float4*>(a.gu_out + row * 2 * a.inter + a.inter + col) = up;
+      *reinterpret_cast<float4*>(a.h_out + row * a.inter + col) = h;
+      float amax = fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w)));
+      amax = max8(amax);
+      const float d = (amax > 0.0f) ? amax / 127.0f : 0.0f;
+      int s;
+      const uint32_t packed = q8_pack4(h, d, s);
+      *reinterpret_cast<uint32_t*>(a.hq + row * a.inter + col) = packed;
+      s = sum4(s);
+      s += other_quad(s);
+      if (part == 0) {
+        a.hd[row * (a.inter / 32) + j] = d;
+        a.hs[row * (a.inter / 32) + j] = s;
+      }
+    }
+    __syncthreads();  // s_gu is reused by the next item
+  }
+}
+
+// ---------------------------------------------------------- down + combine --
+
+// LPR: lanes per row (units of h per row, <= 64); JU: units per lane.
+template <int FMT, int LPR, int JU>
+__global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
+  using F = typename FmtOf<FMT>::T;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int S1 = a.top_k + 1;
+  const int RB = a.dn_rows;                         // output rows per item (multiple of 64 / LPR)
+  float* s_out = reinterpret_cast<float*>(smem);   // [S1][RB]
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's slot
+  const int lane = threadIdx.x & 63;
+  uint8_t* tile = smem + (size_t)kMaxTok * 64 * sizeof(float) + s * a.tile_bytes;
+  constexpr int RPP = 64 / LPR;
+  const int lam = lane % LPR, rho = lane / LPR;
+  const int U = (int)(a.inter / 32);
+  const int nblk = (int)((a.hidden + RB - 1) / RB);
+  const int n_items = a.m * nblk;
+  uint32_t cbr[5] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3], 0x03020100u};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int t = item / nblk, blk = item - t * nblk;
+    const int64_t r0 = (int64_t)blk * RB;
+    const int nrows = (int)((a.hidden - r0) < RB ? (a.hidden - r0) : RB);
+    const int e = s < a.top_k ? a.ids_out[t * a.top_k + s] : -1;
+    const uint8_t* W = e < 0 ? a.dn_shared : a.dn + (int64_t)e * a.dn_stride;
+    const int64_t b0 = r0 * a.rb_dn;
+    const int64_t a0 = b0 & ~(int64_t)15;
+    const int nch = (int)(((b0 + nrows * a.rb_dn + 15) & ~(int64_t)15) - a0) >> 4;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + a0), 0, nch * 16, kBufDword3);
+    u32x4 buf[kDnLPL];
+#pragma unroll
+    for (int i = 0; i < kDnLPL; ++i)
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, kNonTemporal);
+    // The slot's re-quantized h: this lane's units lam + LPR jj.
+    const int64_t hrow = (int64_t)t * S1 + s;
+    Act x[JU];
+#pragma unroll
+    for (int jj = 0; jj < JU; ++jj) {
+      const int u = lam + LPR * jj;
+      const int4 lo = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u];
+      const int4 hi = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u + 1];
+      x[jj].x[0] = lo.x; x[jj].x[1] = lo.y; x[jj].x[2] = lo.z; x[jj].x[3] = lo.w;
+      x[jj].x[4] = hi.x; x[jj].x[5] = hi.y; x[jj].x[6] = hi.z; x[jj].x[7] = hi.w;
+      x[jj].dx = a.hd[hrow * U + u];
+      const int ones = 0x01010101;
+      x[jj].sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
+      x[jj].sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
+    }
+#pragma unroll
+    for (int i = 0; i < kDnLPL; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
+    }
+    const uint32_t base = (uint32_t)(b0 - a0);
+    for (int p = 0; p * RPP < nrows; ++p) {
+      int rl = p * RPP + rho;
+      const bool valid = rl < nrows;
+      rl = valid ? rl : nrows - 1;
+      float acc = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < JU; ++jj) {
+        const int u = lam + LPR * jj;
+        const typename F::W w =
+            F::load(tile, base + (uint32_t)(rl * a.rb_dn) + (uint32_t)((u / F::kUPB) * F::kBB), u % F::kUPB, cbr);
+        acc = F::fma(w, x[jj], acc);
+      }
+      const float sum = group_sum(acc, LPR);
+      if (lam == 0 && valid) s_out[s * RB + rl] = sum;
+    }
+    __syncthreads();
+    // y = sum over routed slots in order of weight * output, plus the shared expert.
+    for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+      float acc = 0.0f;
+      for (int k = 0; k < a.top_k; ++k) acc = fmaf(a.wts_out[t * a.top_k + k], s_out[k * RB + r], acc);
+      a.y[(int64_t)t * a.hidden + r0 + r] = acc + s_out[a.top_k * RB + r];
+    }
+    __syncthreads();  // s_out and the tiles are reused by the next item
+  }
+}
+
+// ------------------------------------------------------------- launchers --
+
+namespace {
+
+size_t up_lds(const MoeFusedArgs& a) {
+  return sizeof(Route) + (size_t)kMaxTok * 64 * sizeof(float) + (size_t)a.act_bytes +
+         (size_t)kUpWaves * a.tile_bytes;
+}
+
+template <int FMT, int LPL, int NPL>
+hipError_t launch_up_t(const MoeFusedArgs& a, int n_items_max, hipStream_t s) {
+  auto kern = moe_up_kernel<FMT, LPL, NPL>;
+  const size_t lds = up_lds(a);
+  int per_cu = 0, cus = 0;
+  hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), kUpWaves * 64, lds, true, &per_cu, &cus);
+  if (e != hipSuccess) return e;
+  int64_t grid = (int64_t)cus * per_cu;
+  if (grid > n_items_max) grid = n_items_max;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kUpWaves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+// Loads per lane for a wave's four rows of rb bytes (plus alignment).
+int up_loads(int64_t rb) { return (int)((kUpRows * rb + 32 + 1023) / 1024); }
+
+template <int FMT>
+hipError_t launch_up_npl(const MoeFusedArgs& a, int n_items_max, hipStream_t s) {
+  const bool small = up_loads(a.rb_gu) <= 5;
+  if (a.n_experts <= 256)
+    return small ? launch_up_t<FMT, 5, 4>(a, n_items_max, s) : launch_up_t<FMT, kUpLPL, 4>(a, n_items_max, s);
+  return small ? launch_up_t<FMT, 5, 16>(a, n_items_max, s) : launch_up_t<FMT, kUpLPL, 16>(a, n_items_max, s);
+}
+
+template <int FMT, int LPR, int JU>
+hipError_t launch_dn_t(const MoeFusedArgs& a, hipStream_t s) {
+  auto kern = moe_down_kernel<FMT, LPR, JU>;
+  const int S1 = a.top_k + 1;
+  const size_t lds = (size_t)kMaxTok * 64 * sizeof(float) + (size_t)S1 * a.tile_bytes;
+  int per_cu = 0, cus = 0;
+  hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), S1 * 64, lds, true, &per_cu, &cus);
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)a.m * ((a.hidden + a.dn_rows - 1) / a.dn_rows);
+  int64_t grid = (int64_t)cus * per_cu;
+  if (grid > items) grid = items;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S1 * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool moe_fused_ok(const MoeCall& c) {
+  const int64_t rb_gu = fmt_row_bytes(c.fmt, c.hidden), rb_dn = fmt_row_bytes(c.fmt, c.inter);
+  if (rb_gu <= 0 || rb_dn <= 0) return false;
+  const int64_t U = c.inter / 32;
+  if (c.m < 1 || c.m > kFusedMaxTok || c.top_k < 1 || c.top_k > 15 || c.n_experts > kMaxExperts) return false;
+  if (c.hidden % 2048 || c.hidden > 8192 || c.inter % 32 || c.m * (c.hidden / 32) > 2048) return false;
+  if (U != 16 && U != 32 && U != 64 && U != 128) return false;
+  if (up_loads(rb_gu) > kUpLPL) return false;   // a wave's four rows in one load
+  const int rpp = 64 / (int)(U < 64 ? U : 64);
+  const int rows = rpp * 2 > 8 ? rpp * 2 : 8;
+  if (rows * rb_dn + 32 > (int64_t)kDnLPL * 1024) return false;
+  const size_t up = sizeof(Route) + (size_t)kMaxTok * 64 * 4 + (size_t)c.m * act_token_bytes((int)(c.hidden / 32)) +
+                    (size_t)kUpWaves * (size_t)((kUpRows * rb_gu + 32 + 15) / 16 * 16 + 16);
+  return up <= (size_t)kLdsBytes;
+}
+
+hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
+  if (!moe_fused_ok(c)) return hipErrorInvalidValue;
+  MoeFusedArgs a;
+  a.logits = c.logits;
+  a.n_experts = c.n_experts;
+  a.top_k = c.top_k;
+  a.m = c.m;
+  a.ids_out = c.ids;
+  a.wts_out = c.wts;
+  a.gu = c.gu;
+  a.gu_shared = c.gu_shared;
+  a.dn = c.dn;
+  a.dn_shared = c.dn_shared;
+  a.gu_stride = c.gu_stride;
+  a.dn_stride = c.dn_stride;
+  a.xq = c.xq;
+  a.dx = c.dx;
+  a.hidden = c.hidden;
+  a.inter = c.inter;
+  a.rb_gu = fmt_row_bytes(c.fmt, c.hidden);
+  a.rb_dn = fmt_row_bytes(c.fmt, c.inter);
+  a.gu_out = c.gu_out;
+  a.h_out = c.h;
+  a.hq = c.hq;
+  a.hd = c.hd;
+  a.hs = c.hs;
+  a.y = c.y;
+  for (int i = 0; i < 4; ++i) a.cb[i] = c.cb[i];
+  a.act_bytes = c.m * act_token_bytes((int)(c.hidden / 32));
+  a.tile_bytes = (int)((kUpRows * a.rb_gu + 32 + 15) / 16 * 16 + 16);
+  const int U = (int)(c.inter / 32);
+  const int rpp = 64 / (U < 64 ? U : 64);
+  a.dn_rows = rpp * 2 > 8 ? rpp * 2 : 8;
+  // Entries: at most one per (token, slot) pair, plus the shared expert.
+  const int n_items_max = (c.m * c.top_k + 1) * (int)(c.inter / 32);
+  hipError_t e;
+  switch (c.fmt) {
+    case kQ4_0: e = launch_up_npl<kQ4_0>(a, n_items_max, s); break;
+    case kQ8_0: e = launch_up_npl<kQ8_0>(a, n_items_max, s); break;
+    case kIQ4_NL: e = launch_up_npl<kIQ4_NL>(a, n_items_max, s); break;
+    case kQ4_K: e = launch_up_npl<kQ4_K>(a, n_items_max, s); break;
+    case kQ6_K: e = launch_up_npl<kQ6_K>(a, n_items_max, s); break;
+    case kQ5_K: e = launch_up_npl<kQ5_K>(a, n_items_max, s); break;
+    case kIQ4_XS: e = launch_up_npl<kIQ4_XS>(a, n_items_max, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  // The down launch reuses the tile size of its own rows.
+  MoeFusedArgs d = a;
+  d.tile_bytes = (int)((a.dn_rows * a.rb_dn + 32 + 15) / 16 * 16 + 16);
+  switch (c.fmt) {
+#define QG_DN(F)                                                           \
+  case F:                                                                  \
+    switch (U) {                                                           \
+      case 16: return launch_dn_t<F, 16, 1>(d, s);                         \
+      case 32: return launch_dn_t<F, 32, 1>(d, s);                         \
+      case 64: return launch_dn_t<F, 64, 1>(d, s);                         \
+      default: return launch_dn_t<F, 64, 2>(d, s);                         \
+    }
+    QG_DN(kQ4_0)
+    QG_DN(kQ8_0)
+    QG_DN(kIQ4_NL)
+    QG_DN(kQ4_K)
+    QG_DN(kQ6_K)
+    QG_DN(kQ5_K)
+    QG_DN(kIQ4_XS)
+#undef QG_DN
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qg
