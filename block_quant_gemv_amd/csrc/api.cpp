@@ -88,8 +88,8 @@ Layout layout_of(const qgemv_plan* h, int m) {
       // quantizer for every plan so that plans with the same k share a
       // quantized workspace
       L.add("xqt", gemm32_tiled_act_bytes(d.k));
-      const size_t part = mfma_supported(d.fmt) ? gemm32_partials_bytes(d.n, d.k) : 0;
-      if (part) L.add("partials", part);
+      L.add("dxt", (size_t)(d.k / 32) * 32 * 4);
+      L.add("cxt", (size_t)(d.k / 32) * 32 * 4);
     }
   } else if (d.kind == QKIND_FFN) {
     L.add("xq", (size_t)m * d.hidden);
@@ -288,10 +288,16 @@ int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const 
 
 int gemv_quantize(qgemv_t h, const float* x, int m, void* ws, hipStream_t s) {
   const Layout L = layout_of(h, m);
-  int8_t* xqt = m >= kMfmaMinTokens ? region<int8_t>(ws, L, "xqt") : nullptr;
+  TiledAct t;
+  if (m >= kMfmaMinTokens) {
+    t.codes = region<int8_t>(ws, L, "xqt");
+    t.dx = region<float>(ws, L, "dxt");
+    t.c = region<float>(ws, L, "cxt");
+    t.kblocks = (int)(h->d.k / 32);
+  }
   return check_launch(launch_quant_q8(x, region<int8_t>(ws, L, "xq"), region<float>(ws, L, "dx"),
-                                      region<int32_t>(ws, L, "sx"), (int64_t)m * (h->d.k / 32), s, xqt,
-                                      (int)(h->d.k / 32)),
+                                      region<int32_t>(ws, L, "sx"), (int64_t)m * (h->d.k / 32), s,
+                                      m >= kMfmaMinTokens ? &t : nullptr),
                       "quantize");
 }
 
@@ -303,9 +309,8 @@ int gemv_from_quantized(qgemv_t h, const void* w, float* y, int m, const void* w
   const float* dx = region<float>(wsm, L, "dx");
   const int32_t* sx = region<int32_t>(wsm, L, "sx");
   if (m >= kMfmaMinTokens && mfma_supported(d.fmt)) {
-    float* part = gemm32_partials_bytes(d.n, d.k) ? region<float>(wsm, L, "partials") : nullptr;
-    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), region<int8_t>(wsm, L, "xqt"), dx,
-                                      sx, y, part, d.n, d.k, m, s),
+    return check_launch(launch_gemm32(d.fmt, static_cast<const uint8_t*>(w), region<int8_t>(wsm, L, "xqt"),
+                                      region<float>(wsm, L, "dxt"), region<float>(wsm, L, "cxt"), y, d.n, d.k, m, s),
                         "gemm32");
   }
   GemvProblem p;

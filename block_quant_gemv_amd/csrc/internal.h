@@ -61,17 +61,33 @@ struct GemvProblem {
   int act_div = 1;
 };
 
-// Q8 quantizer over nblocks 32-element blocks (token-major). With xqt set it
-// also writes the codes as [block][token][32] for at most 32 tokens of
-// kblocks blocks each.
+// Second copy of at most 32 tokens' quantized activations for the batched
+// matrix-core path, block-major so that one block's 32 tokens are contiguous:
+// codes [block][g][t % 16][t / 16][8] (g = element / 8: the 16 bytes of
+// tokens t and t + 16 for elements 8 g .. 8 g + 7 sit together), the block
+// scales dx [block][32] and the products dx * (block code sum) c [block][32].
+// Token slots m..31 are not written.
+struct TiledAct {
+  int8_t* codes = nullptr;
+  float* dx = nullptr;
+  float* c = nullptr;
+  int kblocks = 0;
+};
+__host__ __device__ inline int64_t tiled_code_offset(int64_t b, int t, int e) {
+  return b * 1024 + (((e >> 3) * 16 + (t & 15)) * 2 + (t >> 4)) * 8 + (e & 7);
+}
+
+// Q8 quantizer over nblocks 32-element blocks (token-major). With tiled set
+// it also writes the block-major copy for the matrix-core path (at most 32
+// tokens of tiled->kblocks blocks each).
 hipError_t launch_quant_q8(const float* x, int8_t* xq, float* dx, int32_t* sx,
-                           int64_t nblocks, hipStream_t s, int8_t* xqt = nullptr, int kblocks = 0);
+                           int64_t nblocks, hipStream_t s, const TiledAct* tiled = nullptr);
 
 // Row GEMV over packed blocks for m <= 16 tokens (chunks larger m on the
 // host). dots_epilogue selects the integer-store checking epilogue.
 hipError_t launch_gemv(int fmt, const GemvProblem& p, bool dots_epilogue, hipStream_t s);
 
-// Codes xq [m, k] (m <= 32) copied to the token-tiled layout [block][token][32].
+// Codes xq [m, k] (m <= 32) copied to the block-major layout of TiledAct::codes.
 hipError_t launch_tile_codes(const int8_t* xq, int8_t* xqt, int m, int kblocks, hipStream_t s);
 
 // Single-token Q4_K / Q5_K GEMV that loads the 16-byte-aligned super-block

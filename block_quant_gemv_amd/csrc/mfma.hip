@@ -6,325 +6,351 @@
 // integer block dots run on the matrix cores instead (the prefill/batched
 // case of "01 · Phase overview: from 2B to 8B to MoE", icman.com.cn, section
 // 九: at batch 32 the dp4a path was exhausted and matrix cores were needed).
-// Every MFMA stays inside one scale group -- a 32-element Q4_K sub-block (two
-// K=16 MFMAs) or a 16-element Q6_K sub-block (one) -- because each group has
-// its own scale (and min), applied in fp32 after the integer product.
+// Every MFMA stays inside one scale group -- a 32-element Q4_K sub-block, or
+// a 16-element Q6_K sub-block with the other half of the weight operand
+// zeroed -- because each group has its own scale (and min), applied in fp32
+// after the integer product.
 //
-// v_mfma_i32_32x32x16_i8, D[m][n] += sum_k A[m][k] B[k][n]:
-//   A (32 x 16): lane l holds A[l % 32][8 (l / 32) .. +7]   (m = token)
-//   B (16 x 32): lane l holds B[8 (l / 32) .. +7][l % 32]   (n = weight row)
-//   D (32 x 32): lane l holds D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32], i < 16
+// v_mfma_i32_16x16x32_i8, D[m][n] += sum_k A[m][k] B[k][n], lane l, g = l / 16:
+//   A (16 x 32): A[l % 16][8 g .. 8 g + 7]        (m = token)
+//   B (32 x 16): B[8 g .. 8 g + 7][l % 16]        (n = weight row)
+//   D (16 x 16): D[4 g + i][l % 16], i < 4
 // so each lane owns one weight row (its scale fields are per-lane values)
-// and 16 tokens. The k order inside a group is free as long as A and B use
-// the same one; it is chosen so that each lane's operands are contiguous.
+// and four tokens of each 16-token half. Q4_K's min term, sum_j (dx s)[t][j]
+// m_j[n], is one fp32 FMA per output and sub-block next to the scale step.
 //
-// Memory: the operands of one MFMA come from 32 different rows (and 32
-// tokens), so reading them straight from global memory touches 32 cache
-// lines per load. Instead a workgroup (4 waves) owns a tile of 32 weight rows
-// and walks K in chunks of 4 super-blocks: the chunk -- 32 row segments of 4
-// contiguous super-blocks -- is read with coalesced 16-byte loads into LDS
-// (the next chunk is already in flight in registers while the current one is
-// computed) and each wave decodes one super-block of it from LDS. The
-// activation codes come from a token-tiled copy ([block][token][32], written
-// by the quantizer), where the 32 tokens of one block are 1 KB of contiguous
-// memory. Each wave accumulates its super-blocks; the four waves' sums are
-// added through LDS in wave order. When there are few row tiles, K is also
-// split across workgroups and a second kernel adds the splits in order. No
-// atomics: results are bitwise reproducible.
+// Work: a workgroup owns 16 weight rows for all 32 tokens and splits K over
+// its waves; each wave streams its own super-blocks (16 row segments read
+// with coalesced 16-byte loads, two super-blocks in flight in registers)
+// through a wave-private LDS tile from which each lane reads its row's
+// fields, and keeps its partial sums in registers. The waves' sums are added
+// through LDS in wave order at the end, so results are bitwise reproducible
+// with no atomics and no second launch. 16-row tiles give 768 workgroups for
+// 12288 rows, three per CU on 256 CUs.
 #include "common.cuh"
 #include "internal.h"
 #include "mfma.h"
-
-#ifndef QG_MM_MINWG
-#define QG_MM_MINWG 512   // with fewer than 256 row tiles, K is split to reach this many workgroups
-#endif
 
 namespace qg {
 
 namespace {
 
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 32;                     // token tile
-constexpr int kRows = 32;                   // weight rows per workgroup
-constexpr int kNW = 4;                      // waves per workgroup = super-blocks per chunk
+constexpr int kRows = 16;                   // weight rows per workgroup
 constexpr int kBufDword3 = 0x00020000;      // raw buffer resource, gfx9 family
 constexpr int kNonTemporal = 2;             // weights are read once
 constexpr uint32_t kNowhere = 0xF0000000u;  // offset past every resource: reads zeros
 
 template <int FMT> struct Geo {
-  static constexpr int BB = FMT == kQ4_K ? 144 : 210;    // bytes per super-block
-  static constexpr int SEG = kNW * BB;                   // bytes of one row in a chunk
-  static constexpr int NCH = (SEG + 15 + 15) / 16;       // 16-byte loads per row (any start alignment)
-  static constexpr int PITCH = 16 * (NCH | 1);           // LDS row pitch: an odd number of 16-byte units
-  static constexpr int LPT = (kRows * NCH + kNW * 64 - 1) / (kNW * 64);  // loads per thread
-  static constexpr int TILE = kRows * PITCH;             // LDS bytes of one chunk
+  static constexpr int BB = FMT == kQ4_K ? 144 : 210;        // bytes per super-block
+  static constexpr int NCH = FMT == kQ4_K ? 9 : 15;          // 16-byte chunks per row segment (any alignment)
+  static constexpr int PITCH = 16 * NCH;                     // LDS row pitch: an odd number of 16-byte units
+  static constexpr int LPL = (kRows * NCH + 63) / 64;        // loads per lane per super-block
+  static constexpr int TILE = kRows * PITCH;                 // LDS bytes of one wave's tile
+  static constexpr int NST = FMT == kQ4_K ? 2 : 1;           // staged per-block floats per token (dx, dx * s)
 };
 
 QG_DEV long pack2(uint32_t lo, uint32_t hi) { return (long)(((uint64_t)hi << 32) | lo); }
-
-QG_DEV uint64_t ld64(__amdgpu_buffer_rsrc_t r, int off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  return (uint64_t)v[0] | ((uint64_t)v[1] << 32);
-}
 
 // q - 32 for four 6-bit codes q in 0..63, one per byte, as signed int8:
 // (q | 0x80) - 0x20 never borrows across bytes, and xor 0x80 recentres.
 QG_DEV uint32_t minus32(uint32_t q) { return ((q | 0x80808080u) - 0x20202020u) ^ 0x80808080u; }
 
-template <int FMT, bool DOTS>
-__global__ __launch_bounds__(kNW * 64) void gemm32_kernel(const uint8_t* __restrict__ W,
-                                                          const int8_t* __restrict__ xqt,
-                                                          const float* __restrict__ dx,
-                                                          const int32_t* __restrict__ sx,
-                                                          float* __restrict__ out, int32_t* __restrict__ dots,
-                                                          int64_t n_rows, int64_t k, int m, int sps) {
+// Per-wave shared memory: the super-block tile and the staged per-block
+// activation scales of the wave's K range ([block][token]).
+template <int FMT>
+struct WaveLds {
+  __host__ __device__ static size_t bytes(int spw) {
+    return (size_t)Geo<FMT>::TILE + (size_t)spw * 8 * kMT * 4 * Geo<FMT>::NST;
+  }
+};
+
+template <int FMT, int NW, bool DOTS>
+__global__ __launch_bounds__(NW * 64, (NW >= 16 ? 1 : 3)) void gemm32_kernel(const uint8_t* __restrict__ W,
+                                                         const int8_t* __restrict__ xqt,
+                                                         const float* __restrict__ dxt,
+                                                         const float* __restrict__ cxt,
+                                                         float* __restrict__ y, int32_t* __restrict__ dots,
+                                                         int64_t n_rows, int64_t k, int m, int spw) {
   using G = Geo<FMT>;
   constexpr int BB = G::BB;
   extern __shared__ __align__(16) uint8_t lds[];
-  uint8_t* wt = lds;                                      // one chunk of weights [row][PITCH]
-  float* s_dx = reinterpret_cast<float*>(lds + G::TILE);  // [block][token] of this split
   const int64_t rb = (k / 256) * BB;
   const int nsb = (int)(k / 256);
   const int kblocks = (int)(k / 32);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 5, col = lane & 31;
+  const int g = lane >> 4, col = lane & 15;
   const int64_t row0 = (int64_t)blockIdx.x * kRows;
   const int64_t n = row0 + col;
   const int rows_here = (int)((n_rows - row0) < kRows ? (n_rows - row0) : kRows);
-  const int split = blockIdx.y;
-  const int sb_begin = split * sps;
-  const int sb_end = (sb_begin + sps) < nsb ? (sb_begin + sps) : nsb;
-  const int nkb = (sb_end - sb_begin) * 8;  // 32-element blocks of this split
-  float* s_c = s_dx + nkb * kMT;
+  const int sb_begin = wid * spw;
+  const int sb_end = (sb_begin + spw) < nsb ? (sb_begin + spw) : nsb;
+  const int nmine = sb_end > sb_begin ? sb_end - sb_begin : 0;
+  const size_t wave_bytes = WaveLds<FMT>::bytes(spw);
+  uint8_t* tile = lds + (size_t)wid * wave_bytes;
+  float* s_dx = reinterpret_cast<float*>(tile + G::TILE);   // [local block][token]
+  float* s_c = s_dx + spw * 8 * kMT;                        // Q4_K: dx * s
 
-  if constexpr (!DOTS) {
-    for (int i = threadIdx.x; i < nkb * kMT; i += kNW * 64) {
-      const int b = i >> 5, t = i & 31;
-      const int64_t gb = (int64_t)sb_begin * 8 + b;
-      float d = 0.0f;
-      if (t < m) d = dx[(int64_t)t * kblocks + gb];
-      s_dx[i] = d;
-      if constexpr (FMT == kQ4_K) s_c[i] = t < m ? d * (float)sx[(int64_t)t * kblocks + gb] : 0.0f;
-    }
-  }
-
-  // Weights of the tile (rows past n_rows read zeros; the extent is rounded
-  // up to 16 bytes, the readable padding after a matrix) and the token-tiled
-  // activation codes (codes of tokens past m are never used: their rows of D
-  // are dropped).
+  // Weights of the tile: rows past n_rows read zeros (the extent is rounded
+  // up to 16 bytes, the readable padding after a matrix).
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(W + row0 * rb), 0, (int)((rows_here * rb + 15) & ~(int64_t)15), kBufDword3);
+  // Block-major activation codes (1 KB per block); token slots past m hold
+  // anything (their rows of D are dropped).
   const __amdgpu_buffer_rsrc_t ar =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xqt), 0, kblocks * kMT * 32, kBufDword3);
 
-  // Chunk c covers super-blocks sb_begin + 4c .. +3 of every row of the tile;
-  // row r's bytes sit at wt + r * PITCH + (its start % 16).
-  const int nchunks = (sb_end - sb_begin + kNW - 1) / kNW;
-  u32x4 pre[G::LPT];
-  auto issue = [&](int c) __attribute__((always_inline)) {
-    const bool ok = c < nchunks;
-    const int64_t sb0 = sb_begin + kNW * c;
+  // Chunk c of a super-block's 16 row segments: row c / NCH, 16-byte chunk
+  // c % NCH of the row's aligned span; row r lands at tile + r * PITCH.
+  auto issue = [&](u32x4 (&buf)[G::LPL], int sb) __attribute__((always_inline)) {
+    const bool ok = sb < sb_end;
 #pragma unroll
-    for (int i = 0; i < G::LPT; ++i) {
-      const int p = threadIdx.x + kNW * 64 * i;
-      const int r = p / G::NCH, ch = p - r * G::NCH;
+    for (int i = 0; i < G::LPL; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / G::NCH, ch = c - r * G::NCH;
       uint32_t off = kNowhere;
-      if (ok && r < kRows) off = (uint32_t)(((int64_t)r * rb + sb0 * BB) & ~(int64_t)15) + 16u * ch;
-      pre[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, kNonTemporal);
+      if (ok && r < kRows) off = (uint32_t)(((int64_t)r * rb + (int64_t)sb * BB) & ~(int64_t)15) + 16u * ch;
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, kNonTemporal);
     }
   };
-  // This wave's activation codes for super-block sb, token col: Q4_K
-  // elements 16 g .. 16 g + 15 of each sub-block; Q6_K elements 8 g .. 8 g + 7
-  // (a) and 16 + 8 g .. (b) of each group.
-  auto load_act = [&](int sb, u32x4 (&a)[8]) __attribute__((always_inline)) {
+  auto store = [&](const u32x4 (&buf)[G::LPL]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t o = ((uint32_t)((sb * 8 + j) * kMT + col)) * 32u;
-      if constexpr (FMT == kQ4_K) {
-        a[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, (int)(o + 16u * g), 0, 0);
-      } else {
-        const uint64_t va = ld64(ar, (int)(o + 8u * g));
-        const uint64_t vb = ld64(ar, (int)(o + 16u + 8u * g));
-        a[j] = u32x4{(uint32_t)va, (uint32_t)(va >> 32), (uint32_t)vb, (uint32_t)(vb >> 32)};
+    for (int i = 0; i < G::LPL; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / G::NCH, ch = c - r * G::NCH;
+      if (r < kRows) *reinterpret_cast<u32x4*>(tile + r * G::PITCH + 16 * ch) = buf[i];
+    }
+  };
+  // This lane's activation operands for the 32-element group (global block)
+  // b: tokens col (half 0) and 16 + col (half 1), elements 8 g .. 8 g + 7,
+  // which the block-major layout keeps in one 16-byte piece.
+  auto load_act = [&](int64_t b, long& a0, long& a1) __attribute__((always_inline)) {
+    const uint32_t o = (uint32_t)(b * 1024) + 16u * (uint32_t)lane;
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ar, (int)o, 0, 0);
+    a0 = pack2(v[0], v[1]);
+    a1 = pack2(v[2], v[3]);
+  };
+
+  v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // tokens 4g + i, 16 + 4g + i
+
+  // Weights two super-blocks ahead in registers (double buffer); the
+  // activation operands of a super-block are requested when its step starts,
+  // before the weights two ahead (loads return in order, so waiting for the
+  // activations never waits for those weights), and other waves on the SIMD
+  // cover their L2 latency.
+  u32x4 bufA[G::LPL], bufB[G::LPL];
+  issue(bufA, sb_begin);
+  issue(bufB, sb_begin + 1);
+
+  // The wave's per-block scales (and Q4_K's dx * block sum), contiguous in
+  // the block-major layout: 16-byte loads, all requested before the first
+  // is stored; token slots past m become zero.
+  if constexpr (!DOTS) {
+    const int nvec = nmine * 8 * kMT / 4;  // float4s of the wave's range
+    const float4* gdx = reinterpret_cast<const float4*>(dxt + (int64_t)sb_begin * 8 * kMT);
+    const float4* gc = reinterpret_cast<const float4*>(cxt + (int64_t)sb_begin * 8 * kMT);
+    for (int v0 = 0; v0 < nvec; v0 += 4 * 64) {
+      float4 vd[4], vc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = v0 + lane + 64 * i;
+        if (v < nvec) {
+          vd[i] = gdx[v];
+          if constexpr (FMT == kQ4_K) vc[i] = gc[v];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = v0 + lane + 64 * i;
+        if (v < nvec) {
+          const int t = (4 * v) & (kMT - 1);  // token of the first of the four
+          float4 d = vd[i];
+          d.x = t + 0 < m ? d.x : 0.0f;
+          d.y = t + 1 < m ? d.y : 0.0f;
+          d.z = t + 2 < m ? d.z : 0.0f;
+          d.w = t + 3 < m ? d.w : 0.0f;
+          reinterpret_cast<float4*>(s_dx)[v] = d;
+          if constexpr (FMT == kQ4_K) {
+            float4 c = vc[i];
+            c.x = t + 0 < m ? c.x : 0.0f;
+            c.y = t + 1 < m ? c.y : 0.0f;
+            c.z = t + 2 < m ? c.z : 0.0f;
+            c.w = t + 3 < m ? c.w : 0.0f;
+            reinterpret_cast<float4*>(s_c)[v] = c;
+          }
+        }
       }
     }
-  };
-  auto store = [&]() __attribute__((always_inline)) {
+  }
+  // One super-block: its weights from the registers to the wave's LDS tile,
+  // its activations and the weights two ahead requested, then the products
+  // from the tile.
+  auto step = [&](int sb, u32x4 (&buf)[G::LPL]) __attribute__((always_inline)) {
+    const int bl0 = (sb - sb_begin) * 8;         // wave-local block of the first group
+    __builtin_amdgcn_wave_barrier();  // the previous super-block's tile reads are done
+    store(buf);
+    long act[8][2];
 #pragma unroll
-    for (int i = 0; i < G::LPT; ++i) {
-      const int p = threadIdx.x + kNW * 64 * i;
-      const int r = p / G::NCH, ch = p - r * G::NCH;
-      if (r < kRows) *reinterpret_cast<u32x4*>(wt + r * G::PITCH + 16 * ch) = pre[i];
-    }
-  };
-
-  float acc[16], accs[16], accm[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-
-  // One super-block from the LDS chunk; this lane's row's super-block starts
-  // at LDS byte `base`.
-  auto compute = [&](int sb, uint32_t base, const u32x4 (&a)[8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { accs[i] = 0.0f; accm[i] = 0.0f; }
-    const int bl0 = (sb - sb_begin) * 8;  // split-local block of the first sub-block
-    float d = 0.0f, dmin = 0.0f;
+    for (int j = 0; j < 8; ++j) load_act((int64_t)sb * 8 + j, act[j][0], act[j][1]);
+    issue(buf, sb + 2);
+    __builtin_amdgcn_wave_barrier();  // the tile is written before any lane reads it
+    const uint32_t base = (uint32_t)(col * G::PITCH) + (uint32_t)(((int64_t)col * rb + (int64_t)sb * BB) & 15);
+    v4f accs0 = {0.f, 0.f, 0.f, 0.f}, accs1 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == kQ4_K) {
-      const u32x4 h = *reinterpret_cast<const u32x4*>(wt + base);
-      d = half_bits(h.x & 0xffffu);
-      dmin = half_bits(h.x >> 16);
+      v4f accm0 = {0.f, 0.f, 0.f, 0.f}, accm1 = {0.f, 0.f, 0.f, 0.f};
+      const u32x4 h = *reinterpret_cast<const u32x4*>(tile + base);
+      const float d = half_bits(h.x & 0xffffu);
+      const float dmin = half_bits(h.x >> 16);
       // 6-bit sc_j at bit 6 j, m_j at bit 48 + 6 j of the 96-bit stream.
       const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
       const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
+      const int sh = (g >> 1) * 4;  // lane groups 2, 3 take the high nibbles (elements 16..31)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(wt + base + 16 + 16 * j);
-        const int sh = g ? 4 : 0;
-        const long b0 = pack2((q.x >> sh) & 0x0F0F0F0Fu, (q.y >> sh) & 0x0F0F0F0Fu);
-        const long b1 = pack2((q.z >> sh) & 0x0F0F0F0Fu, (q.w >> sh) & 0x0F0F0F0Fu);
-        v16i D = {0};
-        D = __builtin_amdgcn_mfma_i32_32x32x16_i8(pack2(a[j].x, a[j].y), b0, D, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_i32_32x32x16_i8(pack2(a[j].z, a[j].w), b1, D, 0, 0, 0);
+        const uint2 q = *reinterpret_cast<const uint2*>(tile + base + 16 + 16 * j + 8 * (g & 1));
+        const long b = pack2((q.x >> sh) & 0x0F0F0F0Fu, (q.y >> sh) & 0x0F0F0F0Fu);
+        v4i D0 = {0, 0, 0, 0}, D1 = {0, 0, 0, 0};
+        D0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[j][0], b, D0, 0, 0, 0);
+        D1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[j][1], b, D1, 0, 0, 0);
         if constexpr (DOTS) {
           if (n < n_rows) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int tt = 8 * (i >> 2) + 4 * g + (i & 3);
-              if (tt < m) dots[((int64_t)tt * n_rows + n) * kblocks + (int64_t)sb * 8 + j] = D[i];
+            for (int i = 0; i < 4; ++i) {
+              const int t0 = 4 * g + i, t1 = 16 + 4 * g + i;
+              if (t0 < m) dots[((int64_t)t0 * n_rows + n) * kblocks + (int64_t)sb * 8 + j] = D0[i];
+              if (t1 < m) dots[((int64_t)t1 * n_rows + n) * kblocks + (int64_t)sb * 8 + j] = D1[i];
             }
           }
         } else {
           const int sc = (int)((s_lo >> (6 * j)) & 63u);
-          const float4* dxv = reinterpret_cast<const float4*>(s_dx + (bl0 + j) * kMT);
-#pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const float4 dd = dxv[2 * a4 + g];
-            const float dl[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * a4 + r;
-              accs[i] = fmaf(dl[r], (float)__mul24(D[i], sc), accs[i]);
-            }
-          }
+          const float mj = (float)((s_hi >> (16 + 6 * j)) & 63u);
+          const float4 d0 = *reinterpret_cast<const float4*>(s_dx + (bl0 + j) * kMT + 4 * g);
+          const float4 d1 = *reinterpret_cast<const float4*>(s_dx + (bl0 + j) * kMT + 16 + 4 * g);
+          // min term: sum_j (dx s)[t][j] m_j of the lane's row
+          const float4 c0 = *reinterpret_cast<const float4*>(s_c + (bl0 + j) * kMT + 4 * g);
+          const float4 c1 = *reinterpret_cast<const float4*>(s_c + (bl0 + j) * kMT + 16 + 4 * g);
+          accm0[0] = fmaf(c0.x, mj, accm0[0]);
+          accm0[1] = fmaf(c0.y, mj, accm0[1]);
+          accm0[2] = fmaf(c0.z, mj, accm0[2]);
+          accm0[3] = fmaf(c0.w, mj, accm0[3]);
+          accm1[0] = fmaf(c1.x, mj, accm1[0]);
+          accm1[1] = fmaf(c1.y, mj, accm1[1]);
+          accm1[2] = fmaf(c1.z, mj, accm1[2]);
+          accm1[3] = fmaf(c1.w, mj, accm1[3]);
+          accs0[0] = fmaf(d0.x, (float)__mul24(D0[0], sc), accs0[0]);
+          accs0[1] = fmaf(d0.y, (float)__mul24(D0[1], sc), accs0[1]);
+          accs0[2] = fmaf(d0.z, (float)__mul24(D0[2], sc), accs0[2]);
+          accs0[3] = fmaf(d0.w, (float)__mul24(D0[3], sc), accs0[3]);
+          accs1[0] = fmaf(d1.x, (float)__mul24(D1[0], sc), accs1[0]);
+          accs1[1] = fmaf(d1.y, (float)__mul24(D1[1], sc), accs1[1]);
+          accs1[2] = fmaf(d1.z, (float)__mul24(D1[2], sc), accs1[2]);
+          accs1[3] = fmaf(d1.w, (float)__mul24(D1[3], sc), accs1[3]);
         }
       }
       if constexpr (!DOTS) {
-        // Min term sum_j c[t][j] m_j[n] of the super-block as a 32 x 8 by 8 x 32
-        // fp32 product on the matrix cores (v_mfma_f32_32x32x2_f32, same D
-        // layout): A[t][kk] = c of token col, block 2 s + kk (kk = g); B[kk][n]
-        // = m_{2 s + kk} of this lane's row.
-        v16f M = {0.0f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int jj = 2 * st + g;
-          const float cval = s_c[(bl0 + jj) * kMT + col];
-          const float mval = (float)((s_hi >> (16 + 6 * jj)) & 63u);
-          M = __builtin_amdgcn_mfma_f32_32x32x2f32(cval, mval, M, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          acc0[i] = fmaf(d, accs0[i], fmaf(-dmin, accm0[i], acc0[i]));
+          acc1[i] = fmaf(d, accs1[i], fmaf(-dmin, accm1[i], acc1[i]));
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) accm[i] = M[i];
       }
     } else {
-      d = half_bits(lds_u16(wt, base));
+      const float d = half_bits(lds_u16(tile, base));
 #pragma unroll
       for (int grp = 0; grp < 8; ++grp) {
-        // Element 8g + c of sub-block a: low nibble of ql[16 grp + 8 g + c],
-        // bits 2g..2g+1 of qh[8 grp + c]; sub-block b: high nibble, bits 2(g + 2).
+        // Elements 8 (g & 1) .. + 7 of 16-element sub-block (g >> 1): low
+        // 4 bits in ql[16 grp + 8 (g & 1) + c] (low nibble for sub-block a,
+        // high for b), high 2 bits at bits 2 (g & 1) + 4 (g >> 1) of
+        // qh[8 grp + c].
         uint32_t ql[2], qh[2];
-        lds_read_unaligned<2>(wt, base + 18 + 16 * grp + 8 * g, ql);
-        lds_read_unaligned<2>(wt, base + 146 + 8 * grp, qh);
-        const uint32_t scs = lds_u16(wt, base + 2 + 2 * grp);
-        const int sha = 2 * g, shb = 2 * g + 4;
-        const uint32_t ca0 = minus32((ql[0] & 0x0F0F0F0Fu) | (((qh[0] >> sha) & 0x03030303u) << 4));
-        const uint32_t ca1 = minus32((ql[1] & 0x0F0F0F0Fu) | (((qh[1] >> sha) & 0x03030303u) << 4));
-        const uint32_t cb0 = minus32(((ql[0] >> 4) & 0x0F0F0F0Fu) | (((qh[0] >> shb) & 0x03030303u) << 4));
-        const uint32_t cb1 = minus32(((ql[1] >> 4) & 0x0F0F0F0Fu) | (((qh[1] >> shb) & 0x03030303u) << 4));
-        v16i Da = {0}, Db = {0};
-        Da = __builtin_amdgcn_mfma_i32_32x32x16_i8(pack2(a[grp].x, a[grp].y), pack2(ca0, ca1), Da, 0, 0, 0);
-        Db = __builtin_amdgcn_mfma_i32_32x32x16_i8(pack2(a[grp].z, a[grp].w), pack2(cb0, cb1), Db, 0, 0, 0);
+        lds_read_unaligned<2>(tile, base + 18 + 16 * grp + 8 * (g & 1), ql);
+        lds_read_unaligned<2>(tile, base + 146 + 8 * grp, qh);
+        const uint32_t scs = lds_u16(tile, base + 2 + 2 * grp);
+        const int lsh = 4 * (g >> 1), hsh = 2 * (g & 1) + 4 * (g >> 1);
+        const uint32_t c0 = minus32(((ql[0] >> lsh) & 0x0F0F0F0Fu) | (((qh[0] >> hsh) & 0x03030303u) << 4));
+        const uint32_t c1 = minus32(((ql[1] >> lsh) & 0x0F0F0F0Fu) | (((qh[1] >> hsh) & 0x03030303u) << 4));
+        // Lane group g holds elements 8g..8g+7 of the 32-element group: groups
+        // 0, 1 are sub-block a, groups 2, 3 sub-block b. One product per
+        // sub-block, with the other sub-block's operand lanes zeroed.
+        const long ba = (g < 2) ? pack2(c0, c1) : 0l;
+        const long bb = (g >= 2) ? pack2(c0, c1) : 0l;
+        v4i Pa0 = {0, 0, 0, 0}, Pa1 = {0, 0, 0, 0}, Pb0 = {0, 0, 0, 0}, Pb1 = {0, 0, 0, 0};
+        Pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[grp][0], ba, Pa0, 0, 0, 0);
+        Pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[grp][1], ba, Pa1, 0, 0, 0);
+        Pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[grp][0], bb, Pb0, 0, 0, 0);
+        Pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(act[grp][1], bb, Pb1, 0, 0, 0);
         if constexpr (DOTS) {
           if (n < n_rows) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int tt = 8 * (i >> 2) + 4 * g + (i & 3);
-              if (tt < m) {
-                int32_t* o2 = dots + ((int64_t)tt * n_rows + n) * (k / 16) + (int64_t)sb * 16 + 2 * grp;
-                o2[0] = Da[i];
-                o2[1] = Db[i];
+            for (int i = 0; i < 4; ++i) {
+              const int t0 = 4 * g + i, t1 = 16 + 4 * g + i;
+              const int64_t jo = (int64_t)sb * 16 + 2 * grp;
+              if (t0 < m) {
+                int32_t* o = dots + ((int64_t)t0 * n_rows + n) * (k / 16) + jo;
+                o[0] = Pa0[i];
+                o[1] = Pb0[i];
+              }
+              if (t1 < m) {
+                int32_t* o = dots + ((int64_t)t1 * n_rows + n) * (k / 16) + jo;
+                o[0] = Pa1[i];
+                o[1] = Pb1[i];
               }
             }
           }
         } else {
           const int sca = (int)(int8_t)(scs & 0xffu), scb = (int)(int8_t)(scs >> 8);
-          const float4* dxv = reinterpret_cast<const float4*>(s_dx + (bl0 + grp) * kMT);
+          const float4 d0 = *reinterpret_cast<const float4*>(s_dx + (bl0 + grp) * kMT + 4 * g);
+          const float4 d1 = *reinterpret_cast<const float4*>(s_dx + (bl0 + grp) * kMT + 16 + 4 * g);
+          // |sc P| <= 128 * 16 * 127 * 32 per sub-block: the integer sum is
+          // exact in int32 and in its fp32 conversion (< 2^24).
+          accs0[0] = fmaf(d0.x, (float)(__mul24(Pa0[0], sca) + __mul24(Pb0[0], scb)), accs0[0]);
+          accs0[1] = fmaf(d0.y, (float)(__mul24(Pa0[1], sca) + __mul24(Pb0[1], scb)), accs0[1]);
+          accs0[2] = fmaf(d0.z, (float)(__mul24(Pa0[2], sca) + __mul24(Pb0[2], scb)), accs0[2]);
+          accs0[3] = fmaf(d0.w, (float)(__mul24(Pa0[3], sca) + __mul24(Pb0[3], scb)), accs0[3]);
+          accs1[0] = fmaf(d1.x, (float)(__mul24(Pa1[0], sca) + __mul24(Pb1[0], scb)), accs1[0]);
+          accs1[1] = fmaf(d1.y, (float)(__mul24(Pa1[1], sca) + __mul24(Pb1[1], scb)), accs1[1]);
+          accs1[2] = fmaf(d1.z, (float)(__mul24(Pa1[2], sca) + __mul24(Pb1[2], scb)), accs1[2]);
+          accs1[3] = fmaf(d1.w, (float)(__mul24(Pa1[3], sca) + __mul24(Pb1[3], scb)), accs1[3]);
+        }
+      }
+      if constexpr (!DOTS) {
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const float4 dd = dxv[2 * a4 + g];
-            const float dl[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * a4 + r;
-              accs[i] = fmaf(dl[r], (float)(__mul24(Da[i], sca) + __mul24(Db[i], scb)), accs[i]);
-            }
-          }
+        for (int i = 0; i < 4; ++i) {
+          acc0[i] = fmaf(d, accs0[i], acc0[i]);
+          acc1[i] = fmaf(d, accs1[i], acc1[i]);
         }
       }
     }
-    if constexpr (!DOTS) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = fmaf(d, accs[i], fmaf(-dmin, accm[i], acc[i]));
-    }
-  };
-
-  issue(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();  // the previous chunk is no longer read (and dx is staged)
-    store();
-    __syncthreads();
-    issue(c + 1);
-    const int sb = sb_begin + kNW * c + wid;
-    if (sb < sb_end) {
-      u32x4 a[8];
-      load_act(sb, a);
-      const int64_t sb0 = sb_begin + kNW * c;
-      const uint32_t base = (uint32_t)(col * G::PITCH) + (uint32_t)(((int64_t)col * rb + sb0 * BB) & 15) +
-                            (uint32_t)(wid * BB);
-      compute(sb, base, a);
-    }
+    };
+  for (int sb = sb_begin; sb < sb_end; sb += 2) {
+    step(sb, bufA);
+    if (sb + 1 < sb_end) step(sb + 1, bufB);
   }
 
   if constexpr (!DOTS) {
-    // The waves' sums, added in wave order through LDS (the chunk area is free).
+    // The waves' sums, added in wave order through LDS.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);  // [kNW][16][64]
+    float* red = reinterpret_cast<float*>(lds);  // [NW][8][64]
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[(wid * 16 + i) * 64 + lane] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      red[(wid * 8 + i) * 64 + lane] = acc0[i];
+      red[(wid * 8 + 4 + i) * 64 + lane] = acc1[i];
+    }
     __syncthreads();
-    float* dst = out + (int64_t)split * kMT * n_rows;  // y itself when there is one split
-    for (int o = threadIdx.x; o < 16 * 64; o += kNW * 64) {
+    for (int o = threadIdx.x; o < 8 * 64; o += NW * 64) {
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) s += red[w * 16 * 64 + o];
+      for (int w = 0; w < NW; ++w) s += red[w * 8 * 64 + o];
       const int i = o >> 6, l = o & 63;
-      const int tt = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
-      const int64_t nn = row0 + (l & 31);
-      if (tt < m && nn < n_rows) dst[(int64_t)tt * n_rows + nn] = s;
+      const int tt = (i < 4 ? 0 : 16) + 4 * (l >> 4) + (i & 3);
+      const int64_t nn = row0 + (l & 15);
+      if (tt < m && nn < n_rows) y[(int64_t)tt * n_rows + nn] = s;
     }
   }
-}
-
-// y[t][n] = sum over splits, in split order.
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials,
-                                                           float* __restrict__ y, int64_t n_rows, int m,
-                                                           int splits) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)m * n_rows) return;
-  float s = 0.0f;
-  for (int p = 0; p < splits; ++p) s += partials[(int64_t)p * kMT * n_rows + i];
-  y[i] = s;
 }
 
 bool shape_ok(int fmt, int64_t n, int64_t k, int m) {
@@ -334,76 +360,64 @@ bool shape_ok(int fmt, int64_t n, int64_t k, int m) {
          rb * kRows < (1ll << 30) && (k / 32) * kMT * 32 < (1ll << 30);
 }
 
-// Super-blocks per split: one split when the row tiles alone give every CU a
-// workgroup, else K is shared out in whole chunks.
-void split_plan(int64_t n, int64_t k, int& splits, int& sps) {
+// Waves per workgroup: enough to keep about 12 waves per CU (three per
+// SIMD) when the row tiles alone do not, each wave taking at least two
+// super-blocks.
+int waves_for(int64_t n, int64_t k) {
   const int64_t tiles = (n + kRows - 1) / kRows;
+  const int64_t want = (int64_t)device_cus() * 12;
   const int nsb = (int)(k / 256);
-  // Measured on MI355X: 384 row tiles run best unsplit; 128 tiles (4096
-  // rows) best with K shared out four ways.
-  int want = tiles >= 256 ? 1 : (int)((QG_MM_MINWG + tiles - 1) / tiles);
-  const int maxs = nsb / kNW > 0 ? nsb / kNW : 1;
-  if (want > maxs) want = maxs;
-  sps = (nsb + want - 1) / want;
-  sps = (sps + kNW - 1) / kNW * kNW;
-  splits = (nsb + sps - 1) / sps;
+  int nw = 4;
+  while (nw < 16 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
+  return nw;
+}
+
+template <int FMT, int NW, bool DOTS>
+hipError_t launch_t(const uint8_t* w, const int8_t* xqt, const float* dxt, const float* cxt, float* y,
+                    int32_t* dots, int64_t n, int64_t k, int m, hipStream_t s) {
+  auto kern = gemm32_kernel<FMT, NW, DOTS>;
+  const int nsb = (int)(k / 256);
+  const int spw = (nsb + NW - 1) / NW;
+  size_t lds = (size_t)NW * WaveLds<FMT>::bytes(spw);
+  const size_t red = (size_t)NW * 8 * 64 * sizeof(float);
+  if (lds < red) lds = red;
+  if (lds > (size_t)kLdsBytes) return hipErrorInvalidValue;
+  int per_cu = 0;  // raises the dynamic-LDS limit (once per kernel and device)
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), NW * 64, lds, true, &per_cu);
+  if (qe != hipSuccess) return qe;
+  const unsigned tiles = (unsigned)((n + kRows - 1) / kRows);
+  hipLaunchKernelGGL(kern, dim3(tiles), dim3(NW * 64), lds, s, w, xqt, dxt, cxt, y, dots, n, k, m, spw);
+  return hipGetLastError();
 }
 
 template <int FMT, bool DOTS>
-hipError_t launch_t(const uint8_t* w, const int8_t* xqt, const float* dx, const int32_t* sx, float* out,
-                    int32_t* dots, int64_t n, int64_t k, int m, int splits, int sps, hipStream_t s) {
-  using G = Geo<FMT>;
-  auto kern = gemm32_kernel<FMT, DOTS>;
-  const size_t stage = DOTS ? 0 : (size_t)sps * 8 * kMT * sizeof(float) * (FMT == kQ4_K ? 2 : 1);
-  const size_t red = (size_t)kNW * 16 * 64 * sizeof(float);
-  size_t lds = (size_t)G::TILE + stage;
-  if (lds < red) lds = red;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  int per_cu = 0;  // raises the dynamic-LDS limit (once per kernel and device)
-  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kNW * 64, lds, true, &per_cu);
-  if (qe != hipSuccess) return qe;
-  const unsigned tiles = (unsigned)((n + kRows - 1) / kRows);
-  hipLaunchKernelGGL(kern, dim3(tiles, (unsigned)splits), dim3(kNW * 64), lds, s, w, xqt, dx, sx, out, dots, n,
-                     k, m, sps);
-  return hipGetLastError();
+hipError_t launch_fmt(const uint8_t* w, const int8_t* xqt, const float* dxt, const float* cxt, float* y,
+                      int32_t* dots, int64_t n, int64_t k, int m, hipStream_t s) {
+  switch (waves_for(n, k)) {
+    case 4: return launch_t<FMT, 4, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+    case 8: return launch_t<FMT, 8, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+    default: return launch_t<FMT, 16, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+  }
 }
 
 }  // namespace
 
 bool mfma_supported(int fmt) { return fmt == kQ4_K || fmt == kQ6_K; }
 
-size_t gemm32_partials_bytes(int64_t n, int64_t k) {
-  int splits, sps;
-  split_plan(n, k, splits, sps);
-  return splits > 1 ? (size_t)splits * kMT * n * sizeof(float) : 0;
-}
-
 size_t gemm32_tiled_act_bytes(int64_t k) { return (size_t)(k / 32) * kMT * 32; }
 
-hipError_t launch_gemm32(int fmt, const uint8_t* w, const int8_t* xqt, const float* dx, const int32_t* sx,
-                         float* y, float* partials, int64_t n, int64_t k, int m, hipStream_t s) {
+hipError_t launch_gemm32(int fmt, const uint8_t* w, const int8_t* xqt, const float* dxt, const float* cxt,
+                         float* y, int64_t n, int64_t k, int m, hipStream_t s) {
   if (!shape_ok(fmt, n, k, m)) return hipErrorInvalidValue;
-  int splits, sps;
-  split_plan(n, k, splits, sps);
-  if (splits > 1 && !partials) return hipErrorInvalidValue;
-  float* out = splits > 1 ? partials : y;
-  hipError_t e = fmt == kQ4_K ? launch_t<kQ4_K, false>(w, xqt, dx, sx, out, nullptr, n, k, m, splits, sps, s)
-                              : launch_t<kQ6_K, false>(w, xqt, dx, sx, out, nullptr, n, k, m, splits, sps, s);
-  if (e != hipSuccess || splits == 1) return e;
-  const int64_t total = (int64_t)m * n;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, partials, y, n,
-                     m, splits);
-  return hipGetLastError();
+  return fmt == kQ4_K ? launch_fmt<kQ4_K, false>(w, xqt, dxt, cxt, y, nullptr, n, k, m, s)
+                      : launch_fmt<kQ6_K, false>(w, xqt, dxt, cxt, y, nullptr, n, k, m, s);
 }
 
 hipError_t launch_gemm32_dots(int fmt, const uint8_t* w, const int8_t* xqt, int32_t* dots, int64_t n,
                               int64_t k, int m, hipStream_t s) {
   if (!shape_ok(fmt, n, k, m)) return hipErrorInvalidValue;
-  int splits, sps;
-  split_plan(n, k, splits, sps);
-  return fmt == kQ4_K
-             ? launch_t<kQ4_K, true>(w, xqt, nullptr, nullptr, nullptr, dots, n, k, m, splits, sps, s)
-             : launch_t<kQ6_K, true>(w, xqt, nullptr, nullptr, nullptr, dots, n, k, m, splits, sps, s);
+  return fmt == kQ4_K ? launch_fmt<kQ4_K, true>(w, xqt, nullptr, nullptr, nullptr, dots, n, k, m, s)
+                      : launch_fmt<kQ6_K, true>(w, xqt, nullptr, nullptr, nullptr, dots, n, k, m, s);
 }
 
 }  // namespace qg

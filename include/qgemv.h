@@ -175,9 +175,12 @@ int qgemv_workspace_size(qgemv_t h, int m, size_t *bytes);
  * not have. Names: "xq" (int8 [m, K]), "dx" (fp32 [m, K/32]), "sx" (int32
  * [m, K/32]); FFN adds "gu" (fp32 [m, 2*inter]), "h" (fp32 [m, inter]), "hq",
  * "hd", "hs"; a GEMV workspace for m >= 9 adds "xqt" (the codes again,
- * int8 [k/32][32][32]: block, token, element -- the layout of the batched
- * matrix-core path, written by the quantizer) and, for Q4_K and Q6_K plans
- * whose K is split across workgroups, "partials" (fp32); MoE adds "logits"
+ * int8, 1 KB per 32-element block holding 32 token slots: for element group
+ * g = e / 8 and token t, the 8 codes sit at byte
+ * ((g * 16 + t % 16) * 2 + t / 16) * 8 of the block), "dxt" (fp32
+ * [K/32][32]: the scales again, block-major) and "cxt" (fp32 [K/32][32]: each
+ * scale times its block's code sum), all written by the quantizer for the
+ * batched matrix-core path (token slots m..31 are left as they were); MoE adds "logits"
  * (fp32 [m, n_experts]), "ids" (int32
  * [m, top_k]), "wts" (fp32 [m, top_k]), "gu" (fp32 [m, top_k + 1, 2*inter]),
  * "h", "hq", "hd", "hs" (per token and slot, shared expert last). */
@@ -199,8 +202,8 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t *bytes);
  * `stream`: for k <= 2048 and m <= 16 one GEMV kernel that quantizes x in its
  * prologue; otherwise the activation quantizer, then the format's GEMV
  * kernel. For Q4_K and Q6_K with m >= 9 the block dots run on int8 matrix
- * cores over 32-token tiles (a K-split GEMM plus a fixed-order reduction);
- * results follow the same rounding contract either way. */
+ * cores over 32-token tiles (K split across a workgroup's waves, summed in a
+ * fixed order); results follow the same rounding contract either way. */
 int qgemv_run(qgemv_t h, const void *w, const float *x, float *y, int m,
               void *ws, size_t ws_bytes, void *stream);
 
