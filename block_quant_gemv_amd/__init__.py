@@ -15,7 +15,7 @@ import os
 import torch  # loads torch's HIP runtime first; the library then binds to it
 
 __all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "debug_quantize_s16",
-           "clear_launch_cache", "lib_path", "LAYOUT_VERSION"]
+           "clear_launch_cache", "debug_stream_read", "lib_path", "LAYOUT_VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libqgemv.so")
@@ -74,9 +74,10 @@ _lib.qgemv_debug_quantize_s16.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _vp]
 _lib.qgemv_debug_block_dots_s16.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.qgemv_debug_clear_launch_cache.argtypes = []
 _lib.qgemv_run_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, _vp]
+_lib.qgemv_debug_stream_read.argtypes = [_vp, _sz, _vp, _vp]
 _lib.qattn_workspace_size.argtypes = [_i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]
 _lib.qattn_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _sz, _vp]
-for _f in ("qgemv_run_noalloc", "qgemv_debug_clear_launch_cache", "qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
+for _f in ("qgemv_debug_stream_read", "qgemv_run_noalloc", "qgemv_debug_clear_launch_cache", "qmoe_run_s16", "qgemv_workspace_size_s16", "qgemv_run_s16", "qgemv_run_f32act", "qgemv_debug_quantize_s16", "qgemv_debug_block_dots_s16",
            "qattn_workspace_size", "qattn_decode", "qgemv_create", "qgemv_destroy", "qgemv_workspace_size", "qgemv_workspace_offset",
            "qgemv_weight_bytes", "qgemv_run", "qgemv_quantize", "qgemv_run_quantized", "qffn_run", "qmoe_run", "qgemv_debug_quantize",
            "qgemv_debug_block_dots"):
@@ -395,6 +396,16 @@ def clear_launch_cache():
     """Forget the library's cached launch facts (per-device CU counts and
     kernel residencies): the next launch of each kernel queries them again."""
     _check(_lib.qgemv_debug_clear_launch_cache(), "qgemv_debug_clear_launch_cache")
+
+
+def debug_stream_read(buf: torch.Tensor, out: torch.Tensor, stream=None):
+    """Read buf (a contiguous GPU tensor, 16-byte multiple) once with the
+    GEMVs' load shape (qgemv_debug_stream_read); out: one int32 on the GPU."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _check(_lib.qgemv_debug_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                        _dev(out, torch.int32, "out"), _stream(stream)),
+           "qgemv_debug_stream_read")
 
 
 class Attention:

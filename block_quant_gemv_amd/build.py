@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["api.cpp", "launch_cache.cpp", "quant.hip", "gemv.hip", "kdirect.hip", "swiglu.hip", "moe.hip", "mfma.hip", "attn.hip", "s16.hip", "fact.hip", "noalloc.hip", "moe_fused.hip"]
+SOURCES = ["api.cpp", "launch_cache.cpp", "quant.hip", "gemv.hip", "kdirect.hip", "swiglu.hip", "moe.hip", "mfma.hip", "attn.hip", "s16.hip", "fact.hip", "noalloc.hip", "moe_fused.hip", "stream.hip"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

@@ -741,4 +741,11 @@ int qgemv_debug_clear_launch_cache(void) {
   return QGEMV_OK;
 }
 
+int qgemv_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out) return fail(QGEMV_EINVAL, "qgemv_debug_stream_read: null pointer");
+  if (!aligned(buf, 16) || !aligned(out, 4) || bytes % 16)
+    return fail(QGEMV_EALIGN, "qgemv_debug_stream_read: buf and bytes need 16-byte alignment");
+  return check_launch(launch_stream_read(buf, bytes, out, static_cast<hipStream_t>(stream)), "stream read");
+}
+
 }  // extern "C"

@@ -111,6 +111,10 @@ hipError_t kernel_residency(const void* kern, int threads, size_t lds, bool rais
 // Forgets every cached fact (the next launch of each kernel queries again).
 void clear_launch_cache();
 
+// Streaming-read measurement (stream.hip): reads bytes (a multiple of 16,
+// buf 16-byte aligned) once with 16-byte non-temporal loads over every CU.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
+
 // Bytes of the fixed device scratch behind the allocation-free GEMV entry
 // point (noalloc.hip), and the address of the current device's copy of it
 // (looked up once per device with that device current).

@@ -343,6 +343,18 @@ int qgemv_debug_block_dots_s16(qgemv_t h, const void *w, const int16_t *xq, int3
  * threads at once). Never needed for correctness. */
 int qgemv_debug_clear_launch_cache(void);
 
+/* Streaming-read measurement: reads `bytes` bytes of device memory at `buf`
+ * once, with the load shape of the GEMV kernels (16-byte non-temporal
+ * vector loads, several in flight per lane, workgroups on every compute
+ * unit), and computes nothing from them. Timing it at a matrix's size gives
+ * the read rate a GEMV of that matrix could reach at best (the pages drill
+ * down to such a single-kernel access-pattern test: "01 · Phase overview:
+ * from 2B to 8B to MoE", icman.com.cn, issue ledger). buf and bytes need
+ * 16-byte alignment; `out` is one device uint32 that is written only if the
+ * data xor-reduce to one fixed constant (so that the loads cannot be
+ * dropped); its value means nothing. Asynchronous on `stream`. */
+int qgemv_debug_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
