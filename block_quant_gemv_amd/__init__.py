@@ -18,7 +18,9 @@ __all__ = ["FORMATS", "GEMV", "FFN", "MoE", "Attention", "debug_quantize", "debu
            "clear_launch_cache", "debug_stream_read", "lib_path", "LAYOUT_VERSION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB = os.path.join(_HERE, "libqgemv.so")
+# QGEMV_LIBRARY: path of another build of the same library (the host-sanitized
+# one of the ABI tests); the in-tree build otherwise.
+_LIB = os.environ.get("QGEMV_LIBRARY") or os.path.join(_HERE, "libqgemv.so")
 LAYOUT_VERSION = 1
 
 FORMATS = {"f32": 0, "q4_0": 1, "q8_0": 2, "q4_k": 3, "q6_k": 4, "iq4_nl": 5, "q5_k": 6, "iq4_xs": 7}
