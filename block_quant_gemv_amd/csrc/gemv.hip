@@ -70,11 +70,14 @@ template <bool FUSEQ> constexpr int waves_per_wg() { return FUSEQ ? QG_FUSED_WAV
 // Packed bytes per step (max), per format. Measured on MI355X: smaller steps
 // give each wave more steps (a shorter pipeline tail after its last load)
 // and leave LDS for more resident waves; below ~2.5 KB the per-step overhead
-// wins. Q8_0 rows (4352 B at K=4096) are then split into K-segments.
+// wins. Q8_0 rows (4352 B at K=4096) are then split into K-segments. IQ4_NL
+// is bound by its codebook arithmetic, not by the loads: four 2304-byte rows
+// per step spread the per-step row sums over more blocks (lm_head 4096 ->
+// 248320: 119.0 -> 116.9 us sustained).
 constexpr int tile_cap(int fmt) {
   return QG_TILE_CAP > 0 ? QG_TILE_CAP
          : fmt == kQ8_0 ? 2560 : fmt == kQ4_K ? 5120 : fmt == kQ5_K ? 5632
-         : (fmt == kIQ4_NL || fmt == kIQ4_XS) ? 4608 : 3584;
+         : fmt == kIQ4_NL ? 9216 : fmt == kIQ4_XS ? 4608 : 3584;
 }
 // 16-byte chunks a step can span (alignment adds up to two), per lane.
 template <int FMT> constexpr int loads_per_lane() { return (tile_cap(FMT) + 32 + 1023) / 1024; }
