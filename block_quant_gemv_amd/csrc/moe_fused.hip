@@ -45,7 +45,7 @@ namespace {
 
 constexpr int kUpWaves = 16;        // waves per moe_up_kernel workgroup
 constexpr int kUpRows = 4;          // rows per wave per item (16 waves x 4 = 64 = 32 gate + 32 up)
-constexpr int kUpTok = 4;         // tokens per accumulation pass
+constexpr int kUpTok = 2;         // tokens per accumulation pass
 constexpr int kUpLPL = 9;           // 16-byte loads per lane: a wave's four rows, at most 9216 B
 constexpr int kDnLPL = 5;           // 16-byte loads per lane in moe_down_kernel
 constexpr int kMaxTok = 16;         // tokens a launch can hold
@@ -261,33 +261,55 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
 #pragma unroll
   for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
 
+  // The byte range of this wave's four rows of an item: virtual rows
+  // 4 wid .. 4 wid + 3 (0..31 gate, 32..63 up), contiguous in the matrix.
+  const int v0 = kUpRows * wid;
+  auto item_range = [&](int item, const uint8_t*& W, int64_t& b0) __attribute__((always_inline)) {
+    const int en = item / tiles, j = item - en * tiles;
+    const int e = R.ent_expert[en];
+    W = e < 0 ? a.gu_shared : a.gu + (int64_t)e * a.gu_stride;
+    const int64_t row0 = v0 < 32 ? (int64_t)32 * j + v0 : a.inter + (int64_t)32 * j + (v0 - 32);
+    b0 = row0 * a.rb_gu;
+  };
+  // Loads of an item's rows (items past the end read zeros from an empty
+  // range, with no memory access): issued one item ahead, so an item's
+  // weights are in flight while the previous item is decoded.
+  auto issue = [&](u32x4 (&buf)[LPL], int item) __attribute__((always_inline)) {
+    const uint8_t* W = a.gu_shared;
+    int64_t b0 = 0;
+    int nch = 0;
+    if (item < n_items) {
+      item_range(item, W, b0);
+      nch = (int)(((b0 + kUpRows * a.rb_gu + 15) & ~(int64_t)15) - (b0 & ~(int64_t)15)) >> 4;
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W + (b0 & ~(int64_t)15)), 0, nch * 16, kBufDword3);
+#pragma unroll
+    for (int i = 0; i < LPL; ++i)
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, kNonTemporal);
+  };
+  u32x4 buf[LPL];
+  issue(buf, blockIdx.x);
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int en = item / tiles, j = item - en * tiles;
     const int e = R.ent_expert[en];
     const uint32_t mask = R.ent_mask[en];
     const int c = __popc(mask);
-    const uint8_t* W = e < 0 ? a.gu_shared : a.gu + (int64_t)e * a.gu_stride;
-    // This wave's four rows: virtual rows 4 wid .. 4 wid + 3 of the item
-    // (0..31 gate, 32..63 up), contiguous in the matrix.
-    const int v0 = kUpRows * wid;
-    const int64_t row0 = v0 < 32 ? (int64_t)32 * j + v0 : a.inter + (int64_t)32 * j + (v0 - 32);
-    const int64_t b0 = row0 * a.rb_gu;
+    const uint8_t* W;
+    int64_t b0;
+    item_range(item, W, b0);
     const int64_t a0 = b0 & ~(int64_t)15;
     const int nch = (int)(((b0 + kUpRows * a.rb_gu + 15) & ~(int64_t)15) - a0) >> 4;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + a0), 0, nch * 16, kBufDword3);
-    u32x4 buf[LPL];
-#pragma unroll
-    for (int i = 0; i < LPL; ++i)
-      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, kNonTemporal);
 
-    // Weights to the wave's LDS tile, then decode: lane l takes units
-    // l + 64 jj of each row.
+    // Weights to the wave's LDS tile, the next item's requested, then
+    // decode: lane l takes units l + 64 jj of each row.
 #pragma unroll
     for (int i = 0; i < LPL; ++i) {
       const int ch = lane + 64 * i;
       if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
     }
+    issue(buf, item + gridDim.x);
     const uint32_t base = (uint32_t)(b0 - a0);
     // Tokens in chunks of kUpTok (accumulators stay in registers); the
     // weights are decoded from LDS again for each chunk.
@@ -389,22 +411,45 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
 #pragma unroll
   for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // The byte range of this wave's slot's rows of an item.
+  auto item_range = [&](int item, const uint8_t*& W, int64_t& b0, int& nrows) __attribute__((always_inline)) {
     const int t = item / nblk, blk = item - t * nblk;
     const int64_t r0 = (int64_t)blk * RB;
-    const int nrows = (int)((a.hidden - r0) < RB ? (a.hidden - r0) : RB);
+    nrows = (int)((a.hidden - r0) < RB ? (a.hidden - r0) : RB);
     const int e = s < a.top_k ? a.ids_out[t * a.top_k + s] : -1;
-    const uint8_t* W = e < 0 ? a.dn_shared : a.dn + (int64_t)e * a.dn_stride;
-    const int64_t b0 = r0 * a.rb_dn;
-    const int64_t a0 = b0 & ~(int64_t)15;
-    const int nch = (int)(((b0 + nrows * a.rb_dn + 15) & ~(int64_t)15) - a0) >> 4;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + a0), 0, nch * 16, kBufDword3);
-    u32x4 buf[kDnLPL];
+    W = e < 0 ? a.dn_shared : a.dn + (int64_t)e * a.dn_stride;
+    b0 = r0 * a.rb_dn;
+  };
+  // Loads of an item's rows, issued one item ahead (items past the end read
+  // zeros from an empty range, with no memory access).
+  auto issue = [&](u32x4 (&buf)[kDnLPL], int item) __attribute__((always_inline)) {
+    const uint8_t* W = a.dn_shared;
+    int64_t b0 = 0;
+    int nrows = 0, nch = 0;
+    if (item < n_items) {
+      item_range(item, W, b0, nrows);
+      nch = (int)(((b0 + nrows * a.rb_dn + 15) & ~(int64_t)15) - (b0 & ~(int64_t)15)) >> 4;
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W + (b0 & ~(int64_t)15)), 0, nch * 16, kBufDword3);
 #pragma unroll
     for (int i = 0; i < kDnLPL; ++i)
       buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, kNonTemporal);
-    // The slot's re-quantized h: this lane's units lam + LPR jj.
+  };
+  u32x4 buf[kDnLPL];
+  issue(buf, blockIdx.x);
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int t = item / nblk, blk = item - t * nblk;
+    const int64_t r0 = (int64_t)blk * RB;
+    const uint8_t* W;
+    int64_t b0;
+    int nrows;
+    item_range(item, W, b0, nrows);
+    const int64_t a0 = b0 & ~(int64_t)15;
+    const int nch = (int)(((b0 + nrows * a.rb_dn + 15) & ~(int64_t)15) - a0) >> 4;
+    // The slot's re-quantized h (requested before the next item's weights,
+    // so waiting for it never waits for them): this lane's units lam + LPR jj.
     const int64_t hrow = (int64_t)t * S1 + s;
     Act x[JU];
 #pragma unroll
@@ -415,14 +460,18 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
       x[jj].x[0] = lo.x; x[jj].x[1] = lo.y; x[jj].x[2] = lo.z; x[jj].x[3] = lo.w;
       x[jj].x[4] = hi.x; x[jj].x[5] = hi.y; x[jj].x[6] = hi.z; x[jj].x[7] = hi.w;
       x[jj].dx = a.hd[hrow * U + u];
-      const int ones = 0x01010101;
-      x[jj].sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
-      x[jj].sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
     }
 #pragma unroll
     for (int i = 0; i < kDnLPL; ++i) {
       const int ch = lane + 64 * i;
       if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
+    }
+    issue(buf, item + gridDim.x);
+#pragma unroll
+    for (int jj = 0; jj < JU; ++jj) {
+      const int ones = 0x01010101;
+      x[jj].sa = dot4(x[jj].x[0], ones, dot4(x[jj].x[1], ones, dot4(x[jj].x[2], ones, dot4(x[jj].x[3], ones, 0))));
+      x[jj].sb = dot4(x[jj].x[4], ones, dot4(x[jj].x[5], ones, dot4(x[jj].x[6], ones, dot4(x[jj].x[7], ones, 0))));
     }
     const uint32_t base = (uint32_t)(b0 - a0);
     for (int p = 0; p * RPP < nrows; ++p) {
