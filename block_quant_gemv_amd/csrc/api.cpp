@@ -276,6 +276,20 @@ namespace {
 #endif
 constexpr int64_t kFusedQuantMaxK = QG_FUSED_MAXK;
 
+// Whether the GEMV kernel quantizes x itself (one launch) rather than after
+// a separate quantizer launch. Every workgroup of a fused launch quantizes
+// all of x, which pays for the saved launch only for one token. Measured on
+// MI355X (qgemv_run, weights from HBM): one token, K = 2048: 1.0-1.2 us
+// faster for Q4_0, Q8_0 and Q4_K; K = 4096: 1.0 us faster for Q8_0 at 4096
+// rows, even for Q8_0 / Q4_K / Q4_0 / Q6_K at 12288 rows, but 0.5-0.8 us
+// slower for Q5_K, IQ4_XS and IQ4_NL (their decode is heavier, and the fused
+// instances run fewer, larger workgroups); four or sixteen tokens: 1-15 us
+// slower for every format.
+bool fuse_quantizer(int fmt, int64_t k, int m) {
+  if (m != 1 || k > kFusedQuantMaxK) return false;
+  return k <= 2048 || fmt == kQ4_0 || fmt == kQ8_0 || fmt == kQ4_K || fmt == kQ6_K;
+}
+
 int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const char* fn) {
   if (!h || h->d.kind != QKIND_GEMV) return fail(QGEMV_EINVAL, "%s: not a GEMV plan", fn);
   if (!ws) return fail(QGEMV_EINVAL, "%s: null workspace", fn);
@@ -344,15 +358,13 @@ namespace {
 int gemv_run(qgemv_t h, const void* w, const float* x, float* y, int m, void* ws, hipStream_t s) {
   int rc;
   const qgemv_desc& d = h->d;
-  if (m > kGemvMaxTokens || d.k > kFusedQuantMaxK || (m >= kMfmaMinTokens && mfma_supported(d.fmt))) {
+  if (m > kGemvMaxTokens || !fuse_quantizer(d.fmt, d.k, m) || (m >= kMfmaMinTokens && mfma_supported(d.fmt))) {
     if ((rc = gemv_quantize(h, x, m, ws, s))) return rc;
     return gemv_from_quantized(h, w, y, m, ws, s);
   }
-  // Short rows: one launch, the GEMV kernel quantizes x in its prologue
-  // (same arithmetic as the standalone quantizer) and its first workgroup
-  // stores the codes in the workspace regions "xq", "dx", "sx". For longer
-  // rows every resident workgroup re-quantizing all of x costs more than the
-  // separate quantizer launch, so those take two launches.
+  // One token, short rows: one launch, the GEMV kernel quantizes x in its
+  // prologue (same arithmetic as the standalone quantizer) and its first
+  // workgroup stores the codes in the workspace regions "xq", "dx", "sx".
   const Layout L = layout_of(h, m);
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w);
@@ -447,14 +459,14 @@ int qffn_run(qgemv_t h, const void* w_gateup, const void* w_down, const float* x
   int rc;
   GemvProblem p;
   p.w = static_cast<const uint8_t*>(w_gateup);
-  if (d.hidden <= kFusedQuantMaxK) {
+  if (fuse_quantizer(d.fmt_gateup, d.hidden, m)) {
     p.xf = x;  // quantized in the gate|up kernel's prologue, codes stored in ws
     p.xq_out = xq;
     p.dx_out = dx;
     p.sx_out = sx;
   } else {
-    // Long rows: one quantizer launch is cheaper than every workgroup of the
-    // gate|up GEMV quantizing x again.
+    // Several tokens or long rows: one quantizer launch is cheaper than
+    // every workgroup of the gate|up GEMV quantizing x again.
     if ((rc = check_launch(launch_quant_q8(x, xq, dx, sx, (int64_t)m * d.hidden / 32, s), "quantize"))) return rc;
     p.xq = xq;
     p.dx = dx;

@@ -199,9 +199,9 @@ int qgemv_weight_bytes(qgemv_t h, int which, size_t *bytes);
  * its Q&A on computing GGUF blocks without FP16 expansion).
  * x: fp32 [m, k], 16-byte aligned. y: fp32 [m, n]. ws: workspace of at
  * least qgemv_workspace_size(h, m) bytes, 256-byte aligned. Launches on
- * `stream`: for k <= 2048 and m <= 16 one GEMV kernel that quantizes x in its
- * prologue; otherwise the activation quantizer, then the format's GEMV
- * kernel. For Q4_K and Q6_K with m >= 9 the block dots run on int8 matrix
+ * `stream`: for one token with k <= 2048 (k <= 4096 for Q4_0, Q8_0, Q4_K
+ * and Q6_K) one GEMV kernel that quantizes x in its prologue; otherwise the
+ * activation quantizer, then the format's GEMV kernel. For Q4_K and Q6_K with m >= 9 the block dots run on int8 matrix
  * cores over 32-token tiles (K split across a workgroup's waves, summed in a
  * fixed order); results follow the same rounding contract either way. */
 int qgemv_run(qgemv_t h, const void *w, const float *x, float *y, int m,
