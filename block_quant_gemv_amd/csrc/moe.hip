@@ -45,35 +45,41 @@ constexpr int kRouterMaxTok = 16;
 // quantize x to Q8 blocks for the expert GEMVs (block b by workgroup b mod
 // grid, eight lanes per block as in the activation quantizer), so no
 // separate quantizer launch is needed.
+// MT: token slots (m <= MT). A thread requests a chunk's weights and the
+// chunk of every token before it multiplies any of them, so a chunk costs one
+// memory round trip whatever m is (token slots past m re-read the last
+// token's chunk and are never stored); two chunks are in flight together.
+template <int MT>
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ wr,
                                                      const float* __restrict__ x,
                                                      float* __restrict__ logits, int8_t* __restrict__ xq,
                                                      float* __restrict__ dx, int32_t* __restrict__ sx,
                                                      int n_experts, int64_t hidden, int m) {
-  __shared__ float part[4][kRouterMaxTok];
+  __shared__ float part[4][MT];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t e = blockIdx.x;
   const float4* wrow = reinterpret_cast<const float4*>(wr + e * hidden);
   const int64_t nch = hidden / 4;
-  float acc[kRouterMaxTok];
+  float acc[MT];
 #pragma unroll
-  for (int t = 0; t < kRouterMaxTok; ++t) acc[t] = 0.0f;
+  for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+#pragma unroll 2
   for (int64_t c = threadIdx.x; c < nch; c += blockDim.x) {
     const float4 w = wrow[c];
+    float4 v[MT];
 #pragma unroll
-    for (int t = 0; t < kRouterMaxTok; ++t) {
-      if (t < m) {
-        const float4 v = reinterpret_cast<const float4*>(x + (int64_t)t * hidden)[c];
-        acc[t] = fmaf(w.x, v.x, fmaf(w.y, v.y, fmaf(w.z, v.z, fmaf(w.w, v.w, acc[t]))));
-      }
+    for (int t = 0; t < MT; ++t) {
+      const int tt = t < m ? t : m - 1;
+      v[t] = reinterpret_cast<const float4*>(x + (int64_t)tt * hidden)[c];
     }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      acc[t] = fmaf(w.x, v[t].x, fmaf(w.y, v[t].y, fmaf(w.z, v[t].z, fmaf(w.w, v[t].w, acc[t]))));
   }
 #pragma unroll
-  for (int t = 0; t < kRouterMaxTok; ++t) {
-    if (t < m) {
-      const float s = group_sum(acc[t], 64);
-      if (lane == 0) part[wid][t] = s;
-    }
+  for (int t = 0; t < MT; ++t) {
+    const float s = group_sum(acc[t], 64);
+    if (lane == 0) part[wid][t] = s;
   }
   // Q8 blocks of x: 32 blocks per workgroup pass, eight lanes each.
   const int64_t nblocks = (int64_t)m * (hidden / 32);
@@ -261,7 +267,9 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (c.m < 1 || c.m > kRouterMaxTok || c.top_k > 16) return hipErrorInvalidValue;
   if (c.n_experts < 1 || c.n_experts > 4096 || c.hidden % 32) return hipErrorInvalidValue;
   // 1. router logits, and x quantized to Q8 blocks
-  hipLaunchKernelGGL(router_kernel, dim3((unsigned)c.n_experts), dim3(256), 0, s, c.router, c.x, c.logits,
+  auto router = c.m <= 1 ? router_kernel<1> : c.m <= 2 ? router_kernel<2> : c.m <= 4 ? router_kernel<4>
+               : c.m <= 8 ? router_kernel<8> : router_kernel<16>;
+  hipLaunchKernelGGL(router, dim3((unsigned)c.n_experts), dim3(256), 0, s, c.router, c.x, c.logits,
                      c.xq, c.dx, c.sx, c.n_experts, c.hidden, c.m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
