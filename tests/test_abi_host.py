@@ -270,3 +270,14 @@ def test_f32act_validation_before_launch():
     assert lib.qgemv_run_f32act(hk, a, a, a, 1, None) == EFORMAT
     lib.qgemv_destroy(hk)
 
+
+
+def test_stream_read_validation_before_launch():
+    A = 0x10000  # aligned fake addresses: validation never dereferences them
+    f = lib.qgemv_debug_stream_read
+    assert f(None, 1024, A, None) == EINVAL
+    assert f(A, 1024, None, None) == EINVAL
+    assert f(A + 8, 1024, A, None) == EALIGN       # buffer not 16-byte aligned
+    assert f(A, 1000, A, None) == EALIGN           # size not a multiple of 16
+    assert f(A, 1024, A + 2, None) == EALIGN       # out not 4-byte aligned
+    assert b"stream_read" in lib.qgemv_last_error()
