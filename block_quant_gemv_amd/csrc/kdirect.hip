@@ -172,11 +172,27 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
   };
 
   // One row group in flight per wave; other resident waves cover the wait.
-  // The first group is requested before the activations are prepared, so
-  // both round trips overlap.
+  // With the quantizer fused and groups of several rows, this thread's fp32 x
+  // is requested first and the first row group right after it: loads return
+  // in issue order, so x is quantized while the weights are still in flight
+  // (measured: 12288 rows 9.8 -> 8.9 us, 24576 rows 13.6 -> 12.6 us). With one
+  // row per group (fewer than 8192 rows) the row goes first (4096 rows: 4.9
+  // against 5.3 us the other way round).
+  constexpr bool kXFirst = FUSEQ && R > 1;
+  constexpr int kXPre = (64 * JU * 8 + NW * 64 - 1) / (NW * 64);  // x tasks per thread
+  float4 xpre[FUSEQ ? kXPre : 1];
+  auto load_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < kXPre; ++r) {
+      const int i = threadIdx.x + r * NW * 64;
+      xpre[r] = i < 64 * JU * 8 ? reinterpret_cast<const float4*>(A.xf)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if constexpr (kXFirst) load_x();
   u32x4 hA[R][JU], qA[R][JU];
   uint32_t xA[R][JU];
   load(hA, qA, xA, gw);
+  if constexpr (FUSEQ && !kXFirst) load_x();
 
   if constexpr (FUSEQ) {
     // Quantize x once per workgroup into LDS: eight lanes per 32-element
@@ -188,8 +204,11 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
     float* s_dx = reinterpret_cast<float*>(smem + U * 32);             // [U]
     int* s_sum = reinterpret_cast<int*>(smem + U * 36);                // [U]
     const bool wb = A.xq_out && blockIdx.x == 0;
-    for (int i = threadIdx.x; i < U * 8; i += NW * 64) {  // whole 8-lane groups in or out
-      const float4 v = reinterpret_cast<const float4*>(A.xf)[i];
+#pragma unroll
+    for (int r = 0; r < kXPre; ++r) {
+      const int i = threadIdx.x + r * NW * 64;
+      if (i >= U * 8) break;  // whole 8-lane groups in or out
+      const float4 v = xpre[r];
       const int u = i >> 3, part = i & 7;
       const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
       const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
