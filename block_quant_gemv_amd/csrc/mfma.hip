@@ -137,6 +137,50 @@ __global__ __launch_bounds__(NW * 64, (NW >= 16 ? 1 : 3)) void gemm32_kernel(con
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // tokens 4g + i, 16 + 4g + i
 
+  // The wave's per-block scales (and Q4_K's dx * block sum), contiguous in
+  // the block-major layout, in batches of four 16-byte loads per lane; token
+  // slots past m become zero. The first batch (the whole range when a wave
+  // has at most four super-blocks) is requested before the weights: loads
+  // return in issue order, so storing it waits for no weights.
+  const int nvec = DOTS ? 0 : nmine * 8 * kMT / 4;  // float4s of the wave's range
+  const float4* gdx = reinterpret_cast<const float4*>(dxt + (int64_t)sb_begin * 8 * kMT);
+  const float4* gc = reinterpret_cast<const float4*>(cxt + (int64_t)sb_begin * 8 * kMT);
+  float4 vd[4], vc[4];
+  auto load_scales = [&](int v0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = v0 + lane + 64 * i;
+      if (v < nvec) {
+        vd[i] = gdx[v];
+        if constexpr (FMT == kQ4_K) vc[i] = gc[v];
+      }
+    }
+  };
+  auto store_scales = [&](int v0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = v0 + lane + 64 * i;
+      if (v < nvec) {
+        const int t = (4 * v) & (kMT - 1);  // token of the first of the four
+        float4 d = vd[i];
+        d.x = t + 0 < m ? d.x : 0.0f;
+        d.y = t + 1 < m ? d.y : 0.0f;
+        d.z = t + 2 < m ? d.z : 0.0f;
+        d.w = t + 3 < m ? d.w : 0.0f;
+        reinterpret_cast<float4*>(s_dx)[v] = d;
+        if constexpr (FMT == kQ4_K) {
+          float4 c = vc[i];
+          c.x = t + 0 < m ? c.x : 0.0f;
+          c.y = t + 1 < m ? c.y : 0.0f;
+          c.z = t + 2 < m ? c.z : 0.0f;
+          c.w = t + 3 < m ? c.w : 0.0f;
+          reinterpret_cast<float4*>(s_c)[v] = c;
+        }
+      }
+    }
+  };
+  if constexpr (!DOTS) load_scales(0);
+
   // Weights two super-blocks ahead in registers (double buffer); the
   // activation operands of a super-block are requested when its step starts,
   // before the weights two ahead (loads return in order, so waiting for the
@@ -146,44 +190,11 @@ __global__ __launch_bounds__(NW * 64, (NW >= 16 ? 1 : 3)) void gemm32_kernel(con
   issue(bufA, sb_begin);
   issue(bufB, sb_begin + 1);
 
-  // The wave's per-block scales (and Q4_K's dx * block sum), contiguous in
-  // the block-major layout: 16-byte loads, all requested before the first
-  // is stored; token slots past m become zero.
   if constexpr (!DOTS) {
-    const int nvec = nmine * 8 * kMT / 4;  // float4s of the wave's range
-    const float4* gdx = reinterpret_cast<const float4*>(dxt + (int64_t)sb_begin * 8 * kMT);
-    const float4* gc = reinterpret_cast<const float4*>(cxt + (int64_t)sb_begin * 8 * kMT);
-    for (int v0 = 0; v0 < nvec; v0 += 4 * 64) {
-      float4 vd[4], vc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + lane + 64 * i;
-        if (v < nvec) {
-          vd[i] = gdx[v];
-          if constexpr (FMT == kQ4_K) vc[i] = gc[v];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = v0 + lane + 64 * i;
-        if (v < nvec) {
-          const int t = (4 * v) & (kMT - 1);  // token of the first of the four
-          float4 d = vd[i];
-          d.x = t + 0 < m ? d.x : 0.0f;
-          d.y = t + 1 < m ? d.y : 0.0f;
-          d.z = t + 2 < m ? d.z : 0.0f;
-          d.w = t + 3 < m ? d.w : 0.0f;
-          reinterpret_cast<float4*>(s_dx)[v] = d;
-          if constexpr (FMT == kQ4_K) {
-            float4 c = vc[i];
-            c.x = t + 0 < m ? c.x : 0.0f;
-            c.y = t + 1 < m ? c.y : 0.0f;
-            c.z = t + 2 < m ? c.z : 0.0f;
-            c.w = t + 3 < m ? c.w : 0.0f;
-            reinterpret_cast<float4*>(s_c)[v] = c;
-          }
-        }
-      }
+    store_scales(0);
+    for (int v0 = 4 * 64; v0 < nvec; v0 += 4 * 64) {
+      load_scales(v0);
+      store_scales(v0);
     }
   }
   // One super-block: its weights from the registers to the wave's LDS tile,
