@@ -69,7 +69,7 @@ struct WaveLds {
 };
 
 template <int FMT, int NW, bool DOTS>
-__global__ __launch_bounds__(NW * 64, (NW >= 16 ? 1 : 3)) void gemm32_kernel(const uint8_t* __restrict__ W,
+__global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ xqt,
                                                          const float* __restrict__ dxt,
                                                          const float* __restrict__ cxt,
@@ -373,13 +373,14 @@ bool shape_ok(int fmt, int64_t n, int64_t k, int m) {
 
 // Waves per workgroup: enough to keep about 12 waves per CU (three per
 // SIMD) when the row tiles alone do not, each wave taking at least two
-// super-blocks.
+// super-blocks; at most 8 (16-wave workgroups leave 128 registers per lane,
+// which spills: Q6_K 4096 x 12288 at 32 tokens 27.6 us with 16, 25.9 with 8).
 int waves_for(int64_t n, int64_t k) {
   const int64_t tiles = (n + kRows - 1) / kRows;
   const int64_t want = (int64_t)device_cus() * 12;
   const int nsb = (int)(k / 256);
   int nw = 4;
-  while (nw < 16 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
+  while (nw < 8 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
   return nw;
 }
 
@@ -404,11 +405,8 @@ hipError_t launch_t(const uint8_t* w, const int8_t* xqt, const float* dxt, const
 template <int FMT, bool DOTS>
 hipError_t launch_fmt(const uint8_t* w, const int8_t* xqt, const float* dxt, const float* cxt, float* y,
                       int32_t* dots, int64_t n, int64_t k, int m, hipStream_t s) {
-  switch (waves_for(n, k)) {
-    case 4: return launch_t<FMT, 4, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
-    case 8: return launch_t<FMT, 8, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
-    default: return launch_t<FMT, 16, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
-  }
+  if (waves_for(n, k) == 4) return launch_t<FMT, 4, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+  return launch_t<FMT, 8, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
 }
 
 }  // namespace

@@ -23,7 +23,7 @@ PAIRS = [
     ("q8_0", 4096, 4096, 8, 8, 1),      # separate quantizer + decode GEMV
     ("q4_0", 2048, 2048, 4, 3, 1),      # quantizer fused into the GEMV
     ("q4_k", 12288, 4096, 32, 32, 1),   # int8 matrix cores, then register-direct
-    ("q6_k", 1024, 12288, 32, 32, 9),   # matrix cores, K split over 16 waves
+    ("q6_k", 1024, 12288, 32, 32, 9),   # matrix cores, K split over 8 waves
 ]
 
 
