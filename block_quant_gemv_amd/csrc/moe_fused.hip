@@ -16,8 +16,9 @@
 // token by repeated wave-wide maxima of an order-preserving (logit, expert)
 // key, softmax over the selected logits, then the table of entries -- one
 // per distinct selected expert, in order of first selection (token-major,
-// slot order), holding every token that chose it, plus the shared expert
-// with all tokens. All workgroups build the same table, so no grid-wide
+// slot order), holding every token that chose it, after the shared
+// expert's entries (its tokens in groups of four, so that its items weigh
+// about as much as a routed expert's and are taken first). All workgroups build the same table, so no grid-wide
 // hand-off is needed, and each distinct expert's weights are read once for
 // all of its tokens. An item is (entry, 32 consecutive elements of h): the
 // 32 gate rows and the 32 matching up rows of the expert, so the workgroup
@@ -51,13 +52,18 @@ constexpr int kDnLPL = 5;           // 16-byte loads per lane in moe_down_kernel
 constexpr int kMaxTok = 16;         // tokens a launch can hold
 // Tokens up to which the two-launch expert stage is used. Measured on MI355X
 // (256 experts, top-8 + shared, hidden 2048, expert intermediate 512, Q4_0,
-// expert weights from HBM): 18.1 / 25.8 / 33.6 us at 1 / 2 / 4 tokens against
-// 24.4 / 29.2 / 37.7 us for the six-launch path, but 56.5 / 100 us against
-// 52.4 / 81.0 us at 8 / 16 tokens, where each workgroup walks several items
-// one after another and the item's load, decode and re-quantization do not
-// overlap.
-constexpr int kFusedMaxTok = 4;
+// expert weights from HBM): 16.5 / 23.7 / 30.6 / 43.1 / 70.3 us at 1 / 2 / 4
+// / 8 / 16 tokens against 24.4 / 29.2 / 37.7 / 48.9 / 75.0 us for the
+// six-launch path, once the shared expert's tokens are split over entries of
+// kShareTok tokens that are taken first (one entry with all 16 tokens, last:
+// 100 us at 16 tokens).
+constexpr int kFusedMaxTok = kMaxTok;
 constexpr int kMaxPairs = kMaxTok * 16;
+// Tokens per shared-expert entry: the shared expert serves every token, so
+// its tokens are split over several entries (each reads the shared weights
+// again, mostly from cache) to keep its items as light as the routed ones.
+constexpr int kShareTok = 4;
+constexpr int kMaxShare = (kMaxTok + kShareTok - 1) / kShareTok;
 constexpr int kBufDword3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
@@ -67,8 +73,8 @@ constexpr int kMaxExperts = 1024;
 struct alignas(16) Route {
   int32_t ids[kMaxPairs];       // [token][slot] selected expert
   float wts[kMaxPairs];         // [token][slot] softmax weight
-  int32_t ent_expert[kMaxPairs + 1];
-  uint32_t ent_mask[kMaxPairs + 1];  // tokens of the entry, bit t
+  int32_t ent_expert[kMaxPairs + kMaxShare];
+  uint32_t ent_mask[kMaxPairs + kMaxShare];  // tokens of the entry, bit t
   uint32_t tok_mask[kMaxExperts];    // per expert: tokens that chose it
   int32_t first_pair[kMaxExperts];   // per expert: its first (token, slot) pair
   int32_t wave_first[kMaxPairs / 64];
@@ -146,18 +152,24 @@ QG_DEV void build_route(Route& R, const float* __restrict__ logits, int n_expert
   const uint64_t bal = __ballot(first);
   if (lane == 0 && wid < kMaxPairs / 64) R.wave_first[wid] = __popcll(bal);
   __syncthreads();
+  // The shared expert's entries come first (kShareTok tokens each), so
+  // their heavier items are taken at the start rather than at the tail.
+  const int nsh = (m + kShareTok - 1) / kShareTok;
   if (first) {
     int idx = __popcll(bal & ((1ull << lane) - 1ull));
     for (int w = 0; w < wid; ++w) idx += R.wave_first[w];
-    R.ent_expert[idx] = e;
-    R.ent_mask[idx] = mask;
+    R.ent_expert[nsh + idx] = e;
+    R.ent_mask[nsh + idx] = mask;
+  }
+  if (tid < nsh) {
+    const int t0 = kShareTok * tid, t1 = (t0 + kShareTok) < m ? (t0 + kShareTok) : m;
+    R.ent_expert[tid] = -1;
+    R.ent_mask[tid] = (uint32_t)((1ull << t1) - (1ull << t0));
   }
   if (tid == 0) {
     int nr = 0;
     for (int w = 0; w < (np + 63) / 64; ++w) nr += R.wave_first[w];
-    R.ent_expert[nr] = -1;  // the shared expert, every token
-    R.ent_mask[nr] = m >= 32 ? 0xffffffffu : ((1u << m) - 1u);
-    R.n_entries = nr + 1;
+    R.n_entries = nr + nsh;
   }
   __syncthreads();
 }
@@ -600,8 +612,8 @@ hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
   const int U = (int)(c.inter / 32);
   const int rpp = 64 / (U < 64 ? U : 64);
   a.dn_rows = rpp * 2 > 8 ? rpp * 2 : 8;
-  // Entries: at most one per (token, slot) pair, plus the shared expert.
-  const int n_items_max = (c.m * c.top_k + 1) * (int)(c.inter / 32);
+  // Entries: at most one per (token, slot) pair, plus the shared expert's.
+  const int n_items_max = (c.m * c.top_k + (c.m + kShareTok - 1) / kShareTok) * (int)(c.inter / 32);
   hipError_t e;
   switch (c.fmt) {
     case kQ4_0: e = launch_up_npl<kQ4_0>(a, n_items_max, s); break;

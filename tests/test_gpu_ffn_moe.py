@@ -132,12 +132,13 @@ def _moe_inputs(E, H, I, seed, fmt="q4_0"):
     return wr, gu_all, dn_all, gu_sh, dn_sh
 
 
-# Shapes: the decode workload at 1, 4 and 16 tokens (two-launch expert stage
-# up to 4 tokens, six launches above); small shapes (six launches); other
-# expert formats (Q4_K, IQ4_NL and Q5_K through the two-launch stage, Q8_0
-# through the six launches: its 2176-byte rows do not fit the stage's LDS).
+# Shapes: the decode workload at 1, 4, 8 and 16 tokens (two-launch expert
+# stage); small shapes (six launches); other expert formats (Q4_K, IQ4_NL and
+# Q5_K through the two-launch stage, Q8_0 through the six launches, also at
+# 16 tokens: its 2176-byte rows do not fit the stage's LDS).
 @pytest.mark.parametrize("E,H,I,K,m,fmt", [(256, 2048, 512, 8, 1, "q4_0"), (256, 2048, 512, 8, 4, "q4_0"),
-                                            (256, 2048, 512, 8, 16, "q4_0"),
+                                            (256, 2048, 512, 8, 8, "q4_0"),
+                                            (256, 2048, 512, 8, 16, "q4_0"), (32, 2048, 512, 8, 16, "q8_0"),
                                             (16, 256, 64, 4, 5, "q4_0"), (8, 512, 128, 8, 2, "q4_0"),
                                             (32, 2048, 512, 8, 3, "q8_0"), (32, 2048, 1024, 6, 2, "q4_k"),
                                             (16, 2048, 512, 4, 2, "iq4_nl"), (16, 2048, 512, 8, 3, "q5_k")])
