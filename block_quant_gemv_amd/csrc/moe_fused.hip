@@ -276,6 +276,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
   // The byte range of this wave's four rows of an item: virtual rows
   // 4 wid .. 4 wid + 3 (0..31 gate, 32..63 up), contiguous in the matrix.
   const int v0 = kUpRows * wid;
+  const int rr = lane >> 4, lam = lane & 15;  // this lane's row of the four, and unit phase
   auto item_range = [&](int item, const uint8_t*& W, int64_t& b0) __attribute__((always_inline)) {
     const int en = item / tiles, j = item - en * tiles;
     const int e = R.ent_expert[en];
@@ -322,7 +323,10 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
       if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
     }
     issue(buf, item + gridDim.x);
-    const uint32_t base = (uint32_t)(b0 - a0);
+    // Each 16-lane row of the wave takes one of its four rows (lane l:
+    // row l / 16, units l % 16 + 16 i), so a row's sum is a 16-lane
+    // reduction and one reduction serves all four rows.
+    const uint32_t base = (uint32_t)(b0 - a0) + (uint32_t)(rr * a.rb_gu);
     // Tokens in chunks of kUpTok (accumulators stay in registers); the
     // weights are decoded from LDS again for each chunk.
     uint32_t mrem = mask;  // tokens of the entry not yet taken, ascending
@@ -333,68 +337,56 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
         tok[t] = mrem ? __builtin_ctz(mrem) : 0;
         mrem &= mrem - 1;
       }
-      float acc[kUpRows][kUpTok];
+      float acc[kUpTok];
 #pragma unroll
-      for (int r = 0; r < kUpRows; ++r)
-#pragma unroll
-        for (int t = 0; t < kUpTok; ++t) acc[r][t] = 0.0f;
-      for (int u = lane; u < U; u += 64) {
+      for (int t = 0; t < kUpTok; ++t) acc[t] = 0.0f;
+      for (int u = lam; u < U; u += 16) {
         const uint32_t uoff = (uint32_t)((u / F::kUPB) * F::kBB);
         const int sub = u % F::kUPB;
-        Act x[kUpTok];
+        const typename F::W w = F::load(tile, base + uoff, sub, cbr);
 #pragma unroll
         for (int t = 0; t < kUpTok; ++t)
-          if (t0 + t < c) x[t] = load_act(act + tok[t] * tokb, U, u);
-#pragma unroll
-        for (int r = 0; r < kUpRows; ++r) {
-          const typename F::W w = F::load(tile, base + (uint32_t)(r * a.rb_gu) + uoff, sub, cbr);
-#pragma unroll
-          for (int t = 0; t < kUpTok; ++t)
-            if (t0 + t < c) acc[r][t] = F::fma(w, x[t], acc[r][t]);
-        }
+          if (t0 + t < c) acc[t] = F::fma(w, load_act(act + tok[t] * tokb, U, u), acc[t]);
       }
 #pragma unroll
       for (int t = 0; t < kUpTok; ++t) {
         if (t0 + t < c) {
-#pragma unroll
-          for (int r = 0; r < kUpRows; ++r) {
-            const float sum = group_sum(acc[r][t], 64);
-            if (lane == 0) s_gu[(t0 + t) * 64 + v0 + r] = sum;
-          }
+          const float sum = group_sum16(acc[t], 16);
+          if (lam == 0) s_gu[(t0 + t) * 64 + v0 + rr] = sum;
         }
       }
     }
     __syncthreads();
 
-    // SwiGLU and Q8 re-quantization of the item's 32 elements of h, eight
-    // lanes per token (the activation quantizer's arithmetic).
-    if ((int)threadIdx.x < 8 * c) {
-      const int i = threadIdx.x >> 3, part = threadIdx.x & 7;
+    // SwiGLU and Q8 re-quantization of the item's 32 elements of h, 32
+    // lanes per token, one element each (the activation quantizer's
+    // arithmetic: the block's absolute maximum, d = amax / 127, the codes
+    // and their sum).
+    if ((int)threadIdx.x < 32 * c) {
+      const int i = threadIdx.x >> 5, el = threadIdx.x & 31;
       int t = -1;
       for (int q = 0; q <= i; ++q) t = __builtin_ffs(mask >> (t + 1)) + t;
       const int64_t row = (int64_t)t * S1 + slot_of(R, t, e, a.top_k);
-      const float4 g = *reinterpret_cast<const float4*>(s_gu + i * 64 + 4 * part);
-      const float4 up = *reinterpret_cast<const float4*>(s_gu + i * 64 + 32 + 4 * part);
-      float4 h;
-      h.x = g.x / (1.0f + expf(-g.x)) * up.x;
-      h.y = g.y / (1.0f + expf(-g.y)) * up.y;
-      h.z = g.z / (1.0f + expf(-g.z)) * up.z;
-      h.w = g.w / (1.0f + expf(-g.w)) * up.w;
-      const int64_t col = (int64_t)32 * j + 4 * part;
-      *reinterpret_cast<float4*>(a.gu_out + row * 2 * a.inter + col) = g;
-      *reinterpret_cast<float4*>(a.gu_out + row * 2 * a.inter + a.inter + col) = up;
-      *reinterpret_cast<float4*>(a.h_out + row * a.inter + col) = h;
-      float amax = fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w)));
-      amax = max8(amax);
+      const float g = s_gu[i * 64 + el];
+      const float up = s_gu[i * 64 + 32 + el];
+      const float h = g / (1.0f + expf(-g)) * up;
+      const int64_t col = (int64_t)32 * j + el;
+      a.gu_out[row * 2 * a.inter + col] = g;
+      a.gu_out[row * 2 * a.inter + a.inter + col] = up;
+      a.h_out[row * a.inter + col] = h;
+      float amax = max8(fabsf(h));
+      amax = fmaxf(amax, dpp<0x140>(amax));           // 16 lanes (row_mirror)
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));  // 32 lanes
       const float d = (amax > 0.0f) ? amax / 127.0f : 0.0f;
-      int s;
-      const uint32_t packed = q8_pack4(h, d, s);
-      *reinterpret_cast<uint32_t*>(a.hq + row * a.inter + col) = packed;
-      s = sum4(s);
-      s += other_quad(s);
-      if (part == 0) {
+      const int q = d != 0.0f ? q8_code(h, d, __builtin_amdgcn_rcpf(d)) : 0;
+      a.hq[row * a.inter + col] = (int8_t)q;
+      int qs = sum4(q);
+      qs += other_quad(qs);
+      qs += dpp_i<0x140>(qs);        // 16 lanes
+      qs += __shfl_xor(qs, 16, 64);  // 32 lanes
+      if (el == 0) {
         a.hd[row * (a.inter / 32) + j] = d;
-        a.hs[row * (a.inter / 32) + j] = s;
+        a.hs[row * (a.inter / 32) + j] = qs;
       }
     }
     __syncthreads();  // s_gu is reused by the next item
@@ -546,18 +538,42 @@ hipError_t launch_up_npl(const MoeFusedArgs& a, int n_items_max, hipStream_t s) 
   return small ? launch_up_t<FMT, 5, 16>(a, n_items_max, s) : launch_up_t<FMT, kUpLPL, 16>(a, n_items_max, s);
 }
 
+// Output rows per down item: a.dn_rows or twice that when a wave's rows
+// still fit its loads. An item costs about as much as kDnItemRows rows more
+// than its rows, and the workgroups take the items in rounds, so the choice
+// with fewer rounds x (rows + kDnItemRows) wins (measured on MI355X, Q4_0,
+// hidden 2048, expert intermediate 512: 16 rows at 16 tokens 70.4 -> 66.7 us
+// per layer; 8 rows stay best where a round more would be needed).
+constexpr int kDnItemRows = 8;
+
 template <int FMT, int LPR, int JU>
-hipError_t launch_dn_t(const MoeFusedArgs& a, hipStream_t s) {
+hipError_t launch_dn_t(MoeFusedArgs a, hipStream_t s) {
   auto kern = moe_down_kernel<FMT, LPR, JU>;
   const int S1 = a.top_k + 1;
-  const size_t lds = (size_t)kMaxTok * 64 * sizeof(float) + (size_t)S1 * a.tile_bytes;
-  int per_cu = 0, cus = 0;
-  hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), S1 * 64, lds, true, &per_cu, &cus);
-  if (e != hipSuccess) return e;
-  const int64_t items = (int64_t)a.m * ((a.hidden + a.dn_rows - 1) / a.dn_rows);
-  int64_t grid = (int64_t)cus * per_cu;
-  if (grid > items) grid = items;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S1 * 64), lds, s, a);
+  const int rows0 = a.dn_rows;
+  int64_t best_cost = -1, best_grid = 0;
+  size_t best_lds = 0;
+  for (int rows = rows0; rows <= 2 * rows0; rows *= 2) {
+    if (rows > rows0 && rows * a.rb_dn + 32 > (int64_t)kDnLPL * 1024) break;
+    const int tile = (int)((rows * a.rb_dn + 32 + 15) / 16 * 16 + 16);
+    const size_t lds = (size_t)kMaxTok * 64 * sizeof(float) + (size_t)S1 * tile;
+    int per_cu = 0, cus = 0;
+    hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), S1 * 64, lds, true, &per_cu, &cus);
+    if (e != hipSuccess) return e;
+    const int64_t items = (int64_t)a.m * ((a.hidden + rows - 1) / rows);
+    int64_t grid = (int64_t)cus * per_cu;
+    if (grid > items) grid = items;
+    if (grid < 1) grid = 1;
+    const int64_t cost = (items + grid - 1) / grid * (rows + kDnItemRows);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_grid = grid;
+      best_lds = lds;
+      a.dn_rows = rows;
+      a.tile_bytes = tile;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)best_grid), dim3(S1 * 64), best_lds, s, a);
   return hipGetLastError();
 }
 
@@ -626,9 +642,8 @@ hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  // The down launch reuses the tile size of its own rows.
-  MoeFusedArgs d = a;
-  d.tile_bytes = (int)((a.dn_rows * a.rb_dn + 32 + 15) / 16 * 16 + 16);
+  // The down launch picks its rows per item and the tile size for them.
+  const MoeFusedArgs& d = a;
   switch (c.fmt) {
 #define QG_DN(F)                                                           \
   case F:                                                                  \
