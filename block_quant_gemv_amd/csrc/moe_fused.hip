@@ -59,6 +59,9 @@ constexpr int kMaxTok = 16;         // tokens a launch can hold
 // 100 us at 16 tokens).
 constexpr int kFusedMaxTok = kMaxTok;
 constexpr int kMaxPairs = kMaxTok * 16;
+// moe_up_kernel's gate|up sums of an item, [token][64], two of them: items
+// alternate, so SwiGLU of one item and the decode of the next can overlap.
+constexpr int kUpSgu = 2 * kMaxTok * 64 * 4;
 // Tokens per shared-expert entry: the shared expert serves every token, so
 // its tokens are split over several entries (each reads the shared weights
 // again, mostly from cache) to keep its items as light as the routed ones.
@@ -217,8 +220,8 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
   using F = typename FmtOf<FMT>::T;
   extern __shared__ __align__(16) uint8_t smem[];
   Route& R = *reinterpret_cast<Route*>(smem);
-  float* s_gu = reinterpret_cast<float*>(smem + sizeof(Route));         // [kMaxTok][64]
-  uint8_t* act = smem + sizeof(Route) + kMaxTok * 64 * sizeof(float);   // staged activations
+  float* s_gu2 = reinterpret_cast<float*>(smem + sizeof(Route));  // [2][kMaxTok][64]
+  uint8_t* act = smem + sizeof(Route) + kUpSgu;                     // staged activations
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   uint8_t* tile = act + a.act_bytes + wid * a.tile_bytes;
@@ -304,7 +307,10 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
   u32x4 buf[LPL];
   issue(buf, blockIdx.x);
 
+  int half = 0;  // which half of s_gu2 this item uses
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    float* s_gu = s_gu2 + half * (kMaxTok * 64);
+    half ^= 1;
     const int en = item / tiles, j = item - en * tiles;
     const int e = R.ent_expert[en];
     const uint32_t mask = R.ent_mask[en];
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
     const int nch = (int)(((b0 + kUpRows * a.rb_gu + 15) & ~(int64_t)15) - a0) >> 4;
 
     // Weights to the wave's LDS tile, the next item's requested, then
-    // decode: lane l takes units l + 64 jj of each row.
+    // decode.
 #pragma unroll
     for (int i = 0; i < LPL; ++i) {
       const int ch = lane + 64 * i;
@@ -389,7 +395,10 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
         a.hs[row * (a.inter / 32) + j] = qs;
       }
     }
-    __syncthreads();  // s_gu is reused by the next item
+    // No barrier here: the next item writes the other half of s_gu2, and
+    // its own barrier (after its decode) orders these reads before the
+    // item after it writes this half again. The waves that do no SwiGLU
+    // go on to the next item's decode at once.
   }
 }
 
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
 namespace {
 
 size_t up_lds(const MoeFusedArgs& a) {
-  return sizeof(Route) + (size_t)kMaxTok * 64 * sizeof(float) + (size_t)a.act_bytes +
+  return sizeof(Route) + (size_t)kUpSgu + (size_t)a.act_bytes +
          (size_t)kUpWaves * a.tile_bytes;
 }
 
@@ -590,7 +599,7 @@ bool moe_fused_ok(const MoeCall& c) {
   const int rpp = 64 / (int)(U < 64 ? U : 64);
   const int rows = rpp * 2 > 8 ? rpp * 2 : 8;
   if (rows * rb_dn + 32 > (int64_t)kDnLPL * 1024) return false;
-  const size_t up = sizeof(Route) + (size_t)kMaxTok * 64 * 4 + (size_t)c.m * act_token_bytes((int)(c.hidden / 32)) +
+  const size_t up = sizeof(Route) + (size_t)kUpSgu + (size_t)c.m * act_token_bytes((int)(c.hidden / 32)) +
                     (size_t)kUpWaves * (size_t)((kUpRows * rb_gu + 32 + 15) / 16 * 16 + 16);
   return up <= (size_t)kLdsBytes;
 }
