@@ -38,49 +38,63 @@ namespace qg {
 
 constexpr int kRouterMaxTok = 16;
 
-// One workgroup per expert row: its 256 threads split the row into float4
-// chunks, each thread accumulates its chunks against the same chunks of every
-// token, and the workgroup adds the partial sums in a fixed order (DPP within
-// a wave, then the four waves in order). The router's workgroups also
-// quantize x to Q8 blocks for the expert GEMVs (block b by workgroup b mod
-// grid, eight lanes per block as in the activation quantizer), so no
-// separate quantizer launch is needed.
-// MT: token slots (m <= MT). A thread requests a chunk's weights and the
-// chunk of every token before it multiplies any of them, so a chunk costs one
-// memory round trip whatever m is (token slots past m re-read the last
-// token's chunk and are never stored); two chunks are in flight together.
-template <int MT>
+// A workgroup computes the logits of ET experts for TT tokens: its 256
+// threads split the rows into float4 chunks, each thread accumulates its
+// chunks of every (expert, token) pair, and the workgroup adds the partial
+// sums in a fixed order (DPP within a wave, then the four waves in order), so
+// a logit does not depend on the tiling. Tiles of several experts and several
+// tokens cut the bytes each workgroup reads (ET rows of W_r plus TT rows of
+// x) from 8 KB x (1 + m) to 8 KB x (ET + TT) at hidden 2048. The router's
+// workgroups also quantize x to Q8 blocks for the expert GEMVs (block b by
+// workgroup b mod grid, eight lanes per block as in the activation
+// quantizer), so no separate quantizer launch is needed.
+// A thread requests a chunk's weights and x before it multiplies any of them,
+// so a chunk costs one memory round trip; two chunks are in flight together.
+// Experts and tokens past the end re-read the last one and are not stored.
+template <int ET, int TT>
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ wr,
                                                      const float* __restrict__ x,
                                                      float* __restrict__ logits, int8_t* __restrict__ xq,
                                                      float* __restrict__ dx, int32_t* __restrict__ sx,
                                                      int n_experts, int64_t hidden, int m) {
-  __shared__ float part[4][MT];
+  __shared__ float part[4][ET * TT];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t e = blockIdx.x;
-  const float4* wrow = reinterpret_cast<const float4*>(wr + e * hidden);
-  const int64_t nch = hidden / 4;
-  float acc[MT];
+  const int n_eg = (n_experts + ET - 1) / ET;
+  const int e0 = (int)(blockIdx.x % n_eg) * ET, t0 = (int)(blockIdx.x / n_eg) * TT;
+  const float4* wrow[ET];
+  const float4* xrow[TT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+  for (int i = 0; i < ET; ++i)
+    wrow[i] = reinterpret_cast<const float4*>(wr + (int64_t)(e0 + i < n_experts ? e0 + i : n_experts - 1) * hidden);
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+    xrow[t] = reinterpret_cast<const float4*>(x + (int64_t)(t0 + t < m ? t0 + t : m - 1) * hidden);
+  const int64_t nch = hidden / 4;
+  float acc[ET][TT];
+#pragma unroll
+  for (int i = 0; i < ET; ++i)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[i][t] = 0.0f;
 #pragma unroll 2
   for (int64_t c = threadIdx.x; c < nch; c += blockDim.x) {
-    const float4 w = wrow[c];
-    float4 v[MT];
+    float4 w[ET], v[TT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int tt = t < m ? t : m - 1;
-      v[t] = reinterpret_cast<const float4*>(x + (int64_t)tt * hidden)[c];
+    for (int i = 0; i < ET; ++i) w[i] = wrow[i][c];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) v[t] = xrow[t][c];
+#pragma unroll
+    for (int i = 0; i < ET; ++i)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        acc[i][t] = fmaf(w[i].x, v[t].x, fmaf(w[i].y, v[t].y, fmaf(w[i].z, v[t].z, fmaf(w[i].w, v[t].w, acc[i][t]))));
+  }
+#pragma unroll
+  for (int i = 0; i < ET; ++i)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const float s = group_sum(acc[i][t], 64);
+      if (lane == 0) part[wid][i * TT + t] = s;
     }
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      acc[t] = fmaf(w.x, v[t].x, fmaf(w.y, v[t].y, fmaf(w.z, v[t].z, fmaf(w.w, v[t].w, acc[t]))));
-  }
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const float s = group_sum(acc[t], 64);
-    if (lane == 0) part[wid][t] = s;
-  }
   // Q8 blocks of x: 32 blocks per workgroup pass, eight lanes each.
   const int64_t nblocks = (int64_t)m * (hidden / 32);
   for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks;
@@ -102,10 +116,30 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
     }
   }
   __syncthreads();
-  if (threadIdx.x < m) {
-    const int t = threadIdx.x;
-    logits[(int64_t)t * n_experts + e] = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+  if ((int)threadIdx.x < ET * TT) {
+    const int i = threadIdx.x / TT, t = threadIdx.x % TT;
+    if (e0 + i < n_experts && t0 + t < m)
+      logits[(int64_t)(t0 + t) * n_experts + e0 + i] =
+          (part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x]);
   }
+}
+
+template <int ET, int TT>
+hipError_t launch_router_t(const MoeCall& c, hipStream_t s) {
+  const int grid = (c.n_experts + ET - 1) / ET * ((c.m + TT - 1) / TT);
+  hipLaunchKernelGGL((router_kernel<ET, TT>), dim3((unsigned)grid), dim3(256), 0, s, c.router, c.x, c.logits, c.xq,
+                     c.dx, c.sx, c.n_experts, c.hidden, c.m);
+  return hipGetLastError();
+}
+
+// Tiles: up to 4 tokens per workgroup, and 2 or 4 experts from 5 tokens on
+// (one workgroup per expert tile and token tile).
+hipError_t launch_router(const MoeCall& c, hipStream_t s) {
+  if (c.m <= 1) return launch_router_t<1, 1>(c, s);
+  if (c.m <= 2) return launch_router_t<1, 2>(c, s);
+  if (c.m <= 4) return launch_router_t<1, 4>(c, s);
+  if (c.m <= 8) return launch_router_t<2, 4>(c, s);
+  return launch_router_t<4, 4>(c, s);
 }
 
 // One workgroup of 64 * m threads. Wave t selects token t's top_k experts and
@@ -267,11 +301,7 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (c.m < 1 || c.m > kRouterMaxTok || c.top_k > 16) return hipErrorInvalidValue;
   if (c.n_experts < 1 || c.n_experts > 4096 || c.hidden % 32) return hipErrorInvalidValue;
   // 1. router logits, and x quantized to Q8 blocks
-  auto router = c.m <= 1 ? router_kernel<1> : c.m <= 2 ? router_kernel<2> : c.m <= 4 ? router_kernel<4>
-               : c.m <= 8 ? router_kernel<8> : router_kernel<16>;
-  hipLaunchKernelGGL(router, dim3((unsigned)c.n_experts), dim3(256), 0, s, c.router, c.x, c.logits,
-                     c.xq, c.dx, c.sx, c.n_experts, c.hidden, c.m);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_router(c, s);
   if (e != hipSuccess) return e;
   const bool s16 = c.xq16 != nullptr;
   if (QG_MOE_FUSED && !s16 && moe_fused_ok(c)) return launch_moe_fused(c, s);
