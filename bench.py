@@ -86,19 +86,24 @@ def graph_of(fn, n):
     return g
 
 
-def time_graph(g, n_inner, reps, warm=2):
-    """Mean microseconds per inner call over `reps` replays of graph g."""
+def time_graph(g, n_inner, reps, warm=2, trials=3):
+    """Microseconds per inner call: the median over `trials` windows of
+    `reps` replays of graph g each (a single short window is at the mercy
+    of the clocks the previous work left behind)."""
     import torch
     for _ in range(warm):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * n_inner)
+    out = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / (reps * n_inner))
+    return float(np.median(out))
 
 
 # The dominant kernel of the step: the Q8_0 GEMV with the activation

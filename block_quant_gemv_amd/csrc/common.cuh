@@ -47,6 +47,20 @@ QG_DEV void lds_read_unaligned(const uint8_t* base, uint32_t off, uint32_t (&out
   for (int i = 0; i < N; ++i) out[i] = alignbyte(w[i + 1], w[i], s);
 }
 
+// Four dwords at a 2-byte-aligned LDS address in one read: gfx950 serves
+// unaligned LDS reads (the compiler emits a single ds_read_b128). Measured on
+// MI355X it is slower than lds_read_unaligned's aligned reads plus byte
+// shifts in load-bound kernels, and faster where the vector ALU is the bound
+// (the IQ4_NL lm_head 4096 -> 248320: 115 -> 111 us sustained).
+typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));
+QG_DEV void lds_read4_direct(const uint8_t* base, uint32_t off, uint32_t (&out)[4]) {
+  const u32x4a2 v = *reinterpret_cast<const u32x4a2*>(base + off);
+  out[0] = v.x;
+  out[1] = v.y;
+  out[2] = v.z;
+  out[3] = v.w;
+}
+
 QG_DEV uint32_t lds_u16(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint16_t*>(base + off);
 }

@@ -114,7 +114,7 @@ struct FmtIQ4_NL {
     W w;
     uint32_t q[4];
     w.d = half_bits(lds_u16(t, off));
-    lds_read_unaligned<4>(t, off + 2, q);
+    lds_read4_direct(t, off + 2, q);  // no byte shifts: this decode is ALU-bound
 #pragma unroll
     for (int i = 0; i < 4; ++i) cb_lookup8(q[i], cb, w.v[i], w.v[4 + i]);
     return w;
