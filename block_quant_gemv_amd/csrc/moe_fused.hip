@@ -412,9 +412,11 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
   const int S1 = a.top_k + 1;
   const int RB = a.dn_rows;                         // output rows per item (multiple of 64 / LPR)
   float* s_out = reinterpret_cast<float*>(smem);   // [S1][RB]
+  int32_t* s_ids = reinterpret_cast<int32_t*>(smem + kMaxTok * 64 * 4);  // [m][top_k]
+  float* s_wts = reinterpret_cast<float*>(s_ids + kMaxPairs);             // [m][top_k]
   const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // this wave's slot
   const int lane = threadIdx.x & 63;
-  uint8_t* tile = smem + (size_t)kMaxTok * 64 * sizeof(float) + s * a.tile_bytes;
+  uint8_t* tile = smem + (size_t)kMaxTok * 64 * sizeof(float) + 2 * kMaxPairs * 4 + s * a.tile_bytes;
   constexpr int RPP = 64 / LPR;
   const int lam = lane % LPR, rho = lane / LPR;
   const int U = (int)(a.inter / 32);
@@ -423,13 +425,23 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
   uint32_t cbr[5] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3], 0x03020100u};
 #pragma unroll
   for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+  // The routing (expert ids and weights of every pair) to LDS once: items
+  // then find their experts and combine weights without global-memory
+  // round trips (measured: 8 tokens 40.7 -> 39.3 us per layer). Requesting
+  // the next item's h ahead with its weights measured slower (47 us at 8
+  // tokens) and is not done.
+  for (int p = threadIdx.x; p < a.m * a.top_k; p += blockDim.x) {
+    s_ids[p] = a.ids_out[p];
+    s_wts[p] = a.wts_out[p];
+  }
+  __syncthreads();
 
   // The byte range of this wave's slot's rows of an item.
   auto item_range = [&](int item, const uint8_t*& W, int64_t& b0, int& nrows) __attribute__((always_inline)) {
     const int t = item / nblk, blk = item - t * nblk;
     const int64_t r0 = (int64_t)blk * RB;
     nrows = (int)((a.hidden - r0) < RB ? (a.hidden - r0) : RB);
-    const int e = s < a.top_k ? a.ids_out[t * a.top_k + s] : -1;
+    const int e = s < a.top_k ? s_ids[t * a.top_k + s] : -1;
     W = e < 0 ? a.dn_shared : a.dn + (int64_t)e * a.dn_stride;
     b0 = r0 * a.rb_dn;
   };
@@ -506,7 +518,7 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
     // y = sum over routed slots in order of weight * output, plus the shared expert.
     for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
       float acc = 0.0f;
-      for (int k = 0; k < a.top_k; ++k) acc = fmaf(a.wts_out[t * a.top_k + k], s_out[k * RB + r], acc);
+      for (int k = 0; k < a.top_k; ++k) acc = fmaf(s_wts[t * a.top_k + k], s_out[k * RB + r], acc);
       a.y[(int64_t)t * a.hidden + r0 + r] = acc + s_out[a.top_k * RB + r];
     }
     __syncthreads();  // s_out and the tiles are reused by the next item
@@ -565,7 +577,7 @@ hipError_t launch_dn_t(MoeFusedArgs a, hipStream_t s) {
   for (int rows = rows0; rows <= 2 * rows0; rows *= 2) {
     if (rows > rows0 && rows * a.rb_dn + 32 > (int64_t)kDnLPL * 1024) break;
     const int tile = (int)((rows * a.rb_dn + 32 + 15) / 16 * 16 + 16);
-    const size_t lds = (size_t)kMaxTok * 64 * sizeof(float) + (size_t)S1 * tile;
+    const size_t lds = (size_t)kMaxTok * 64 * sizeof(float) + 2 * kMaxPairs * 4 + (size_t)S1 * tile;
     int per_cu = 0, cus = 0;
     hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), S1 * 64, lds, true, &per_cu, &cus);
     if (e != hipSuccess) return e;
