@@ -311,10 +311,19 @@ class Clocks:
         return out
 
 
+SUSTAIN_S = 2.0  # seconds of each sustained run (--sustain-seconds)
+
+
+def set_sustain(seconds):
+    global SUSTAIN_S
+    SUSTAIN_S = float(seconds)
+
+
 def sustained(graph, n_inner, seconds, clocks, leg):
     """Replay graph back to back for about `seconds` while clocks are
     sampled under `leg`; microseconds per inner call over that window."""
     import torch
+    seconds = SUSTAIN_S if seconds is None else seconds
     clocks.leg = leg
     graph.replay()
     torch.cuda.synchronize()
@@ -330,6 +339,7 @@ def sustained(graph, n_inner, seconds, clocks, leg):
     e1.record()
     torch.cuda.synchronize()
     clocks.leg = None
+    log(f"{leg}: sustained run of {reps} replays done")
     return e0.elapsed_time(e1) * 1e3 / (reps * n_inner), reps * n_inner
 
 
@@ -388,6 +398,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-clocks", action="store_true")
+    ap.add_argument("--sustain-seconds", type=float, default=SUSTAIN_S,
+                    help="length of each sustained run (shorter for counter passes, which serialize dispatches)")
     ap.add_argument("--leg", choices=LEGS,
                     help="run one extra measurement alone and print its results (for profiler runs)")
     ap.add_argument("--only-dominant", action="store_true",
@@ -399,6 +411,7 @@ def main():
     ap.add_argument("--record-mfma", metavar="PMC",
                     help="turn a rocprofv3 --pmc run of --leg m32 into the recorded matrix-core counters")
     args = ap.parse_args()
+    set_sustain(args.sustain_seconds)
     if args.record_traffic:
         return record_traffic(*args.record_traffic)
     if args.record_mfma:
@@ -498,7 +511,7 @@ def main():
     ms_step = e0.elapsed_time(e1) / steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     # The same step graph replayed for about 2 s, with clocks sampled.
-    sus_us, sus_steps = sustained(graph, R, 2.0, clocks, "headline_step")
+    sus_us, sus_steps = sustained(graph, R, None, clocks, "headline_step")
     # Eager (no graph) step time, for reference.
     eager_us = time_calls(lambda i: step(i), 3 * R, warm=R) if not args.no_extras else None
 
@@ -607,7 +620,7 @@ def leg_lm_head(qg, synth, torch, clocks):
     # sustained first (about 2 s, clocks sampled): the short burst after it
     # then starts from the clocks the chip holds under this load, not from
     # an idle GPU's
-    sus, calls = sustained(gg, R, 2.0, clocks, "lm_head")
+    sus, calls = sustained(gg, R, None, clocks, "lm_head")
     us = time_graph(gg, R, reps=8)
     res["lm_head_us"] = round(us, 2)
     res["lm_head_gbps"] = round(b / (us * 1e-6) / 1e9, 1)
