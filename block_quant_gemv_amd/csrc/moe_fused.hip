@@ -12,21 +12,22 @@
 // merged launches gained more than graph capture alone).
 //
 // moe_up_kernel: every workgroup first re-derives the routing from the
-// router's logits (at most 16 tokens x 4096 experts of fp32 in L2): top-k per
+// router's logits (at most 16 tokens x 1024 experts of fp32 in L2): top-k per
 // token by repeated wave-wide maxima of an order-preserving (logit, expert)
-// key, softmax over the selected logits, then the table of entries -- one
-// per distinct selected expert, in order of first selection (token-major,
-// slot order), holding every token that chose it, after the shared
-// expert's entries (its tokens in groups of four, so that its items weigh
-// about as much as a routed expert's and are taken first). All workgroups build the same table, so no grid-wide
-// hand-off is needed, and each distinct expert's weights are read once for
-// all of its tokens. An item is (entry, 32 consecutive elements of h): the
-// 32 gate rows and the 32 matching up rows of the expert, so the workgroup
-// holds both halves of SwiGLU and a whole Q8 block of h, which it
-// re-quantizes itself. Sixteen waves take four rows each, loaded as one
-// coalesced range and decoded from LDS with the format views the decode GEMV
-// uses; the activations (the router launch's Q8 codes of x) are staged in
-// LDS per entry.
+// key, softmax over the selected logits, then the table of entries: first
+// the shared expert's (its tokens in groups of four, so that its items weigh
+// about as much as a routed expert's and are taken first), then one per
+// distinct selected expert, in order of first selection (token-major, slot
+// order), holding every token that chose it. All workgroups build the same
+// table, so no grid-wide hand-off is needed, and each distinct expert's
+// weights are read once for all of its tokens. An item is (entry, 32
+// consecutive elements of h): the 32 gate rows and the 32 matching up rows
+// of the expert, so the workgroup holds both halves of SwiGLU and a whole Q8
+// block of h, which it re-quantizes itself (32 lanes per token). Sixteen
+// waves take four rows each, loaded as one coalesced range into the wave's
+// LDS tile and decoded with the format views the decode GEMV uses, one row
+// per 16-lane group (so one 16-lane reduction serves all four rows); the
+// activations (the router launch's Q8 codes of x) are staged in LDS once.
 //
 // moe_down_kernel: an item is (token, block of output rows). Wave s takes
 // slot s (routed slots in order, then the shared expert): its expert's rows
