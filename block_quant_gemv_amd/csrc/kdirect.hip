@@ -31,6 +31,9 @@
 #ifndef QG_Q5K_RBIG
 #define QG_Q5K_RBIG 4            // rows per wave iteration for large Q5_K matrices
 #endif
+#ifndef QG_Q4K_RFUSED
+#define QG_Q4K_RFUSED 2          // the same with the quantizer fused (one workgroup per CU)
+#endif
 #ifndef QG_DIRECT_FUSED_WGS_PER_CU
 #define QG_DIRECT_FUSED_WGS_PER_CU 1
 #endif
@@ -344,10 +347,14 @@ template <int FMT>
 static hipError_t launch_fmt(const GemvProblem& p, bool dots, hipStream_t s) {
   // Rows per wave iteration, measured on MI355X (Q4_K): four rows (more
   // bytes in flight per wave) once there are enough rows to still give every
-  // CU several waves, one row for smaller matrices (more waves).
+  // CU several waves, one row for smaller matrices (more waves). With the
+  // quantizer fused (12 or 16 waves, one workgroup per CU) two rows: at
+  // 12288 rows, groups of four left each wave a single group and nothing to
+  // overlap its load with (9.1 -> 7.85 us per call; 24576 rows unchanged).
   constexpr int RB = FMT == kQ5_K ? QG_Q5K_RBIG : QG_Q4K_RBIG;
+  constexpr int RF = FMT == kQ5_K ? QG_Q5K_RBIG : QG_Q4K_RFUSED;
   if (dots) return p.n >= 8192 ? launch_ju<FMT, RB, true, false>(p, s) : launch_ju<FMT, 1, true, false>(p, s);
-  if (p.xf) return p.n >= 8192 ? launch_ju<FMT, RB, false, true>(p, s) : launch_ju<FMT, 1, false, true>(p, s);
+  if (p.xf) return p.n >= 8192 ? launch_ju<FMT, RF, false, true>(p, s) : launch_ju<FMT, 1, false, true>(p, s);
   return p.n >= 8192 ? launch_ju<FMT, RB, false, false>(p, s) : launch_ju<FMT, 1, false, false>(p, s);
 }
 
