@@ -46,10 +46,10 @@ hipError_t launch_moe(const MoeCall& c, hipStream_t s);
 // The expert stage (after the router launch has written logits and the Q8
 // codes of x) in two launches: routing + gate|up + SwiGLU + re-quantization,
 // then down + weighted combine (moe_fused.hip). moe_fused_ok tells whether the
-// call's shapes fit it: up to 4 tokens (measured crossover), top_k <= 15, at most 1024 experts,
+// call's shapes fit it: 1..16 tokens, top_k <= 15, at most 1024 experts,
 // hidden a multiple of 2048 up to 8192 with m * hidden <= 65536, inter in
-// {512, 1024, 2048, 4096}
-// and rows short enough for one load per wave.
+// {512, 1024, 2048, 4096}, row bytes a multiple of 16, and rows short enough
+// for one load per wave (and the up workgroup's LDS).
 bool moe_fused_ok(const MoeCall& c);
 hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s);
 
