@@ -12,7 +12,9 @@
 //
 // Launch sequence on one stream (no host synchronisation):
 //   router_kernel     logits[t, e] = W_r[e] . x[t] (fp32, unquantized x);
-//                     the same workgroups quantize x to Q8 blocks
+//                     the same workgroups quantize x to Q8 (or 16-bit) blocks
+// then, when the shapes fit it, the two-launch expert stage of moe_fused.hip
+// (routing + gate|up + SwiGLU + requant, then down + combine); otherwise:
 //   route_kernel      top-k per token (ties to the lower index), softmax over
 //                     the selected logits, then a table that groups the
 //                     (token, slot) pairs by expert so each selected expert's
@@ -27,6 +29,7 @@
 #include "internal.h"
 #include "moe.h"
 #include "route.cuh"
+#include "s16.cuh"
 #include "s16.h"
 #include "swiglu.h"
 
@@ -51,10 +54,13 @@ constexpr int kRouterMaxTok = 16;
 // A thread requests a chunk's weights and x before it multiplies any of them,
 // so a chunk costs one memory round trip; two chunks are in flight together.
 // Experts and tokens past the end re-read the last one and are not stored.
-template <int ET, int TT>
+// S16: x is quantized to 16-bit codes (xq16) instead of Q8 codes (xq), with
+// the 16-bit activation quantizer's arithmetic.
+template <int ET, int TT, bool S16>
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ wr,
                                                      const float* __restrict__ x,
                                                      float* __restrict__ logits, int8_t* __restrict__ xq,
+                                                     int16_t* __restrict__ xq16,
                                                      float* __restrict__ dx, int32_t* __restrict__ sx,
                                                      int n_experts, int64_t hidden, int m) {
   __shared__ float part[4][ET * TT];
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
       const float s = group_sum(acc[i][t], 64);
       if (lane == 0) part[wid][i * TT + t] = s;
     }
-  // Q8 blocks of x: 32 blocks per workgroup pass, eight lanes each.
+  // Q8 (or 16-bit) blocks of x: 32 blocks per workgroup pass, eight lanes each.
   const int64_t nblocks = (int64_t)m * (hidden / 32);
   for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks;
        blk += (int64_t)gridDim.x * 32) {
@@ -104,10 +110,25 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
     const float4 v = reinterpret_cast<const float4*>(x)[blk * 8 + part8];
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     a = max8(a);
-    const float d = (a > 0.0f) ? a / 127.0f : 0.0f;
+    const float d = (a > 0.0f) ? a / (S16 ? 32767.0f : 127.0f) : 0.0f;
     int sum;
-    const uint32_t packed = q8_pack4(v, d, sum);
-    reinterpret_cast<uint32_t*>(xq)[blk * 8 + part8] = packed;
+    if constexpr (S16) {
+      int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+      if (d != 0.0f) {
+        q0 = code16(v.x, d);
+        q1 = code16(v.y, d);
+        q2 = code16(v.z, d);
+        q3 = code16(v.w, d);
+      }
+      uint2 packed;
+      packed.x = ((uint32_t)q0 & 0xffffu) | ((uint32_t)q1 << 16);
+      packed.y = ((uint32_t)q2 & 0xffffu) | ((uint32_t)q3 << 16);
+      reinterpret_cast<uint2*>(xq16)[blk * 8 + part8] = packed;
+      sum = q0 + q1 + q2 + q3;
+    } else {
+      const uint32_t packed = q8_pack4(v, d, sum);
+      reinterpret_cast<uint32_t*>(xq)[blk * 8 + part8] = packed;
+    }
     sum = sum4(sum);
     sum += other_quad(sum);
     if (part8 == 0) {
@@ -127,8 +148,12 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ w
 template <int ET, int TT>
 hipError_t launch_router_t(const MoeCall& c, hipStream_t s) {
   const int grid = (c.n_experts + ET - 1) / ET * ((c.m + TT - 1) / TT);
-  hipLaunchKernelGGL((router_kernel<ET, TT>), dim3((unsigned)grid), dim3(256), 0, s, c.router, c.x, c.logits, c.xq,
-                     c.dx, c.sx, c.n_experts, c.hidden, c.m);
+  if (c.xq16)
+    hipLaunchKernelGGL((router_kernel<ET, TT, true>), dim3((unsigned)grid), dim3(256), 0, s, c.router, c.x, c.logits,
+                       c.xq, c.xq16, c.dx, c.sx, c.n_experts, c.hidden, c.m);
+  else
+    hipLaunchKernelGGL((router_kernel<ET, TT, false>), dim3((unsigned)grid), dim3(256), 0, s, c.router, c.x,
+                       c.logits, c.xq, c.xq16, c.dx, c.sx, c.n_experts, c.hidden, c.m);
   return hipGetLastError();
 }
 
@@ -300,16 +325,15 @@ int64_t moe_table_ints(int m, int top_k) { return 1 + moe_max_entries(m, top_k) 
 hipError_t launch_moe(const MoeCall& c, hipStream_t s) {
   if (c.m < 1 || c.m > kRouterMaxTok || c.top_k > 16) return hipErrorInvalidValue;
   if (c.n_experts < 1 || c.n_experts > 4096 || c.hidden % 32) return hipErrorInvalidValue;
-  // 1. router logits, and x quantized to Q8 blocks
+  // 16-bit codes of x and h (Q4_0 experts): the expert GEMVs read them
+  // instead of Q8 codes (their scales and sums take dx/sx and hd/hs).
+  const bool s16 = c.xq16 != nullptr;
+  if (s16 && (kGroupTokens != 1 || !c.hq16 || !q40_s16_grouped_ok(c.hidden) || !q40_s16_grouped_ok(c.inter)))
+    return hipErrorInvalidValue;
+  // 1. router logits, and x quantized to Q8 (or 16-bit) blocks
   hipError_t e = launch_router(c, s);
   if (e != hipSuccess) return e;
-  const bool s16 = c.xq16 != nullptr;
-  if (QG_MOE_FUSED && !s16 && moe_fused_ok(c)) return launch_moe_fused(c, s);
-  if (s16) {  // the expert GEMVs read 16-bit codes of x (scales and sums replace the Q8 ones)
-    if (kGroupTokens != 1 || !c.hq16 || !q40_s16_grouped_ok(c.hidden) || !q40_s16_grouped_ok(c.inter))
-      return hipErrorInvalidValue;
-    if ((e = launch_quant_s16(c.x, c.xq16, c.dx, c.sx, (int64_t)c.m * c.hidden / 32, s)) != hipSuccess) return e;
-  }
+  if (QG_MOE_FUSED && moe_fused_ok(c)) return launch_moe_fused(c, s);
   // 2. top-k, softmax and grouping
   const int npairs = c.m * c.top_k;
   const size_t lds = (2 * (size_t)c.n_experts + 3 * (size_t)npairs + 1) * 4;

@@ -40,6 +40,9 @@
 #include "internal.h"
 #include "moe.h"
 #include "route.cuh"
+#include "s16.cuh"
+
+#include <type_traits>
 
 namespace qg {
 
@@ -73,6 +76,9 @@ constexpr int kUpSgu = 2 * kMaxTok * 64 * 4;
 // its tokens are split over several entries (each reads the shared weights
 // again, mostly from cache) to keep its items as light as the routed ones.
 constexpr int kShareTok = 4;
+// LDS bytes per token of staged 16-bit activation codes: per 32-element
+// unit 16 dwords of paired codes, then per unit (scale, code sum).
+__host__ __device__ constexpr int act16_token_bytes(int U) { return 72 * U; }
 constexpr int kMaxShare = (kMaxTok + kShareTok - 1) / kShareTok;
 constexpr int kBufDword3 = 0x00020000;
 constexpr int kNonTemporal = 2;
@@ -193,6 +199,23 @@ QG_DEV int slot_of(const Route& R, int t, int e, int top_k) {
   return s;
 }
 
+// A staged unit of 16-bit codes (see act16_token_bytes): LDS reads only.
+QG_DEV Act16 load_act16(const uint8_t* tok, int U, int u) {
+  Act16 x;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(tok + 64 * u + 16 * v);
+    x.p[4 * v + 0] = q.x;
+    x.p[4 * v + 1] = q.y;
+    x.p[4 * v + 2] = q.z;
+    x.p[4 * v + 3] = q.w;
+  }
+  const int2 ms = *reinterpret_cast<const int2*>(tok + 64 * U + 8 * u);
+  x.dx = __int_as_float(ms.x);
+  x.sum = ms.y;
+  return x;
+}
+
 }  // namespace
 
 struct MoeFusedArgs {
@@ -203,12 +226,15 @@ struct MoeFusedArgs {
   const uint8_t *gu, *gu_shared, *dn, *dn_shared;
   int64_t gu_stride, dn_stride;
   const int8_t* xq;
+  const int16_t* xq16;      // 16-bit codes of x instead of xq (S16 kernels)
   const float* dx;
+  const int32_t* sx;        // code sums of the 16-bit blocks of x
   int64_t hidden, inter;
   int64_t rb_gu, rb_dn;     // row bytes of gate|up (K = hidden) and down (K = inter)
   float* gu_out;            // [m * (top_k + 1), 2 inter]
   float* h_out;             // [m * (top_k + 1), inter]
   int8_t* hq;
+  int16_t* hq16;            // 16-bit codes of h instead of hq (S16 kernels)
   float* hd;
   int32_t* hs;
   float* y;                 // [m, hidden]
@@ -221,10 +247,12 @@ struct MoeFusedArgs {
 // ------------------------------------------------------------ gate|up --
 
 // LPL: 16-byte loads per lane (a wave's four rows); NPL: logits per lane in
-// the routing prologue (n_experts <= 64 NPL).
-template <int FMT, int LPL, int NPL>
+// the routing prologue (n_experts <= 64 NPL); S16: 16-bit activation codes
+// of x and h (Q4_0 experts) instead of Q8 codes.
+template <int FMT, int LPL, int NPL, bool S16>
 __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArgs a) {
   using F = typename FmtOf<FMT>::T;
+  static_assert(!S16 || FMT == kQ4_0, "16-bit activations are for Q4_0 experts");
   extern __shared__ __align__(16) uint8_t smem[];
   Route& R = *reinterpret_cast<Route*>(smem);
   float* s_gu2 = reinterpret_cast<float*>(smem + sizeof(Route));  // [2][kMaxTok][64]
@@ -234,22 +262,32 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
   uint8_t* tile = act + a.act_bytes + wid * a.tile_bytes;
 
   const int U = (int)(a.hidden / 32);      // 32-element units per row (multiple of 64)
-  const int tokb = act_token_bytes(U);
+  const int tokb = S16 ? act16_token_bytes(U) : act_token_bytes(U);
   // Activations of every token (the router launch's Q8 codes of x), staged
   // once per workgroup: token t at act + t * tokb. The loads are issued
   // before the routing's logit loads so both round trips overlap.
   constexpr int kStage = 2;  // (token, unit) tasks per thread: m * U <= 2048
-  int4 st_lo[kStage], st_hi[kStage];
+  constexpr int kStW = S16 ? 16 : 8;  // dwords of codes per unit
+  uint32_t st_c[kStage][kStW];
   float st_d[kStage];
+  int st_s[kStage];
 #pragma unroll
   for (int r = 0; r < kStage; ++r) {
     const int i = threadIdx.x + r * kUpWaves * 64;
     if (i < a.m * U) {
       const int t = i / U, u = i - t * U;
-      const int4* xr = reinterpret_cast<const int4*>(a.xq + (int64_t)t * a.hidden);
-      st_lo[r] = xr[2 * u];
-      st_hi[r] = xr[2 * u + 1];
+      const int4* xr = S16 ? reinterpret_cast<const int4*>(a.xq16 + (int64_t)t * a.hidden + 32 * u)
+                           : reinterpret_cast<const int4*>(a.xq + (int64_t)t * a.hidden + 32 * u);
+#pragma unroll
+      for (int v = 0; v < kStW / 4; ++v) {
+        const int4 q = xr[v];
+        st_c[r][4 * v + 0] = (uint32_t)q.x;
+        st_c[r][4 * v + 1] = (uint32_t)q.y;
+        st_c[r][4 * v + 2] = (uint32_t)q.z;
+        st_c[r][4 * v + 3] = (uint32_t)q.w;
+      }
       st_d[r] = a.dx[(int64_t)t * U + u];
+      if constexpr (S16) st_s[r] = a.sx[(int64_t)t * U + u];
     }
   }
   build_route<NPL>(R, a.logits, a.n_experts, a.top_k, a.m, wid, lane, blockDim.x);
@@ -259,13 +297,24 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
     if (i < a.m * U) {
       const int t = i / U, u = i - t * U;
       uint8_t* tok = act + t * tokb;
-      const int ones = 0x01010101;
-      const int4 lo = st_lo[r], hi = st_hi[r];
-      const int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
-      const int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
-      *reinterpret_cast<int4*>(tok + 16 * u) = lo;
-      *reinterpret_cast<int4*>(tok + 16 * U + 16 * u) = hi;
-      *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) = make_int2(__float_as_int(st_d[r]), (sa & 0xffff) | (sb << 16));
+      if constexpr (S16) {
+        // paired codes of the unit, then (scale, code sum)
+        uint32_t pr[16];
+        pair16(st_c[r], pr);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<u32x4*>(tok + 64 * u + 16 * v) = u32x4{pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
+        *reinterpret_cast<int2*>(tok + 64 * U + 8 * u) = make_int2(__float_as_int(st_d[r]), st_s[r]);
+      } else {
+        const int ones = 0x01010101;
+        const int4 lo = make_int4((int)st_c[r][0], (int)st_c[r][1], (int)st_c[r][2], (int)st_c[r][3]);
+        const int4 hi = make_int4((int)st_c[r][4], (int)st_c[r][5], (int)st_c[r][6], (int)st_c[r][7]);
+        const int sa = dot4(lo.x, ones, dot4(lo.y, ones, dot4(lo.z, ones, dot4(lo.w, ones, 0))));
+        const int sb = dot4(hi.x, ones, dot4(hi.y, ones, dot4(hi.z, ones, dot4(hi.w, ones, 0))));
+        *reinterpret_cast<int4*>(tok + 16 * u) = lo;
+        *reinterpret_cast<int4*>(tok + 16 * U + 16 * u) = hi;
+        *reinterpret_cast<int2*>(tok + 32 * U + 8 * u) = make_int2(__float_as_int(st_d[r]), (sa & 0xffff) | (sb << 16));
+      }
     }
   }
   __syncthreads();
@@ -361,8 +410,16 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
         const int sub = u % F::kUPB;
         const typename F::W w = F::load(tile, base + uoff, sub, cbr);
 #pragma unroll
-        for (int t = 0; t < kUpTok; ++t)
-          if (t0 + t < c) acc[t] = F::fma(w, load_act(act + tok[t] * tokb, U, u), acc[t]);
+        for (int t = 0; t < kUpTok; ++t) {
+          if (t0 + t < c) {
+            if constexpr (S16) {
+              const Act16 x = load_act16(act + tok[t] * tokb, U, u);
+              acc[t] = fmaf((float)(q4_dot16(w.q, x.p) - 8 * x.sum), x.dx * w.d, acc[t]);
+            } else {
+              acc[t] = F::fma(w, load_act(act + tok[t] * tokb, U, u), acc[t]);
+            }
+          }
+        }
       }
 #pragma unroll
       for (int t = 0; t < kUpTok; ++t) {
@@ -393,9 +450,15 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
       float amax = max8(fabsf(h));
       amax = fmaxf(amax, dpp<0x140>(amax));           // 16 lanes (row_mirror)
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));  // 32 lanes
-      const float d = (amax > 0.0f) ? amax / 127.0f : 0.0f;
-      const int q = d != 0.0f ? q8_code(h, d, __builtin_amdgcn_rcpf(d)) : 0;
-      a.hq[row * a.inter + col] = (int8_t)q;
+      const float d = (amax > 0.0f) ? amax / (S16 ? 32767.0f : 127.0f) : 0.0f;
+      int q;
+      if constexpr (S16) {
+        q = d != 0.0f ? code16(h, d) : 0;
+        a.hq16[row * a.inter + col] = (int16_t)q;
+      } else {
+        q = d != 0.0f ? q8_code(h, d, __builtin_amdgcn_rcpf(d)) : 0;
+        a.hq[row * a.inter + col] = (int8_t)q;
+      }
       int qs = sum4(q);
       qs += other_quad(qs);
       qs += dpp_i<0x140>(qs);        // 16 lanes
@@ -414,10 +477,12 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
 
 // ---------------------------------------------------------- down + combine --
 
-// LPR: lanes per row (units of h per row, <= 64); JU: units per lane.
-template <int FMT, int LPR, int JU>
+// LPR: lanes per row (units of h per row, <= 64); JU: units per lane; S16:
+// 16-bit codes of h (Q4_0 experts).
+template <int FMT, int LPR, int JU, bool S16>
 __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
   using F = typename FmtOf<FMT>::T;
+  static_assert(!S16 || FMT == kQ4_0, "16-bit activations are for Q4_0 experts");
   extern __shared__ __align__(16) uint8_t smem[];
   const int S1 = a.top_k + 1;
   const int RB = a.dn_rows;                         // output rows per item (multiple of 64 / LPR)
@@ -486,14 +551,29 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
     // The slot's re-quantized h (requested before the next item's weights,
     // so waiting for it never waits for them): this lane's units lam + LPR jj.
     const int64_t hrow = (int64_t)t * S1 + s;
-    Act x[JU];
+    std::conditional_t<S16, Act16, Act> x[JU];
 #pragma unroll
     for (int jj = 0; jj < JU; ++jj) {
       const int u = lam + LPR * jj;
-      const int4 lo = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u];
-      const int4 hi = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u + 1];
-      x[jj].x[0] = lo.x; x[jj].x[1] = lo.y; x[jj].x[2] = lo.z; x[jj].x[3] = lo.w;
-      x[jj].x[4] = hi.x; x[jj].x[5] = hi.y; x[jj].x[6] = hi.z; x[jj].x[7] = hi.w;
+      if constexpr (S16) {
+        const int4* hp = reinterpret_cast<const int4*>(a.hq16 + hrow * a.inter + 32 * u);
+        uint32_t w16[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int4 q = hp[v];
+          w16[4 * v + 0] = (uint32_t)q.x;
+          w16[4 * v + 1] = (uint32_t)q.y;
+          w16[4 * v + 2] = (uint32_t)q.z;
+          w16[4 * v + 3] = (uint32_t)q.w;
+        }
+        pair16(w16, x[jj].p);
+        x[jj].sum = a.hs[hrow * U + u];
+      } else {
+        const int4 lo = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u];
+        const int4 hi = reinterpret_cast<const int4*>(a.hq + hrow * a.inter)[2 * u + 1];
+        x[jj].x[0] = lo.x; x[jj].x[1] = lo.y; x[jj].x[2] = lo.z; x[jj].x[3] = lo.w;
+        x[jj].x[4] = hi.x; x[jj].x[5] = hi.y; x[jj].x[6] = hi.z; x[jj].x[7] = hi.w;
+      }
       x[jj].dx = a.hd[hrow * U + u];
     }
 #pragma unroll
@@ -502,11 +582,13 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
       if (ch < nch) *reinterpret_cast<u32x4*>(tile + 16 * ch) = buf[i];
     }
     issue(buf, item + gridDim.x);
+    if constexpr (!S16) {
 #pragma unroll
-    for (int jj = 0; jj < JU; ++jj) {
-      const int ones = 0x01010101;
-      x[jj].sa = dot4(x[jj].x[0], ones, dot4(x[jj].x[1], ones, dot4(x[jj].x[2], ones, dot4(x[jj].x[3], ones, 0))));
-      x[jj].sb = dot4(x[jj].x[4], ones, dot4(x[jj].x[5], ones, dot4(x[jj].x[6], ones, dot4(x[jj].x[7], ones, 0))));
+      for (int jj = 0; jj < JU; ++jj) {
+        const int ones = 0x01010101;
+        x[jj].sa = dot4(x[jj].x[0], ones, dot4(x[jj].x[1], ones, dot4(x[jj].x[2], ones, dot4(x[jj].x[3], ones, 0))));
+        x[jj].sb = dot4(x[jj].x[4], ones, dot4(x[jj].x[5], ones, dot4(x[jj].x[6], ones, dot4(x[jj].x[7], ones, 0))));
+      }
     }
     const uint32_t base = (uint32_t)(b0 - a0);
     for (int p = 0; p * RPP < nrows; ++p) {
@@ -519,7 +601,10 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
         const int u = lam + LPR * jj;
         const typename F::W w =
             F::load(tile, base + (uint32_t)(rl * a.rb_dn) + (uint32_t)((u / F::kUPB) * F::kBB), u % F::kUPB, cbr);
-        acc = F::fma(w, x[jj], acc);
+        if constexpr (S16)
+          acc = fmaf((float)(q4_dot16(w.q, x[jj].p) - 8 * x[jj].sum), x[jj].dx * w.d, acc);
+        else
+          acc = F::fma(w, x[jj], acc);
       }
       const float sum = group_sum(acc, LPR);
       if (lam == 0 && valid) s_out[s * RB + rl] = sum;
@@ -544,9 +629,9 @@ size_t up_lds(const MoeFusedArgs& a) {
          (size_t)kUpWaves * a.tile_bytes;
 }
 
-template <int FMT, int LPL, int NPL>
+template <int FMT, int LPL, int NPL, bool S16>
 hipError_t launch_up_t(const MoeFusedArgs& a, int n_items_max, hipStream_t s) {
-  auto kern = moe_up_kernel<FMT, LPL, NPL>;
+  auto kern = moe_up_kernel<FMT, LPL, NPL, S16>;
   const size_t lds = up_lds(a);
   int per_cu = 0, cus = 0;
   hipError_t e = kernel_residency(reinterpret_cast<const void*>(kern), kUpWaves * 64, lds, true, &per_cu, &cus);
@@ -561,12 +646,14 @@ hipError_t launch_up_t(const MoeFusedArgs& a, int n_items_max, hipStream_t s) {
 // Loads per lane for a wave's four rows of rb bytes (plus alignment).
 int up_loads(int64_t rb) { return (int)((kUpRows * rb + 32 + 1023) / 1024); }
 
-template <int FMT>
+template <int FMT, bool S16 = false>
 hipError_t launch_up_npl(const MoeFusedArgs& a, int n_items_max, hipStream_t s) {
   const bool small = up_loads(a.rb_gu) <= 5;
   if (a.n_experts <= 256)
-    return small ? launch_up_t<FMT, 5, 4>(a, n_items_max, s) : launch_up_t<FMT, kUpLPL, 4>(a, n_items_max, s);
-  return small ? launch_up_t<FMT, 5, 16>(a, n_items_max, s) : launch_up_t<FMT, kUpLPL, 16>(a, n_items_max, s);
+    return small ? launch_up_t<FMT, 5, 4, S16>(a, n_items_max, s)
+                 : launch_up_t<FMT, kUpLPL, 4, S16>(a, n_items_max, s);
+  return small ? launch_up_t<FMT, 5, 16, S16>(a, n_items_max, s)
+               : launch_up_t<FMT, kUpLPL, 16, S16>(a, n_items_max, s);
 }
 
 // Output rows per down item: a.dn_rows or twice that when a wave's rows
@@ -577,9 +664,9 @@ hipError_t launch_up_npl(const MoeFusedArgs& a, int n_items_max, hipStream_t s) 
 // per layer; 8 rows stay best where a round more would be needed).
 constexpr int kDnItemRows = 8;
 
-template <int FMT, int LPR, int JU>
+template <int FMT, int LPR, int JU, bool S16 = false>
 hipError_t launch_dn_t(MoeFusedArgs a, hipStream_t s) {
-  auto kern = moe_down_kernel<FMT, LPR, JU>;
+  auto kern = moe_down_kernel<FMT, LPR, JU, S16>;
   const int S1 = a.top_k + 1;
   const int rows0 = a.dn_rows;
   int64_t best_cost = -1, best_grid = 0;
@@ -615,13 +702,16 @@ bool moe_fused_ok(const MoeCall& c) {
   if (rb_gu <= 0 || rb_dn <= 0) return false;
   const int64_t U = c.inter / 32;
   if (c.m < 1 || c.m > kFusedMaxTok || c.top_k < 1 || c.top_k > 15 || c.n_experts > kMaxExperts) return false;
+  const bool s16 = c.xq16 != nullptr;
+  if (s16 && (c.fmt != kQ4_0 || !c.hq16 || !c.sx || !c.hs)) return false;
   if (c.hidden % 2048 || c.hidden > 8192 || c.inter % 32 || c.m * (c.hidden / 32) > 2048) return false;
   if (U != 16 && U != 32 && U != 64 && U != 128) return false;
   if (up_loads(rb_gu) > kUpLPL || rb_gu % 16) return false;   // a wave's four rows in one load
   const int rpp = 64 / (int)(U < 64 ? U : 64);
   const int rows = rpp * 2 > 8 ? rpp * 2 : 8;
   if (rows * rb_dn + 32 > (int64_t)kDnLPL * 1024) return false;
-  const size_t up = sizeof(Route) + (size_t)kUpSgu + (size_t)c.m * act_token_bytes((int)(c.hidden / 32)) +
+  const int tokb = s16 ? act16_token_bytes((int)(c.hidden / 32)) : act_token_bytes((int)(c.hidden / 32));
+  const size_t up = sizeof(Route) + (size_t)kUpSgu + (size_t)c.m * tokb +
                     (size_t)kUpWaves * (size_t)((kUpRows * (rb_gu + kPad) + 32 + 15) / 16 * 16 + 16);
   return up <= (size_t)kLdsBytes;
 }
@@ -642,7 +732,9 @@ hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
   a.gu_stride = c.gu_stride;
   a.dn_stride = c.dn_stride;
   a.xq = c.xq;
+  a.xq16 = c.xq16;
   a.dx = c.dx;
+  a.sx = c.sx;
   a.hidden = c.hidden;
   a.inter = c.inter;
   a.rb_gu = fmt_row_bytes(c.fmt, c.hidden);
@@ -650,11 +742,13 @@ hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
   a.gu_out = c.gu_out;
   a.h_out = c.h;
   a.hq = c.hq;
+  a.hq16 = c.hq16;
   a.hd = c.hd;
   a.hs = c.hs;
   a.y = c.y;
   for (int i = 0; i < 4; ++i) a.cb[i] = c.cb[i];
-  a.act_bytes = c.m * act_token_bytes((int)(c.hidden / 32));
+  const bool s16 = c.xq16 != nullptr;  // Q4_0 experts (moe_fused_ok)
+  a.act_bytes = c.m * (s16 ? act16_token_bytes((int)(c.hidden / 32)) : act_token_bytes((int)(c.hidden / 32)));
   a.tile_bytes = (int)((kUpRows * (a.rb_gu + kPad) + 32 + 15) / 16 * 16 + 16);
   const int U = (int)(c.inter / 32);
   const int rpp = 64 / (U < 64 ? U : 64);
@@ -662,6 +756,15 @@ hipError_t launch_moe_fused(const MoeCall& c, hipStream_t s) {
   // Entries: at most one per (token, slot) pair, plus the shared expert's.
   const int n_items_max = (c.m * c.top_k + (c.m + kShareTok - 1) / kShareTok) * (int)(c.inter / 32);
   hipError_t e;
+  if (s16) {
+    if ((e = launch_up_npl<kQ4_0, true>(a, n_items_max, s)) != hipSuccess) return e;
+    switch (U) {
+      case 16: return launch_dn_t<kQ4_0, 16, 1, true>(a, s);
+      case 32: return launch_dn_t<kQ4_0, 32, 1, true>(a, s);
+      case 64: return launch_dn_t<kQ4_0, 64, 1, true>(a, s);
+      default: return launch_dn_t<kQ4_0, 64, 2, true>(a, s);
+    }
+  }
   switch (c.fmt) {
     case kQ4_0: e = launch_up_npl<kQ4_0>(a, n_items_max, s); break;
     case kQ8_0: e = launch_up_npl<kQ8_0>(a, n_items_max, s); break;

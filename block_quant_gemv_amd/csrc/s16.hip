@@ -22,6 +22,7 @@
 // y += dx * (d * sc) * D - dx * (dmin * m) * sum(x16).
 #include "common.cuh"
 #include "internal.h"
+#include "s16.cuh"
 #include "s16.h"
 
 namespace qg {
@@ -30,17 +31,6 @@ namespace {
 
 constexpr int kWaves16 = 4;
 constexpr int kBuf3 = 0x00020000;  // raw buffer resource, gfx9 family
-
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-
-QG_DEV int dot2(uint32_t a, uint32_t b, int c) {
-  return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), c, false);
-}
-
-QG_DEV int code16(float x, float d) {
-  const float q = fminf(fmaxf(roundf(x / d), -32767.0f), 32767.0f);
-  return (int)q;
-}
 
 // Eight lanes per block, four elements each (one 128-bit load).
 __global__ __launch_bounds__(256) void quant_s16_kernel(const float* __restrict__ x, int16_t* __restrict__ xq,

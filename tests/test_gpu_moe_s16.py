@@ -28,7 +28,12 @@ def _inputs(E, H, I, seed):
     return wr, gu_all, dn_all, gu_sh, dn_sh
 
 
-@pytest.mark.parametrize("E,H,I,K,m", [(256, 2048, 512, 8, 1), (256, 2048, 512, 8, 16),
+# Shapes: the decode workload at 1, 4, 12 and 16 tokens (the two-launch
+# expert stage up to 13 tokens at hidden 2048, where its LDS holds the staged
+# 16-bit codes; six launches at 16), intermediate 1024 through the two-launch
+# stage, and small shapes through the six launches.
+@pytest.mark.parametrize("E,H,I,K,m", [(256, 2048, 512, 8, 1), (256, 2048, 512, 8, 4), (256, 2048, 512, 8, 12),
+                                        (256, 2048, 512, 8, 16), (64, 2048, 1024, 8, 3),
                                         (16, 1024, 512, 4, 5), (8, 512, 1024, 8, 2)])
 def test_moe_s16_staged(E, H, I, K, m):
     say(f"moe s16 E={E} H={H} I={I} top{K} m={m}")
