@@ -393,8 +393,10 @@ LEGS = ("ffn", "lm_head", "q4_0_2048", "q5_k_iq4_xs", "s16", "f32act", "m32", "m
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 400 steps are about 27 ms of timed work: long enough that the clocks'
+    # response to the burst and the replays' start-up are a small part of it
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-clocks", action="store_true")
