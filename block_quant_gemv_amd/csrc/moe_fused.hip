@@ -263,9 +263,9 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
 
   const int U = (int)(a.hidden / 32);      // 32-element units per row (multiple of 64)
   const int tokb = S16 ? act16_token_bytes(U) : act_token_bytes(U);
-  // Activations of every token (the router launch's Q8 codes of x), staged
-  // once per workgroup: token t at act + t * tokb. The loads are issued
-  // before the routing's logit loads so both round trips overlap.
+  // Activations of every token (the router launch's Q8 or 16-bit codes of
+  // x), staged once per workgroup: token t at act + t * tokb. The loads are
+  // issued before the routing's logit loads so both round trips overlap.
   constexpr int kStage = 2;  // (token, unit) tasks per thread: m * U <= 2048
   constexpr int kStW = S16 ? 16 : 8;  // dwords of codes per unit
   uint32_t st_c[kStage][kStW];
