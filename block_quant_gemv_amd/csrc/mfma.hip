@@ -183,9 +183,8 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
 
   // Weights two super-blocks ahead in registers (double buffer); the
   // activation operands of a super-block are requested when its step starts,
-  // before the weights two ahead (loads return in order, so waiting for the
-  // activations never waits for those weights), and other waves on the SIMD
-  // cover their L2 latency.
+  // and the weights two ahead at its end, and other waves on the SIMD cover
+  // the L2 latency of the activations.
   u32x4 bufA[G::LPL], bufB[G::LPL];
   issue(bufA, sb_begin);
   issue(bufB, sb_begin + 1);
@@ -198,8 +197,8 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
     }
   }
   // One super-block: its weights from the registers to the wave's LDS tile,
-  // its activations and the weights two ahead requested, then the products
-  // from the tile.
+  // its activations requested, the products from the tile, then the weights
+  // two ahead requested into the freed registers.
   auto step = [&](int sb, u32x4 (&buf)[G::LPL]) __attribute__((always_inline)) {
     const int bl0 = (sb - sb_begin) * 8;         // wave-local block of the first group
     __builtin_amdgcn_wave_barrier();  // the previous super-block's tile reads are done
@@ -207,7 +206,6 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
     long act[8][2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_act((int64_t)sb * 8 + j, act[j][0], act[j][1]);
-    issue(buf, sb + 2);
     __builtin_amdgcn_wave_barrier();  // the tile is written before any lane reads it
     const uint32_t base = (uint32_t)(col * G::PITCH) + (uint32_t)(((int64_t)col * rb + (int64_t)sb * BB) & 15);
     v4f accs0 = {0.f, 0.f, 0.f, 0.f}, accs1 = {0.f, 0.f, 0.f, 0.f};
@@ -336,6 +334,9 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
         }
       }
     }
+    // The weights two ahead, requested once this super-block's products
+    // are done (Q6_K 4096 x 12288: 22.6 -> 21.9 us per kernel; Q4_K the same).
+    issue(buf, sb + 2);
     };
   for (int sb = sb_begin; sb < sb_end; sb += 2) {
     step(sb, bufA);
