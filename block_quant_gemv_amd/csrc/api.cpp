@@ -30,7 +30,7 @@ using namespace qg;
 struct qgemv_plan {
   qgemv_desc d;
   int8_t cb[16];
-  uint32_t cbw[4];
+  uint32_t cbw[4];  // cb as the device's two byte-permute pools (codebook_pools)
 };
 
 namespace {
@@ -52,6 +52,39 @@ bool is_block_fmt(int f) { return f >= QFMT_Q4_0 && f <= QFMT_IQ4_XS; }
 bool has_codebook(int f) { return f == QFMT_IQ4_NL || f == QFMT_IQ4_XS; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Byte-permute pools of a 16-entry int8 codebook T for the device lookup:
+// pool L (words 0, 1) answers codes 0..7 at selector n, pool H (words 2, 3)
+// codes 8..15 at selector n ^ 8, and the device takes the xor of the two
+// permutes. A selector in 8..15 makes the permute yield a fill byte: the
+// sign of pool byte 1, 3, 5 or 7 spread over the byte for 8..11, 0x00 for
+// 12, 0xFF for 13..15. Each pool byte is stored xor-ed with the fill that
+// its code meets in the other pool. The fills of 8..11 depend on pool bytes
+// computed here; those chains end at bytes 4..7 (constant fills) within
+// three links, so four sweeps settle every byte. The final loop decodes all
+// 16 codes the way the device does and checks them against T.
+bool codebook_pools(const int8_t* T, uint32_t* w) {
+  uint8_t L[8] = {0}, H[8] = {0};
+  auto fill = [](const uint8_t* pool, int sel) -> uint8_t {  // sel in 8..15
+    if (sel >= 13) return 0xFF;
+    if (sel == 12) return 0x00;
+    return (pool[2 * (sel - 8) + 1] & 0x80u) ? 0xFF : 0x00;
+  };
+  for (int sweep = 0; sweep < 4; ++sweep)
+    for (int n = 0; n < 8; ++n) {
+      L[n] = (uint8_t)((uint8_t)T[n] ^ fill(H, n + 8));      // code n: H's selector is n + 8
+      H[n] = (uint8_t)((uint8_t)T[n + 8] ^ fill(L, n + 8));  // code n + 8: L's selector is n + 8
+    }
+  for (int c = 0; c < 16; ++c) {
+    const int hs = c ^ 8;
+    const uint8_t lo = c < 8 ? L[c] : fill(L, c);
+    const uint8_t hi = hs < 8 ? H[hs] : fill(H, hs);
+    if ((int8_t)(lo ^ hi) != T[c]) return false;
+  }
+  memcpy(w, L, 8);
+  memcpy(w + 2, H, 8);
+  return true;
+}
 
 // Named regions of a workspace, in order, each 256-byte aligned.
 struct Region { const char* name; size_t bytes; };
@@ -224,7 +257,10 @@ int qgemv_create(qgemv_t* out, const qgemv_desc* d) {
         delete p;
         return fail(QGEMV_EINVAL, "the codebook must be strictly ascending");
       }
-    memcpy(p->cbw, p->cb, 16);
+    if (!codebook_pools(p->cb, p->cbw)) {
+      delete p;
+      return fail(QGEMV_EINVAL, "internal error: codebook pools do not decode");
+    }
   }
   *out = p;
   return QGEMV_OK;

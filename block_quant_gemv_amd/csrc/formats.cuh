@@ -89,22 +89,19 @@ struct FmtQ8_0 {
   static constexpr int kDotsPerUnit = 1;
 };
 
-// 4 codebook indices (one per byte, 0..15) -> 4 int8 codebook values.
-// Entries 0..7 come from {cb1:cb0}, 8..15 from {cb3:cb2}; bit 3 of each
-// index then picks between the two candidates with a third byte permute.
-// cb[4] holds the identity selector 0x03020100 in a register, so the pick
-// is one and-or (a register operand instead of a second literal).
-// b3 holds bit 3 of each index at bit 2 of its byte (any other bits of b3
-// are ignored).
-QG_DEV uint32_t cb_lookup4(uint32_t sel7, uint32_t b3, const uint32_t* cb) {
-  const uint32_t lo = perm(cb[1], cb[0], sel7);
-  const uint32_t hi = perm(cb[3], cb[2], sel7);
-  return perm(hi, lo, (b3 & 0x04040404u) | cb[4]);
-}
-// The 8 indices of one dword of packed nibbles (low nibbles, then high).
+// Codebook lookup of the 8 nibble codes of one dword (low nibbles -> vlo,
+// high nibbles -> vhi, byte i of each from byte i of q). cb holds two
+// 8-byte pools built by the host: L (cb[0], cb[1]) serves codes 0..7 at
+// byte-permute selector n, H (cb[2], cb[3]) codes 8..15 at selector n ^ 8,
+// and the entry is the xor of the two permutes. For a code of the other
+// half a selector lands in 8..15, where the permute yields a fill byte
+// (sign of pool byte 1/3/5/7, 0x00, or 0xFF) instead of a pool byte; every
+// pool byte is stored xor-ed with the fill its code meets in the other pool.
+// Two permutes and an xor per four codes, no bit-3 pick.
 QG_DEV void cb_lookup8(uint32_t q, const uint32_t* cb, uint32_t& vlo, uint32_t& vhi) {
-  vlo = cb_lookup4(q & 0x07070707u, q >> 1, cb);
-  vhi = cb_lookup4((q >> 4) & 0x07070707u, q >> 5, cb);
+  const uint32_t s0 = q & 0x0F0F0F0Fu, s1 = (q >> 4) & 0x0F0F0F0Fu;
+  vlo = perm(cb[1], cb[0], s0) ^ perm(cb[3], cb[2], s0 ^ 0x08080808u);
+  vhi = perm(cb[1], cb[0], s1) ^ perm(cb[3], cb[2], s1 ^ 0x08080808u);
 }
 
 struct FmtIQ4_NL {

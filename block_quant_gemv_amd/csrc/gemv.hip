@@ -325,12 +325,12 @@ __global__ __launch_bounds__(waves_per_wg<FUSEQ>() * 64) void gemv_kernel(const 
                                      FUSEQ && p.xq_out && blockIdx.x == 0 && (!p.tbl || shared), pre);
   __syncthreads();
 
-  // Codebook words plus the identity byte selector, pinned in registers
-  // (opaque values): the byte permutes and the pick's and-or then take them
-  // as register operands without re-copying them from scalar registers.
-  uint32_t cbr[5] = {p.cb[0], p.cb[1], p.cb[2], p.cb[3], 0x03020100u};
+  // Codebook pool words, pinned in registers (opaque values): the byte
+  // permutes then take them as register operands without re-copying them
+  // from scalar registers.
+  uint32_t cbr[4] = {p.cb[0], p.cb[1], p.cb[2], p.cb[3]};
 #pragma unroll
-  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(cbr[i]));
 
   float acc[P][MT];
 #pragma unroll

@@ -52,7 +52,7 @@ struct GemvProblem {
   int64_t n = 0;
   int64_t k = 0;
   int m = 1;
-  uint32_t cb[4] = {0, 0, 0, 0};  // IQ4_NL codebook, 16 int8 little-endian
+  uint32_t cb[4] = {0, 0, 0, 0};  // IQ4_NL / IQ4_XS codebook as two byte-permute pools
   const int32_t* tbl = nullptr;
   int tbl_stride = 0;
   int nprob = 1;

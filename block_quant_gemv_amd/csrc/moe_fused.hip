@@ -328,9 +328,9 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
   const int tiles = (int)(a.inter / 32);
   const int n_items = R.n_entries * tiles;
   const int S1 = a.top_k + 1;
-  uint32_t cbr[5] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3], 0x03020100u};
+  uint32_t cbr[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
 #pragma unroll
-  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(cbr[i]));
 
   // The byte range of this wave's four rows of an item: virtual rows
   // 4 wid .. 4 wid + 3 (0..31 gate, 32..63 up), contiguous in the matrix.
@@ -501,9 +501,9 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(const MoeFusedArgs a) {
   const int U = (int)(a.inter / 32);
   const int nblk = (int)((a.hidden + RB - 1) / RB);
   const int n_items = a.m * nblk;
-  uint32_t cbr[5] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3], 0x03020100u};
+  uint32_t cbr[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
 #pragma unroll
-  for (int i = 0; i < 5; ++i) asm volatile("" : "+v"(cbr[i]));
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(cbr[i]));
   // The routing (expert ids and weights of every pair) to LDS once: items
   // then find their experts and combine weights without global-memory
   // round trips (measured: 8 tokens 40.7 -> 39.3 us per layer). Requesting

@@ -211,3 +211,39 @@ def test_full_size_every_row_and_block_dots(fmt, n):
     say(f"  normwise error {e:.3e}, max per-row relative {rowrel.max():.2e}")
     assert e <= TOL
     assert rowrel.max() <= 1e-4
+
+
+# --------------------------------------------------------- codebooks --
+# The device looks a code up in two byte-permute pools that the library
+# derives from the codebook; the pools depend on the signs of the entries.
+# Codebooks of every sign pattern: all negative, all non-negative, the int8
+# ends -128 and 127, sign change at each position of the first half, and
+# random ones.
+def _codebooks():
+    out = [np.arange(-128, -112, dtype=np.int8), np.arange(0, 16, dtype=np.int8),
+           np.array([-128, -127] + list(range(-5, 8)) + [127], np.int8)]
+    for neg in (1, 3, 5, 7, 9, 12, 15):
+        out.append(np.array(list(range(-neg, 0)) + list(range(1, 17 - neg)), np.int8))
+    out += [synth.codebook(s) for s in (1, 2, 3)]
+    return out
+
+
+@pytest.mark.parametrize("fmt", CB_FORMATS)
+def test_codebook_sign_patterns(fmt):
+    n, k, m = 96, 512, 2
+    w = synth.weights(fmt, n, k, seed=31)
+    x = synth.activations(32, m, k)
+    xq, dx, _ = quantize_q8(x)
+    for i, cb in enumerate(_codebooks()):
+        say(f"codebook {i} {fmt}: {cb.tolist()}")
+        assert np.all(np.diff(cb.astype(np.int32)) > 0)
+        g = qg.GEMV(fmt, n, k, max_m=m, codebook=cb)
+        wd = dev(w)
+        y = torch.empty(m, n, dtype=torch.float32, device="cuda")
+        g.run(wd, dev(x), y)
+        dots = g.block_dots(wd, dev(xq))
+        torch.cuda.synchronize()
+        ref_dots = og.block_dots(fmt, w, n, k, xq, cb)
+        bad = np.argwhere(host(dots) != ref_dots)
+        assert bad.size == 0, f"codebook {i}: {len(bad)} block dots differ, first {bad[:3].tolist()}"
+        assert normwise(host(y), og.gemv_dequant(fmt, w, n, k, xq, dx, cb)) <= TOL
