@@ -121,6 +121,27 @@ QG_DEV float group_sum(float v, int width) {
   return v;
 }
 
+// Totals of four rows over a whole wave: each lane holds a partial value of
+// rows 0..3 in a0..a3; on return the lanes with l % 4 == r hold row r's
+// total. Two exchanges halve the values per lane (lane pairs: odd lanes keep
+// rows 1 and 3; then lane quads: lanes with bit 1 set keep rows 2 and 3),
+// two row rotations add the lanes of a 16-lane row that hold the same row,
+// and two half swaps add the four 16-lane rows. The order of the additions
+// is fixed.
+QG_DEV float rows4_wave_sum(float a0, float a1, float a2, float a3, int lane) {
+  const bool odd = lane & 1;
+  const float b0 = (odd ? a1 : a0) + dpp<0xB1>(odd ? a0 : a1);  // quad_perm [1,0,3,2]
+  const float b1 = (odd ? a3 : a2) + dpp<0xB1>(odd ? a2 : a3);
+  const bool hi = lane & 2;
+  float c = (hi ? b1 : b0) + dpp<0x4E>(hi ? b0 : b1);  // quad_perm [2,3,0,1]
+  c += dpp<0x124>(c);                                  // row_ror:4
+  c += dpp<0x128>(c);                                  // row_ror:8
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  c = __uint_as_float(h[0]) + __uint_as_float(h[1]);  // lanes l and l ^ 32
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);  // 16-lane rows 2i and 2i + 1
+}
+
 QG_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

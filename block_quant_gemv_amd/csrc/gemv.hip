@@ -406,15 +406,25 @@ __global__ __launch_bounds__(waves_per_wg<FUSEQ>() * 64) void gemv_kernel(const 
       for (int t = 0; t < MT; ++t) {
         if (t < mcnt) {
           float outv = 0.0f;
+          auto per_row = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp) {
-            const float sum = group_sum(acc[pp][t], LPR);
-            float v;
-            if (RPP == 1) v = sum;
-            else v = __shfl(sum, (lane & (RPP - 1)) << lpr_log, kWave);
-            if ((lane >> rpp_log) == pp) outv = v;
-            acc[pp][t] = 0.0f;
+            for (int pp = 0; pp < P; ++pp) {
+              const float sum = group_sum(acc[pp][t], LPR);
+              float v;
+              if (RPP == 1) v = sum;
+              else v = __shfl(sum, (lane & (RPP - 1)) << lpr_log, kWave);
+              if ((lane >> rpp_log) == pp) outv = v;
+            }
+          };
+          if constexpr (P == 4) {
+            // A whole wave per row: the four rows are reduced together.
+            if (LPR == kWave) outv = rows4_wave_sum(acc[0][t], acc[1][t], acc[2][t], acc[3][t], lane);
+            else per_row();
+          } else {
+            per_row();
           }
+#pragma unroll
+          for (int pp = 0; pp < P; ++pp) acc[pp][t] = 0.0f;
           if (lane < nrows) p.y[(int64_t)out_row(t) * p.ldy + r0 + lane] = outv;
         }
       }
