@@ -65,9 +65,14 @@ QG_DEV uint32_t lds_u16(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint16_t*>(base + off);
 }
 
+// Lane values moved by a DPP pattern. Every pattern used here (quad
+// permutes, row mirrors, row rotations) gives every lane a source lane, so
+// the bound_ctrl / old-value choice never applies; setting bound_ctrl with a
+// zero old value lets the compiler fold the move into a following add
+// (v_add_*_dpp).
 template <int CTRL>
 QG_DEV float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
 // Sum over aligned groups of `width` lanes, width a power of two <= 16; every
@@ -84,7 +89,7 @@ QG_DEV float group_sum16(float v, int width) {
 
 template <int CTRL>
 QG_DEV int dpp_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
 }
 
 // Reductions over aligned groups of 8 lanes (one 32-element block, 4
