@@ -17,7 +17,9 @@
 //   D (16 x 16): D[4 g + i][l % 16], i < 4
 // so each lane owns one weight row (its scale fields are per-lane values)
 // and four tokens of each 16-token half. Q4_K's min term, sum_j (dx s)[t][j]
-// m_j[n], is one fp32 FMA per output and sub-block next to the scale step.
+// m_j[n], is a real contraction over sub-blocks: two fp32 matrix-core
+// products (v_mfma_f32_16x16x4f32) per super-block and token half, added
+// straight into the accumulators.
 //
 // Work: a workgroup owns 16 weight rows for all 32 tokens and splits K over
 // its waves; each wave streams its own super-blocks (16 row segments read
@@ -50,7 +52,6 @@ template <int FMT> struct Geo {
   static constexpr int PITCH = 16 * NCH;                     // LDS row pitch: an odd number of 16-byte units
   static constexpr int LPL = (kRows * NCH + 63) / 64;        // loads per lane per super-block
   static constexpr int TILE = kRows * PITCH;                 // LDS bytes of one wave's tile
-  static constexpr int NST = FMT == kQ4_K ? 2 : 1;           // staged per-block floats per token (dx, dx * s)
 };
 
 QG_DEV long pack2(uint32_t lo, uint32_t hi) { return (long)(((uint64_t)hi << 32) | lo); }
@@ -64,7 +65,7 @@ QG_DEV uint32_t minus32(uint32_t q) { return ((q | 0x80808080u) - 0x20202020u) ^
 template <int FMT>
 struct WaveLds {
   __host__ __device__ static size_t bytes(int spw) {
-    return (size_t)Geo<FMT>::TILE + (size_t)spw * 8 * kMT * 4 * Geo<FMT>::NST;
+    return (size_t)Geo<FMT>::TILE + (size_t)spw * 8 * kMT * 4;
   }
 };
 
@@ -93,7 +94,6 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
   const size_t wave_bytes = WaveLds<FMT>::bytes(spw);
   uint8_t* tile = lds + (size_t)wid * wave_bytes;
   float* s_dx = reinterpret_cast<float*>(tile + G::TILE);   // [local block][token]
-  float* s_c = s_dx + spw * 8 * kMT;                        // Q4_K: dx * s
 
   // Weights of the tile: rows past n_rows read zeros (the extent is rounded
   // up to 16 bytes, the readable padding after a matrix).
@@ -137,22 +137,20 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // tokens 4g + i, 16 + 4g + i
 
-  // The wave's per-block scales (and Q4_K's dx * block sum), contiguous in
-  // the block-major layout, in batches of four 16-byte loads per lane; token
+  // The wave's per-block activation scales, contiguous in the block-major
+  // layout, in batches of four 16-byte loads per lane; token
   // slots past m become zero. The first batch (the whole range when a wave
   // has at most four super-blocks) is requested before the weights: loads
   // return in issue order, so storing it waits for no weights.
   const int nvec = DOTS ? 0 : nmine * 8 * kMT / 4;  // float4s of the wave's range
   const float4* gdx = reinterpret_cast<const float4*>(dxt + (int64_t)sb_begin * 8 * kMT);
-  const float4* gc = reinterpret_cast<const float4*>(cxt + (int64_t)sb_begin * 8 * kMT);
-  float4 vd[4], vc[4];
+  float4 vd[4];
   auto load_scales = [&](int v0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int v = v0 + lane + 64 * i;
       if (v < nvec) {
         vd[i] = gdx[v];
-        if constexpr (FMT == kQ4_K) vc[i] = gc[v];
       }
     }
   };
@@ -168,14 +166,6 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
         d.z = t + 2 < m ? d.z : 0.0f;
         d.w = t + 3 < m ? d.w : 0.0f;
         reinterpret_cast<float4*>(s_dx)[v] = d;
-        if constexpr (FMT == kQ4_K) {
-          float4 c = vc[i];
-          c.x = t + 0 < m ? c.x : 0.0f;
-          c.y = t + 1 < m ? c.y : 0.0f;
-          c.z = t + 2 < m ? c.z : 0.0f;
-          c.w = t + 3 < m ? c.w : 0.0f;
-          reinterpret_cast<float4*>(s_c)[v] = c;
-        }
       }
     }
   };
@@ -206,11 +196,21 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
     long act[8][2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_act((int64_t)sb * 8 + j, act[j][0], act[j][1]);
+    // Q4_K's min-term operands: (dx s)[token][sub-block 4 q + g] for the
+    // lane's token of each half (the block-major scale copy, from L2).
+    float cm[2][2];
+    if constexpr (FMT == kQ4_K && !DOTS) {
+#pragma unroll
+      for (int qd = 0; qd < 2; ++qd) {
+        const float* c = cxt + ((int64_t)sb * 8 + 4 * qd + g) * kMT;
+        cm[qd][0] = col < m ? c[col] : 0.0f;
+        cm[qd][1] = 16 + col < m ? c[16 + col] : 0.0f;
+      }
+    }
     __builtin_amdgcn_wave_barrier();  // the tile is written before any lane reads it
     const uint32_t base = (uint32_t)(col * G::PITCH) + (uint32_t)(((int64_t)col * rb + (int64_t)sb * BB) & 15);
     v4f accs0 = {0.f, 0.f, 0.f, 0.f}, accs1 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == kQ4_K) {
-      v4f accm0 = {0.f, 0.f, 0.f, 0.f}, accm1 = {0.f, 0.f, 0.f, 0.f};
       const u32x4 h = *reinterpret_cast<const u32x4*>(tile + base);
       const float d = half_bits(h.x & 0xffffu);
       const float dmin = half_bits(h.x >> 16);
@@ -218,6 +218,20 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
       const uint64_t s_lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
       const uint64_t s_hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
       const int sh = (g >> 1) * 4;  // lane groups 2, 3 take the high nibbles (elements 16..31)
+      if constexpr (!DOTS) {
+        // Min term on fp32 matrix cores, straight into the accumulators: for
+        // sub-blocks 4 q .. 4 q + 3, D[t][n] += sum_k (dx s)[t][4 q + k] *
+        // (-dmin m_{4 q + k})[n] (v_mfma_f32_16x16x4f32: A[t][k] in lane
+        // t + 16 k, B[k][n] in lane n + 16 k, D as for the integer products).
+#pragma unroll
+        for (int qd = 0; qd < 2; ++qd) {
+          const int jj = 4 * qd + g;
+          const float bm = -dmin * (float)((uint32_t)(s_hi >> (16 + 6 * jj)) & 63u);
+          const float a0 = cm[qd][0], a1 = cm[qd][1];
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bm, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bm, acc1, 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint2 q = *reinterpret_cast<const uint2*>(tile + base + 16 + 16 * j + 8 * (g & 1));
@@ -236,20 +250,8 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
           }
         } else {
           const int sc = (int)((s_lo >> (6 * j)) & 63u);
-          const float mj = (float)((s_hi >> (16 + 6 * j)) & 63u);
           const float4 d0 = *reinterpret_cast<const float4*>(s_dx + (bl0 + j) * kMT + 4 * g);
           const float4 d1 = *reinterpret_cast<const float4*>(s_dx + (bl0 + j) * kMT + 16 + 4 * g);
-          // min term: sum_j (dx s)[t][j] m_j of the lane's row
-          const float4 c0 = *reinterpret_cast<const float4*>(s_c + (bl0 + j) * kMT + 4 * g);
-          const float4 c1 = *reinterpret_cast<const float4*>(s_c + (bl0 + j) * kMT + 16 + 4 * g);
-          accm0[0] = fmaf(c0.x, mj, accm0[0]);
-          accm0[1] = fmaf(c0.y, mj, accm0[1]);
-          accm0[2] = fmaf(c0.z, mj, accm0[2]);
-          accm0[3] = fmaf(c0.w, mj, accm0[3]);
-          accm1[0] = fmaf(c1.x, mj, accm1[0]);
-          accm1[1] = fmaf(c1.y, mj, accm1[1]);
-          accm1[2] = fmaf(c1.z, mj, accm1[2]);
-          accm1[3] = fmaf(c1.w, mj, accm1[3]);
           accs0[0] = fmaf(d0.x, (float)__mul24(D0[0], sc), accs0[0]);
           accs0[1] = fmaf(d0.y, (float)__mul24(D0[1], sc), accs0[1]);
           accs0[2] = fmaf(d0.z, (float)__mul24(D0[2], sc), accs0[2]);
@@ -263,8 +265,8 @@ __global__ __launch_bounds__(NW * 64, 3) void gemm32_kernel(const uint8_t* __res
       if constexpr (!DOTS) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc0[i] = fmaf(d, accs0[i], fmaf(-dmin, accm0[i], acc0[i]));
-          acc1[i] = fmaf(d, accs1[i], fmaf(-dmin, accm1[i], acc1[i]));
+          acc0[i] = fmaf(d, accs0[i], acc0[i]);
+          acc1[i] = fmaf(d, accs1[i], acc1[i]);
         }
       }
     } else {
