@@ -113,15 +113,18 @@ QG_DEV float readlane_f(float v, int lane) {
 
 // Sum over aligned groups of `width` lanes (power of two <= 64), result in
 // every lane of the group. Groups of 32 and 64 add their 16-lane rows with
-// readlane in a fixed order.
+// lane swaps in a fixed order: (r0 + r1) + (r2 + r3).
 QG_DEV float group_sum(float v, int width) {
   v = group_sum16(v, width);
+  if (width >= 32) {
+    // 16-lane rows 2i and 2i + 1 (v_permlane16_swap gives every lane both).
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
   if (width == 64) {
-    v = (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
-  } else if (width == 32) {
-    const float g0 = readlane_f(v, 0) + readlane_f(v, 16);
-    const float g1 = readlane_f(v, 32) + readlane_f(v, 48);
-    v = (__lane_id() < 32) ? g0 : g1;
+    // The two halves (v_permlane32_swap).
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
   }
   return v;
 }
@@ -145,6 +148,21 @@ QG_DEV float rows4_wave_sum(float a0, float a1, float a2, float a3, int lane) {
   c = __uint_as_float(h[0]) + __uint_as_float(h[1]);  // lanes l and l ^ 32
   const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);  // 16-lane rows 2i and 2i + 1
+}
+
+// Totals of two rows over a whole wave (partials in a0, a1); on return the
+// lanes with l % 2 == r hold row r's total. Same scheme as rows4_wave_sum
+// with one exchange step.
+QG_DEV float rows2_wave_sum(float a0, float a1, int lane) {
+  const bool odd = lane & 1;
+  float c = (odd ? a1 : a0) + dpp<0xB1>(odd ? a0 : a1);  // quad_perm [1,0,3,2]
+  c += dpp<0x4E>(c);                                    // quad_perm [2,3,0,1]
+  c += dpp<0x124>(c);                                   // row_ror:4
+  c += dpp<0x128>(c);                                   // row_ror:8
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  c = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 QG_DEV float wave_max(float v) {

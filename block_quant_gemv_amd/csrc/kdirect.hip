@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
   auto consume = [&](const u32x4 (&h)[R][JU], const u32x4 (&q)[R][JU], const uint32_t (&x5)[R][JU],
                      int64_t grp) __attribute__((always_inline)) {
     const int64_t r0 = grp * R;
-    float outv = 0.0f;
+    float accr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float acc = 0.0f;
@@ -163,12 +163,23 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
         acc = fmaf(xd[j] * dsc, (float)D, acc);
         acc = fmaf(-(xd[j] * dmm), (float)xsum[j], acc);
       }
-      if constexpr (!DOTS) {
-        const float sum = group_sum(acc, 64);
-        if (lane == r) outv = sum;
-      }
+      accr[r] = acc;
     }
     if constexpr (!DOTS) {
+      // Row totals: lane r ends with row r.
+      float outv;
+      if constexpr (R == 4) {
+        outv = rows4_wave_sum(accr[0], accr[1], accr[2], accr[3], lane);
+      } else if constexpr (R == 2) {
+        outv = rows2_wave_sum(accr[0], accr[1], lane);
+      } else {
+        outv = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float sum = group_sum(accr[r], 64);
+          if (lane == r) outv = sum;
+        }
+      }
       const int64_t rows = (n - r0) < R ? (n - r0) : R;
       if (lane < rows) y[r0 + lane] = outv;
     }
