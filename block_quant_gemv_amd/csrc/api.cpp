@@ -319,8 +319,9 @@ constexpr int64_t kFusedQuantMaxK = QG_FUSED_MAXK;
 // faster for Q4_0, Q8_0 and Q4_K; K = 4096: 1.0 us faster for Q8_0 at 4096
 // rows, even for Q8_0 / Q4_K / Q4_0 / Q6_K at 12288 rows, but 0.5-0.8 us
 // slower for Q5_K, IQ4_XS and IQ4_NL (their decode is heavier, and the fused
-// instances run fewer, larger workgroups); four or sixteen tokens: 1-15 us
-// slower for every format.
+// instances run fewer, larger workgroups; the IQ4_NL lm_head 4096 -> 248320
+// again 101.8 against 97.7 us sustained after its decode got lighter); four
+// or sixteen tokens: 1-15 us slower for every format.
 bool fuse_quantizer(int fmt, int64_t k, int m) {
   if (m != 1 || k > kFusedQuantMaxK) return false;
   return k <= 2048 || fmt == kQ4_0 || fmt == kQ8_0 || fmt == kQ4_K || fmt == kQ6_K;
