@@ -317,14 +317,14 @@ constexpr int64_t kFusedQuantMaxK = QG_FUSED_MAXK;
 // all of x, which pays for the saved launch only for one token. Measured on
 // MI355X (qgemv_run, weights from HBM): one token, K = 2048: 1.0-1.2 us
 // faster for Q4_0, Q8_0 and Q4_K; K = 4096: 1.0 us faster for Q8_0 at 4096
-// rows, even for Q8_0 / Q4_K / Q4_0 / Q6_K at 12288 rows, but 0.5-0.8 us
-// slower for Q5_K, IQ4_XS and IQ4_NL (their decode is heavier, and the fused
-// instances run fewer, larger workgroups; the IQ4_NL lm_head 4096 -> 248320
-// again 101.8 against 97.7 us sustained after its decode got lighter); four
-// or sixteen tokens: 1-15 us slower for every format.
+// rows, even for Q8_0 / Q4_K / Q4_0 / Q6_K at 12288 rows; Q5_K and IQ4_XS
+// (register-direct kernel) 4096 -> 12288: 11.6 -> 9.8 and 9.5 -> 7.5 us; but
+// slower for the LDS-staged IQ4_NL (the lm_head 4096 -> 248320: 101.8
+// against 97.7 us sustained); four or sixteen tokens: 1-15 us slower for
+// every format.
 bool fuse_quantizer(int fmt, int64_t k, int m) {
   if (m != 1 || k > kFusedQuantMaxK) return false;
-  return k <= 2048 || fmt == kQ4_0 || fmt == kQ8_0 || fmt == kQ4_K || fmt == kQ6_K;
+  return k <= 2048 || fmt == kQ4_0 || fmt == kQ8_0 || fmt == kQ4_K || fmt == kQ6_K || fmt == kIQ4_XS || fmt == kQ5_K;
 }
 
 int validate_gemv_call(qgemv_t h, int m, const void* ws, size_t ws_bytes, const char* fn) {

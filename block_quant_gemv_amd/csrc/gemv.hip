@@ -47,7 +47,7 @@ namespace qg {
 #define QG_WLOAD_AUX 2    // cache-policy bits of the weight loads (2: non-temporal, read once)
 #endif
 #ifndef QG_Q4K_DIRECT
-#define QG_Q4K_DIRECT 1   // single-token Q4_K and Q5_K GEMVs use the register-direct kernel
+#define QG_Q4K_DIRECT 1   // single-token Q4_K, Q5_K and IQ4_XS GEMVs use the register-direct kernel
 #endif
 #ifndef QG_PREFETCH
 #define QG_PREFETCH 1     // weight steps in flight per wave (1 or 2)

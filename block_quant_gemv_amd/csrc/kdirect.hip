@@ -1,5 +1,5 @@
-// Single-token GEMV over Q4_K and Q5_K super-blocks read straight into
-// registers.
+// Single-token GEMV over Q4_K, Q5_K and IQ4_XS super-blocks read straight
+// into registers.
 //
 // Both super-blocks (144 and 176 bytes) are multiples of 16, so every field a
 // lane needs -- the 16-byte header (d, dmin, the twelve bytes of 6-bit scales
@@ -18,8 +18,15 @@
 // Per (row, sub-block j of super-block b): D = sum xq * q over the 32 codes
 // (q in 0..15, or 0..31 for Q5_K) and s = sum xq (the activation block sum), then
 // y += dx * (d * sc_j) * D - dx * (dmin * m_j) * s, accumulated in fp32 per
-// lane; the 64 lanes of a row are summed in a fixed order (DPP, readlane).
+// lane; the 64 lanes of a row are summed in a fixed order (DPP, lane swaps).
+//
+// IQ4_XS (136-byte super-blocks: d, the sub-scales' high bits, their low
+// nibbles, 128 code bytes) has the same sub-block shape: the lane reads the
+// 8-byte header and its sub-block's 16 code bytes (both 8-byte aligned),
+// maps the codes through the codebook (two byte permutes and an xor per
+// four codes, as in the LDS-staged kernel) and adds dx * d * (ls_j - 32) * D.
 #include "common.cuh"
+#include "formats.cuh"
 #include "internal.h"
 
 #ifndef QG_DIRECT_WGS_PER_CU
@@ -32,7 +39,10 @@
 #define QG_Q5K_RBIG 4            // rows per wave iteration for large Q5_K matrices
 #endif
 #ifndef QG_Q4K_RFUSED
-#define QG_Q4K_RFUSED 2          // the same with the quantizer fused (one workgroup per CU)
+#define QG_Q4K_RFUSED 2          // the same with the quantizer fused (one workgroup per CU), all formats
+#endif
+#ifndef QG_IQ4XS_DIRECT
+#define QG_IQ4XS_DIRECT 1        // single-token IQ4_XS GEMVs use this kernel too
 #endif
 #ifndef QG_DIRECT_FUSED_WGS_PER_CU
 #define QG_DIRECT_FUSED_WGS_PER_CU 1
@@ -63,6 +73,7 @@ struct DirectArgs {
   float* y;
   int32_t* dots;
   int64_t n, rb;
+  uint32_t cb[4];        // IQ4_XS: the codebook's byte-permute pools
 };
 
 // FMT: kQ4_K or kQ5_K; R rows per iteration; JU sub-blocks per lane per row.
@@ -96,8 +107,14 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
   const bool m_low = g < 3;      // m_g within dwords {2, 3}, else dword 3
   const uint32_t m_sh = m_low ? 16 + 6 * g : 6 * g - 16;
   constexpr bool Q5 = FMT == kQ5_K;
-  constexpr uint32_t BB = Q5 ? 176u : 144u;     // super-block bytes
-  constexpr uint32_t QS = Q5 ? 48u : 16u;       // offset of the low code bits
+  constexpr bool XS = FMT == kIQ4_XS;
+  constexpr uint32_t BB = Q5 ? 176u : XS ? 136u : 144u;  // super-block bytes
+  constexpr uint32_t QS = Q5 ? 48u : XS ? 8u : 16u;      // offset of the (low) code bits
+  uint32_t cbr[4] = {A.cb[0], A.cb[1], A.cb[2], A.cb[3]};
+  if constexpr (XS) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(cbr[i]));  // pools in VGPRs for the permutes
+  }
   uint32_t hoff[JU], qoff[JU], xoff[JU];
 #pragma unroll
   for (int j = 0; j < JU; ++j) {
@@ -119,7 +136,12 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < JU; ++j) {
-        h[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(hoff[j] + r * rb), 0, kNonTemporal);
+        if constexpr (XS) {
+          const auto hv = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(hoff[j] + r * rb), 0, kNonTemporal);
+          h[r][j] = u32x4{hv[0], hv[1], 0u, 0u};
+        } else {
+          h[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(hoff[j] + r * rb), 0, kNonTemporal);
+        }
         q[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(qoff[j] + r * rb), 0, kNonTemporal);
         if constexpr (Q5)
           x5[r][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(xoff[j] + r * rb), 0, kNonTemporal);
@@ -140,6 +162,13 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
         int D = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          if constexpr (XS) {
+            uint32_t vlo, vhi;
+            cb_lookup8(qv[i], cbr, vlo, vhi);
+            D = dot4((int)vlo, xa[j][i], D);
+            D = dot4((int)vhi, xa[j][4 + i], D);
+            continue;
+          }
           uint32_t lo = qv[i] & 0x0F0F0F0Fu, hi = (qv[i] >> 4) & 0x0F0F0F0Fu;
           if constexpr (Q5) {
             // fifth bit of sub-block element e at bit 8 (e % 4) + e / 4 of
@@ -152,6 +181,12 @@ __global__ __launch_bounds__(NW * 64) void kdirect_kernel(const DirectArgs A) {
         }
         if constexpr (DOTS) {
           if (r0 + r < n) dots[(r0 + r) * (64 * JU) + lane + 64 * j] = D;
+          continue;
+        }
+        if constexpr (XS) {
+          // 6-bit sub-scale: low nibble g of scales_l, high bits 2g of scales_h
+          const uint32_t ls = ((hh.y >> (4 * g)) & 0xFu) | (((hh.x >> (16 + 2 * g)) & 3u) << 4);
+          acc = fmaf(xd[j] * (half_bits(hh.x & 0xffffu) * (float)((int)ls - 32)), (float)D, acc);
           continue;
         }
         const float d = half_bits(hh.x & 0xffffu);
@@ -301,6 +336,7 @@ hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
   a.dots = p.dots;
   a.n = p.n;
   a.rb = fmt_row_bytes(FMT, p.k);
+  for (int i = 0; i < 4; ++i) a.cb[i] = p.cb[i];
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
@@ -311,7 +347,7 @@ hipError_t launch_t(const GemvProblem& p, hipStream_t s) {
 bool kdirect_ok(int fmt, const GemvProblem& p, bool dots) {
   // fused quantization: one token, K up to 4096 (64 x 2 sub-blocks per lane)
   const bool acts = p.xf ? (!dots && p.k <= 4096 && (!p.xq_out || p.dx_out)) : (p.xq != nullptr);
-  return (fmt == kQ4_K || fmt == kQ5_K) && p.m == 1 && !p.tbl && acts &&
+  return (fmt == kQ4_K || fmt == kQ5_K || (fmt == kIQ4_XS && QG_IQ4XS_DIRECT)) && p.m == 1 && !p.tbl && acts &&
          (dots ? p.dots != nullptr : ((p.xf || p.dx) && p.y)) && p.k % 2048 == 0 && p.k / 2048 >= 1 &&
          p.k / 2048 <= 4 && p.n >= 1;
 }
@@ -359,11 +395,12 @@ static hipError_t launch_fmt(const GemvProblem& p, bool dots, hipStream_t s) {
   // Rows per wave iteration, measured on MI355X (Q4_K): four rows (more
   // bytes in flight per wave) once there are enough rows to still give every
   // CU several waves, one row for smaller matrices (more waves). With the
-  // quantizer fused (12 or 16 waves, one workgroup per CU) two rows: at
-  // 12288 rows, groups of four left each wave a single group and nothing to
-  // overlap its load with (9.1 -> 7.85 us per call; 24576 rows unchanged).
+  // quantizer fused (12 or 16 waves, one workgroup per CU) two rows, for
+  // every format: at 12288 rows, groups of four left each wave a single
+  // group and nothing to overlap its load with (Q4_K 9.1 -> 7.85 us per
+  // call; 24576 rows unchanged).
   constexpr int RB = FMT == kQ5_K ? QG_Q5K_RBIG : QG_Q4K_RBIG;
-  constexpr int RF = FMT == kQ5_K ? QG_Q5K_RBIG : QG_Q4K_RFUSED;
+  constexpr int RF = QG_Q4K_RFUSED;
   if (dots) return p.n >= 8192 ? launch_ju<FMT, RB, true, false>(p, s) : launch_ju<FMT, 1, true, false>(p, s);
   if (p.xf) return p.n >= 8192 ? launch_ju<FMT, RF, false, true>(p, s) : launch_ju<FMT, 1, false, true>(p, s);
   return p.n >= 8192 ? launch_ju<FMT, RB, false, false>(p, s) : launch_ju<FMT, 1, false, false>(p, s);
@@ -371,6 +408,7 @@ static hipError_t launch_fmt(const GemvProblem& p, bool dots, hipStream_t s) {
 
 hipError_t launch_kdirect(int fmt, const GemvProblem& p, bool dots, hipStream_t s) {
   if (!kdirect_ok(fmt, p, dots)) return hipErrorInvalidValue;
+  if (fmt == kIQ4_XS) return launch_fmt<kIQ4_XS>(p, dots, s);
   return fmt == kQ4_K ? launch_fmt<kQ4_K>(p, dots, s) : launch_fmt<kQ5_K>(p, dots, s);
 }
 
