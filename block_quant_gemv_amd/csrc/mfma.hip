@@ -28,7 +28,8 @@
 // fields, and keeps its partial sums in registers. The waves' sums are added
 // through LDS in wave order at the end, so results are bitwise reproducible
 // with no atomics and no second launch. 16-row tiles give 768 workgroups for
-// 12288 rows, three per CU on 256 CUs.
+// 12288 rows, three per CU on 256 CUs (of 8 waves each: two super-blocks per
+// wave at K = 4096).
 #include "common.cuh"
 #include "internal.h"
 #include "mfma.h"
@@ -374,13 +375,15 @@ bool shape_ok(int fmt, int64_t n, int64_t k, int m) {
          rb * kRows < (1ll << 30) && (k / 32) * kMT * 32 < (1ll << 30);
 }
 
-// Waves per workgroup: enough to keep about 12 waves per CU (three per
-// SIMD) when the row tiles alone do not, each wave taking at least two
-// super-blocks; at most 8 (16-wave workgroups leave 128 registers per lane,
-// which spills: Q6_K 4096 x 12288 at 32 tokens 27.6 us with 16, 25.9 with 8).
+// Waves per workgroup: enough to keep about 16 waves per CU (four per
+// SIMD; the Q4_K instance needs about 120 registers) when the row tiles alone
+// do not, each wave taking at least two super-blocks (Q4_K 12288 x 4096:
+// kernel 16.9 -> 16.55 us against a target of 12); at most 8 (16-wave
+// workgroups leave 128 registers per lane, which spills: Q6_K 4096 x 12288
+// at 32 tokens 27.6 us with 16, 25.9 with 8).
 int waves_for(int64_t n, int64_t k) {
   const int64_t tiles = (n + kRows - 1) / kRows;
-  const int64_t want = (int64_t)device_cus() * 12;
+  const int64_t want = (int64_t)device_cus() * 16;
   const int nsb = (int)(k / 256);
   int nw = 4;
   while (nw < 8 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
