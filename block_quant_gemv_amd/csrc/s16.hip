@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
         q[r][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(qoff[j] + r * rb), 0, 2);
         if constexpr (Q5) x5[r][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(xoff[j] + r * rb), 0, 2);
       }
-    float outv = 0.0f;
+    float accr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float acc = 0.0f;
@@ -177,12 +177,21 @@ __global__ __launch_bounds__(kWaves16 * 64) void q4k_s16_kernel(const uint8_t* _
         acc = fmaf(xd[j] * (d * (float)sc), (float)D, acc);
         acc = fmaf(-(xd[j] * (dmin * (float)mn)), (float)xsum[j], acc);
       }
-      if constexpr (!DOTS) {
-        const float sum = group_sum(acc, 64);
-        if (lane == r) outv = sum;
-      }
+      accr[r] = acc;
     }
     if constexpr (!DOTS) {
+      // Row totals: lane r ends with row r (four rows reduced together).
+      float outv;
+      if constexpr (R == 4) {
+        outv = rows4_wave_sum(accr[0], accr[1], accr[2], accr[3], lane);
+      } else {
+        outv = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float sum = group_sum(accr[r], 64);
+          if (lane == r) outv = sum;
+        }
+      }
       if (lane < rows) y[r0 + lane] = outv;
     }
   }
