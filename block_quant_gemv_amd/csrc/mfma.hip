@@ -29,7 +29,7 @@
 // through LDS in wave order at the end, so results are bitwise reproducible
 // with no atomics and no second launch. 16-row tiles give 768 workgroups for
 // 12288 rows, three per CU on 256 CUs (of 8 waves each: two super-blocks per
-// wave at K = 4096).
+// wave at K = 4096); 4096 rows at K = 12288 run 256 workgroups of 16 waves.
 #include "common.cuh"
 #include "internal.h"
 #include "mfma.h"
@@ -376,17 +376,18 @@ bool shape_ok(int fmt, int64_t n, int64_t k, int m) {
 }
 
 // Waves per workgroup: enough to keep about 16 waves per CU (four per
-// SIMD; the Q4_K instance needs about 120 registers) when the row tiles alone
-// do not, each wave taking at least two super-blocks (Q4_K 12288 x 4096:
-// kernel 16.9 -> 16.55 us against a target of 12); at most 8 (16-wave
-// workgroups leave 128 registers per lane, which spills: Q6_K 4096 x 12288
-// at 32 tokens 27.6 us with 16, 25.9 with 8).
+// SIMD) when the row tiles alone do not, each wave taking at least two
+// super-blocks; at most 16, which leaves 128 registers per lane: the Q4_K
+// and Q6_K instances need 118 and 126. Measured: Q4_K 12288 x 4096 with 8
+// waves (target 16 against 12) kernel 16.9 -> 16.55 us; Q6_K 4096 x 12288
+// with 16 waves against 8, call 26.7 -> 26.4 us (an earlier version of the
+// kernel spilled at 16 waves: 27.6 against 25.9 us).
 int waves_for(int64_t n, int64_t k) {
   const int64_t tiles = (n + kRows - 1) / kRows;
   const int64_t want = (int64_t)device_cus() * 16;
   const int nsb = (int)(k / 256);
   int nw = 4;
-  while (nw < 8 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
+  while (nw < 16 && tiles * nw < want && nsb / (nw * 2) >= 2) nw *= 2;
   return nw;
 }
 
@@ -411,7 +412,9 @@ hipError_t launch_t(const uint8_t* w, const int8_t* xqt, const float* dxt, const
 template <int FMT, bool DOTS>
 hipError_t launch_fmt(const uint8_t* w, const int8_t* xqt, const float* dxt, const float* cxt, float* y,
                       int32_t* dots, int64_t n, int64_t k, int m, hipStream_t s) {
-  if (waves_for(n, k) == 4) return launch_t<FMT, 4, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+  const int nw = waves_for(n, k);
+  if (nw == 4) return launch_t<FMT, 4, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
+  if (nw == 16) return launch_t<FMT, 16, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
   return launch_t<FMT, 8, DOTS>(w, xqt, dxt, cxt, y, dots, n, k, m, s);
 }
 
