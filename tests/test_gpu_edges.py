@@ -247,3 +247,32 @@ def test_codebook_sign_patterns(fmt):
         bad = np.argwhere(host(dots) != ref_dots)
         assert bad.size == 0, f"codebook {i}: {len(bad)} block dots differ, first {bad[:3].tolist()}"
         assert normwise(host(y), og.gemv_dequant(fmt, w, n, k, xq, dx, cb)) <= TOL
+
+
+# One token through the register-direct K-quant kernel (Q5_K, IQ4_XS): K of
+# 2048 / 4096 / 8192 (one to four sub-blocks per lane), row counts that leave
+# a ragged last group of rows (groups of 2 or 4 rows from 8192 rows), and for
+# IQ4_XS codebooks of different sign patterns. Block dots exact, outputs
+# within the normwise bound.
+@pytest.mark.parametrize("fmt,n,k", [("iq4_xs", 8195, 2048), ("iq4_xs", 37, 8192), ("iq4_xs", 8193, 4096),
+                                     ("q5_k", 8195, 2048), ("q5_k", 8194, 8192), ("q5_k", 37, 4096)])
+def test_register_direct_one_token(fmt, n, k):
+    cbs = [CB, np.arange(-128, -112, dtype=np.int8)] if fmt == "iq4_xs" else [None]
+    w = synth.weights(fmt, n, k, seed=n + k)
+    x = synth.activations(n + 1, 1, k)
+    xq, dx, _ = quantize_q8(x)
+    wd = dev(w)
+    for cb in cbs:
+        say(f"register-direct {fmt} n={n} k={k} codebook={None if cb is None else int(cb[0])}")
+        g = qg.GEMV(fmt, n, k, codebook=cb)
+        full, y = guarded(torch, n, torch.float32)
+        g.run(wd, dev(x), y.view(1, n))
+        dots = g.block_dots(wd, dev(xq))
+        torch.cuda.synchronize()
+        assert canary_ok(torch, full, n), "output guard band overwritten"
+        ref_dots = og.block_dots(fmt, w, n, k, xq, cb)
+        bad = np.argwhere(host(dots) != ref_dots)
+        assert bad.size == 0, f"{len(bad)} block dots differ, first {bad[:3].tolist()}"
+        e = normwise(host(y).reshape(1, n), og.gemv_dequant(fmt, w, n, k, xq, dx, cb))
+        say(f"  normwise error {e:.3e}")
+        assert e <= TOL
