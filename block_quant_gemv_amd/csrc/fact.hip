@@ -21,6 +21,7 @@
 // added in wave order through LDS, and wave 0 stores y.
 #include "common.cuh"
 #include "fact.h"
+#include "internal.h"
 
 namespace qg {
 
@@ -28,6 +29,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef QG_FA_ROWS
+#define QG_FA_ROWS 1  // one to four tokens take the row-streaming kernel
+#endif
 #ifndef QG_FA_WAVES
 #define QG_FA_WAVES 4
 #endif
@@ -159,6 +163,167 @@ __global__ __launch_bounds__(kFaWaves * 64) void fact_kernel(const uint8_t* __re
   }
 }
 
+// One to four tokens: the matrix cores would do up to 16 times the useful
+// work, and per-lane 2-byte code loads do not coalesce, so the rows stream
+// like the decode GEMV's: a wave copies one row at a time into its own LDS
+// tile with 16-byte loads that are contiguous across lanes (the next row is
+// requested as soon as the current one is in LDS), and each lane takes 32-
+// element blocks b = lane, lane + 64, ...: an fp32 dot of its codes (read
+// from the tile at any 2-byte alignment) with x, staged once per workgroup in
+// LDS, then times the block scale. The 64 lanes of a row are summed in a
+// fixed order, so results are bitwise reproducible.
+constexpr int kRowWaves = 4;
+constexpr int kRowLpl = 5;                       // 16-byte loads per lane per row
+constexpr int kRowTile = kRowLpl * 64 * 16;      // LDS bytes of a wave's row tile
+constexpr int64_t kRowMaxBytes = kRowTile - 30;  // the row plus its alignment chunks must fit
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(kRowWaves * 64) void fact_rows_kernel(const uint8_t* __restrict__ w,
+                                                                   const float* __restrict__ x,
+                                                                   float* __restrict__ y, int m, int64_t n,
+                                                                   int64_t k) {
+  constexpr int BB = kFaBlockBytes<FMT>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  // x of token t in LDS by quarter blocks: float4 v (elements 4v .. 4v + 3)
+  // of block b at slot t * k / 4 + v * nb + b, so that the 64 lanes of a
+  // wave, reading quarter v of blocks lane, lane + 64, ..., read consecutive
+  // 16-byte words (the plain layout puts them 128 bytes apart: bank
+  // conflicts).
+  float* xs = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* tile = smem + (size_t)MT * k * 4 + (size_t)wid * kRowTile;
+  const int64_t nb = k / 32;
+  const int64_t rb = nb * BB;
+  const int64_t gw = (int64_t)blockIdx.x * kRowWaves + wid;
+  const int64_t nw = (int64_t)gridDim.x * kRowWaves;
+
+  // The 16-byte chunks spanning row r, through a buffer resource that covers
+  // exactly them (rows past the end: no chunks, the loads read zeros).
+  auto chunks = [&](int64_t r, int64_t& a0) __attribute__((always_inline)) -> int {
+    if (r >= n) { a0 = 0; return 0; }
+    a0 = (r * rb) & ~(int64_t)15;
+    return (int)((((r * rb + rb + 15) & ~(int64_t)15) - a0) >> 4);
+  };
+  u32x4 buf[kRowLpl];
+  auto issue = [&](int64_t r) __attribute__((always_inline)) {
+    int64_t a0;
+    const int nch = chunks(r, a0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + a0), 0, nch * 16, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kRowLpl; ++i) buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + 64 * i) * 16, 0, 2);
+  };
+  issue(gw);
+
+  // x of every token into LDS (tokens past m read as zeros), in batches of
+  // four 16-byte loads per thread, all issued before any is stored: one
+  // memory round trip per batch.
+  const int64_t nx = (int64_t)MT * k / 4;
+  for (int64_t i0 = threadIdx.x; i0 < nx; i0 += 4 * kRowWaves * 64) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * kRowWaves * 64;
+      v[u] = (i < nx && (4 * i) / k < m) ? reinterpret_cast<const float4*>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * kRowWaves * 64;
+      if (i < nx) {
+        const int64_t t = (4 * i) / k, j = i - t * (k / 4);  // token, float4 within the token
+        reinterpret_cast<float4*>(xs)[t * (k / 4) + (j & 7) * nb + (j >> 3)] = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int64_t r = gw; r < n; r += nw) {
+    int64_t a0;
+    const int nch = chunks(r, a0);
+    __builtin_amdgcn_wave_barrier();  // the previous row's tile reads are done
+#pragma unroll
+    for (int i = 0; i < kRowLpl; ++i)
+      if (lane + 64 * i < nch) *reinterpret_cast<u32x4*>(tile + 16 * (lane + 64 * i)) = buf[i];
+    issue(r + nw);
+    __builtin_amdgcn_wave_barrier();  // the tile is written before any lane reads it
+    const uint32_t base = (uint32_t)(r * rb - a0);
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+    for (int64_t b = lane; b < nb; b += 64) {
+      const uint32_t o = base + (uint32_t)(b * BB);
+      const float d = half_bits(lds_u16(tile, o));
+      float q[32];
+      if constexpr (FMT == 2) {
+        uint32_t c[8];
+        lds_read4_direct(tile, o + 2, *reinterpret_cast<uint32_t(*)[4]>(c));
+        lds_read4_direct(tile, o + 18, *reinterpret_cast<uint32_t(*)[4]>(c + 4));
+#pragma unroll
+        for (int i = 0; i < 32; ++i) q[i] = (float)(int8_t)(c[i / 4] >> (8 * (i % 4)));
+      } else {
+        uint32_t c[4];
+        lds_read4_direct(tile, o + 2, c);
+        // element e < 16: low nibble of byte e; e >= 16: high nibble of byte e - 16
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          q[i] = (float)((int)((c[i / 4] >> (8 * (i % 4))) & 0xfu) - 8);
+          q[16 + i] = (float)((int)((c[i / 4] >> (8 * (i % 4) + 4)) & 0xfu) - 8);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const float4* xv = reinterpret_cast<const float4*>(xs) + (int64_t)t * (k / 4) + b;
+        float sdot = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float4 f = xv[v * nb];
+          sdot = fmaf(q[4 * v], f.x, sdot);
+          sdot = fmaf(q[4 * v + 1], f.y, sdot);
+          sdot = fmaf(q[4 * v + 2], f.z, sdot);
+          sdot = fmaf(q[4 * v + 3], f.w, sdot);
+        }
+        acc[t] = fmaf(d, sdot, acc[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float v = group_sum(acc[t], 64);
+      if (lane == 0 && t < m) y[(int64_t)t * n + r] = v;
+    }
+  }
+}
+
+template <int FMT, int MT>
+hipError_t launch_rows_t(const uint8_t* w, const float* x, float* y, int m, int64_t n, int64_t k, hipStream_t s) {
+  auto kern = fact_rows_kernel<FMT, MT>;
+  const size_t lds = (size_t)MT * k * 4 + (size_t)kRowWaves * kRowTile;
+  int per_cu = 0, cus = 0;
+  hipError_t qe = kernel_residency(reinterpret_cast<const void*>(kern), kRowWaves * 64, lds, true, &per_cu, &cus);
+  if (qe != hipSuccess) return qe;
+  if (per_cu < 1) return hipErrorInvalidValue;
+  int64_t wgs = (int64_t)cus * per_cu;
+  const int64_t need = (n + kRowWaves - 1) / kRowWaves;
+  if (wgs > need) wgs = need;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kRowWaves * 64), lds, s, w, x, y, m, n, k);
+  return hipGetLastError();
+}
+
+// The row-streaming kernel's shapes: up to four tokens whose x fits 64 KB of
+// LDS next to the row tiles, and rows of at most kRowMaxBytes.
+bool rows_ok(int fmt, int m, int64_t k) {
+  const int64_t rb = k / 32 * (fmt == 1 ? 18 : 34);
+  const int mt = m <= 1 ? 1 : m <= 2 ? 2 : 4;
+  return QG_FA_ROWS && m <= 4 && rb <= kRowMaxBytes && (int64_t)mt * k * 4 + kRowWaves * kRowTile <= 64 * 1024;
+}
+
+template <int FMT>
+hipError_t launch_rows(const uint8_t* w, const float* x, float* y, int m, int64_t n, int64_t k, hipStream_t s) {
+  if (m <= 1) return launch_rows_t<FMT, 1>(w, x, y, m, n, k, s);
+  if (m <= 2) return launch_rows_t<FMT, 2>(w, x, y, m, n, k, s);
+  return launch_rows_t<FMT, 4>(w, x, y, m, n, k, s);
+}
+
 }  // namespace
 
 bool fact_supported(int fmt) { return fmt == 1 || fmt == 2; }
@@ -166,6 +331,7 @@ bool fact_supported(int fmt) { return fmt == 1 || fmt == 2; }
 hipError_t launch_fact(int fmt, const uint8_t* w, const float* x, float* y, int m, int64_t n, int64_t k,
                        hipStream_t s) {
   if (!fact_supported(fmt) || m < 1 || m > 32 || n < 1 || k < 32 || k % 32) return hipErrorInvalidValue;
+  if (rows_ok(fmt, m, k)) return fmt == 1 ? launch_rows<1>(w, x, y, m, n, k, s) : launch_rows<2>(w, x, y, m, n, k, s);
   const dim3 grid((unsigned)((n + 15) / 16)), block(kFaWaves * 64);
   if (fmt == 1) {
     if (m <= 16) hipLaunchKernelGGL((fact_kernel<1, 1>), grid, block, 0, s, w, x, y, m, n, k);
