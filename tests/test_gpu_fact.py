@@ -22,7 +22,8 @@ import block_quant_gemv_amd as qg  # noqa: E402
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("n,k,m", [(1, 32, 1), (37, 96, 3), (300, 1024, 16), (300, 1024, 17),
-                                   (1000, 2048, 32), (4095, 512, 9), (16, 4096, 2), (129, 8192, 31)])
+                                   (1000, 2048, 32), (4095, 512, 9), (16, 4096, 2), (129, 8192, 31),
+                                   (517, 2048, 5), (300, 4096, 8), (33, 1024, 7)])
 def test_f32act_parity(fmt, n, k, m):
     say(f"f32act parity {fmt} n={n} k={k} m={m}")
     w = synth.weights(fmt, n, k, seed=71)
