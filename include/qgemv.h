@@ -255,7 +255,9 @@ int qgemv_run_s16(qgemv_t h, const void *w, const float *x, float *y, void *ws, 
  * batched (prefill) path, where int8 activations cost about 3 % perplexity
  * and float activations about 0.2 % in "01 · Phase overview: from 2B to 8B
  * to MoE" (icman.com.cn, issue ledger item ⑮). Products and sums are fp32
- * (fp32 matrix cores). Supported for QFMT_Q4_0 and QFMT_Q8_0 plans
+ * (one to four tokens where x fits in LDS: fp32 vector dot products per
+ * 32-element block; otherwise fp32 matrix cores). Supported for QFMT_Q4_0
+ * and QFMT_Q8_0 plans
  * (QGEMV_EFORMAT otherwise); m outside 1..32 is QGEMV_ESHAPE (the plan's
  * max_m does not apply: no workspace is used). x: fp32 [m, k], 16-byte
  * aligned; w 16-byte aligned; y: fp32 [m, n]. One kernel on `stream`. */
