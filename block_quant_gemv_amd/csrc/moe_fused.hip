@@ -76,8 +76,10 @@ constexpr int kUpSgu = 2 * kMaxTok * 64 * 4;
 // its tokens are split over several entries (each reads the shared weights
 // again, mostly from cache) to keep its items as light as the routed ones.
 constexpr int kShareTok = 4;
-// LDS bytes per token of staged 16-bit activation codes: per 32-element
-// unit 16 dwords of paired codes, then per unit (scale, code sum).
+// LDS bytes per token of staged 16-bit activation codes: the 16 dwords of
+// paired codes of each 32-element unit as four 16-byte quarters, quarter v
+// of unit u at 16 (v U + u) (lanes reading consecutive units read
+// consecutive words: no LDS bank conflicts), then per unit (scale, code sum).
 __host__ __device__ constexpr int act16_token_bytes(int U) { return 72 * U; }
 constexpr int kMaxShare = (kMaxTok + kShareTok - 1) / kShareTok;
 constexpr int kBufDword3 = 0x00020000;
@@ -204,7 +206,7 @@ QG_DEV Act16 load_act16(const uint8_t* tok, int U, int u) {
   Act16 x;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(tok + 64 * u + 16 * v);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(tok + 16 * (v * U + u));
     x.p[4 * v + 0] = q.x;
     x.p[4 * v + 1] = q.y;
     x.p[4 * v + 2] = q.z;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kUpWaves * 64) void moe_up_kernel(const MoeFusedArg
         pair16(st_c[r], pr);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          *reinterpret_cast<u32x4*>(tok + 64 * u + 16 * v) = u32x4{pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
+          *reinterpret_cast<u32x4*>(tok + 16 * (v * U + u)) = u32x4{pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
         *reinterpret_cast<int2*>(tok + 64 * U + 8 * u) = make_int2(__float_as_int(st_d[r]), st_s[r]);
       } else {
         const int ones = 0x01010101;
